@@ -1,0 +1,240 @@
+"""Plain CPU oracle of the MiMo-V2 image pixel path -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library
+(``vision_image_preprocessing_amd``) never imports it, and the two share no
+code: the C source here (``oracle.c``) is compiled by gcc on its own, with
+``-ffp-contract=off`` so that the only fused multiply-adds are the explicit
+``fmaf`` calls that reproduce torch's float32 resize arithmetic.
+
+Each wrapper below names the passage of the pages it follows; the C source
+carries the step-by-step definitions.  Pages:
+
+* NeMo Automodel, ``mimo_v2_flash.processing`` (module docstring,
+  ``MimoV2ImageProcessor``, ``smart_resize``, ``_to_rgb``,
+  ``get_number_of_image_patches``);
+* docs.rs ``cortiq_engine::mimo_vision`` (module conventions,
+  ``resize_bilinear``, ``column_permutation``, ``smart_resize``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+OK = 0
+E_INVALID = -1
+E_ASPECT = -2
+E_DEGENERATE = -3
+E_NOMEM = -4
+
+# Defaults of MimoV2ImageProcessor (processing page, class signature).
+PATCH = 16
+TEMPORAL = 2
+MERGE = 2
+MIN_PIXELS = 8192
+MAX_PIXELS = 8388608
+# Aspect guard of the Qwen2-VL smart_resize the processing page defers to.
+MAX_ASPECT = 200.0
+
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so with gcc (no GPU code involved)."""
+    if force or not os.path.exists(_LIB_PATH) or (
+        os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)
+    ):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = [
+            "gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+            "-fno-fast-math", "-Wall", "-Wextra", _SRC, "-lm", "-o", tmp,
+        ]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH) or (
+            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)
+        ):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        i64, p = ctypes.c_int64, ctypes.c_void_p
+        lib.oracle_smart_resize.argtypes = [i64, i64, i64, i64, i64, ctypes.c_double,
+                                            ctypes.POINTER(i64), ctypes.POINTER(i64)]
+        lib.oracle_smart_resize.restype = ctypes.c_int
+        lib.oracle_image_grid.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.c_double,
+                                          p, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+        lib.oracle_image_grid.restype = ctypes.c_int
+        lib.oracle_flatten_rgba.argtypes = [p, i64, p]
+        lib.oracle_flatten_rgba.restype = None
+        lib.oracle_resize_bilinear.argtypes = [p, i64, i64, i64, p, i64, i64]
+        lib.oracle_resize_bilinear.restype = None
+        lib.oracle_to_bf16.argtypes = [p, i64, p]
+        lib.oracle_to_bf16.restype = None
+        lib.oracle_preprocess_image.argtypes = [p, i64, i64, i64, i64, i64, i64, i64, i64,
+                                                p, p, p]
+        lib.oracle_preprocess_image.restype = ctypes.c_int
+        lib.oracle_preprocess_rows.argtypes = [p, i64, i64, i64, i64, i64, i64, i64, i64,
+                                               p, p, i64, i64, p]
+        lib.oracle_preprocess_rows.restype = ctypes.c_int
+        lib.oracle_column_permutation.argtypes = [i64, i64, i64, i64, p]
+        lib.oracle_column_permutation.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+class OracleError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: oracle status {code}")
+        self.code = code
+
+
+def _ptr(a: np.ndarray) -> int:
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data
+
+
+def smart_resize(height: int, width: int, factor: int = PATCH * MERGE,
+                 min_pixels: int = MIN_PIXELS, max_pixels: int = MAX_PIXELS,
+                 max_aspect: float = MAX_ASPECT):
+    """processing page, ``smart_resize``: (resized_height, resized_width).
+
+    Raises OracleError with code E_INVALID, E_ASPECT or E_DEGENERATE.
+    """
+    lib = _load()
+    oh, ow = ctypes.c_int64(), ctypes.c_int64()
+    st = lib.oracle_smart_resize(height, width, factor, min_pixels, max_pixels,
+                                 float(max_aspect), ctypes.byref(oh), ctypes.byref(ow))
+    if st != OK:
+        raise OracleError(st, f"smart_resize({height}, {width})")
+    return oh.value, ow.value
+
+
+def smart_resize_status(height, width, factor=PATCH * MERGE, min_pixels=MIN_PIXELS,
+                        max_pixels=MAX_PIXELS, max_aspect=MAX_ASPECT):
+    """Like smart_resize but returns (status, h, w) instead of raising."""
+    lib = _load()
+    oh, ow = ctypes.c_int64(0), ctypes.c_int64(0)
+    st = lib.oracle_smart_resize(height, width, factor, min_pixels, max_pixels,
+                                 float(max_aspect), ctypes.byref(oh), ctypes.byref(ow))
+    return st, oh.value, ow.value
+
+
+def image_grid(height, width, patch=PATCH, merge=MERGE, min_pixels=MIN_PIXELS,
+               max_pixels=MAX_PIXELS, max_aspect=MAX_ASPECT):
+    """get_number_of_image_patches and the image_grid_thw entry.
+
+    Returns ((grid_t, grid_h, grid_w), rows, tokens) with rows = gt*gh*gw
+    patches and tokens = rows / merge**2.
+    """
+    lib = _load()
+    g = np.zeros(3, dtype=np.int64)
+    rows, tokens = ctypes.c_int64(), ctypes.c_int64()
+    st = lib.oracle_image_grid(height, width, patch, merge, min_pixels, max_pixels,
+                               float(max_aspect), _ptr(g), ctypes.byref(rows),
+                               ctypes.byref(tokens))
+    if st != OK:
+        raise OracleError(st, f"image_grid({height}, {width})")
+    return tuple(int(v) for v in g), rows.value, tokens.value
+
+
+def flatten_rgba(rgba: np.ndarray) -> np.ndarray:
+    """_to_rgb: RGBA [..., 4] uint8 flattened onto white -> RGB [..., 3] uint8."""
+    rgba = np.ascontiguousarray(rgba, dtype=np.uint8)
+    assert rgba.shape[-1] == 4
+    npix = rgba.size // 4
+    out = np.empty(rgba.shape[:-1] + (3,), dtype=np.uint8)
+    _load().oracle_flatten_rgba(_ptr(rgba), npix, _ptr(out))
+    return out
+
+
+def resize_bilinear(planar: np.ndarray, out_h: int, out_w: int) -> np.ndarray:
+    """resize_bilinear: planar float32 [C, H, W] -> [C, out_h, out_w]."""
+    planar = np.ascontiguousarray(planar, dtype=np.float32)
+    c, h, w = planar.shape
+    out = np.empty((c, out_h, out_w), dtype=np.float32)
+    _load().oracle_resize_bilinear(_ptr(planar), c, h, w, _ptr(out), out_h, out_w)
+    return out
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns (uint16), round to nearest even."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().oracle_to_bf16(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def _stats(mean255, std255):
+    m = np.ascontiguousarray(np.asarray(mean255, dtype=np.float32).reshape(3))
+    s = np.ascontiguousarray(np.asarray(std255, dtype=np.float32).reshape(3))
+    return m, s
+
+
+def preprocess_image(hwc: np.ndarray, out_h: int, out_w: int, mean255, std255,
+                     patch: int = PATCH, merge: int = MERGE,
+                     temporal: int = TEMPORAL) -> np.ndarray:
+    """_process_one / prepare_image for one uint8 HWC image (C = 3 or 4).
+
+    Returns float32 rows [(out_h/patch)*(out_w/patch), 3*temporal*patch*patch]
+    in merge-block order.
+    """
+    hwc = np.ascontiguousarray(hwc, dtype=np.uint8)
+    h, w, c = hwc.shape
+    m, s = _stats(mean255, std255)
+    rows = (out_h // patch) * (out_w // patch)
+    out = np.empty((rows, 3 * temporal * patch * patch), dtype=np.float32)
+    st = _load().oracle_preprocess_image(_ptr(hwc), h, w, c, out_h, out_w, patch, merge,
+                                         temporal, _ptr(m), _ptr(s), _ptr(out))
+    if st != OK:
+        raise OracleError(st, "preprocess_image")
+    return out
+
+
+def preprocess_rows(hwc: np.ndarray, out_h: int, out_w: int, mean255, std255,
+                    row_begin: int, row_count: int, patch: int = PATCH,
+                    merge: int = MERGE, temporal: int = TEMPORAL) -> np.ndarray:
+    """Rows [row_begin, row_begin+row_count) of preprocess_image, computed
+    one element at a time (for sampling large batches)."""
+    hwc = np.ascontiguousarray(hwc, dtype=np.uint8)
+    h, w, c = hwc.shape
+    m, s = _stats(mean255, std255)
+    out = np.empty((row_count, 3 * temporal * patch * patch), dtype=np.float32)
+    st = _load().oracle_preprocess_rows(_ptr(hwc), h, w, c, out_h, out_w, patch, merge,
+                                        temporal, _ptr(m), _ptr(s), row_begin, row_count,
+                                        _ptr(out))
+    if st != OK:
+        raise OracleError(st, "preprocess_rows")
+    return out
+
+
+def column_permutation(grid_t: int, grid_h: int, grid_w: int, merge: int = MERGE) -> np.ndarray:
+    """cortiq column_permutation: perm[dst] = src, int64 [gt*gh*gw]."""
+    perm = np.empty(grid_t * grid_h * grid_w, dtype=np.int64)
+    st = _load().oracle_column_permutation(grid_t, grid_h, grid_w, merge, _ptr(perm))
+    if st != OK:
+        raise OracleError(st, "column_permutation")
+    return perm
+
+
+def stats255(mean, std):
+    """Statistics in 0-255 units as float32: 255*mean and 255*std formed in
+    float64 and rounded once (the processor's 0-255 normalisation)."""
+    m = np.asarray([255.0 * float(v) for v in mean], dtype=np.float64).astype(np.float32)
+    s = np.asarray([255.0 * float(v) for v in std], dtype=np.float64).astype(np.float32)
+    return m, s

@@ -1,0 +1,443 @@
+/*
+ * oracle.c -- plain, slow CPU oracle of the MiMo-V2 image pixel path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library.  The product path
+ * (the HIP library under vision_image_preprocessing_amd/) never calls it and
+ * shares no code, header, table or helper with it.
+ *
+ * Every function follows the definition on the pages, step by step, with
+ * materialised intermediates and no blocking or fusion:
+ *
+ *   - NeMo Automodel "nemo_automodel.components.models.mimo_v2_flash.processing"
+ *     (module docstring; MimoV2ImageProcessor class docstring and defaults;
+ *      smart_resize; _to_rgb; get_number_of_image_patches),
+ *   - docs.rs "cortiq_engine::mimo_vision" (module conventions list;
+ *      resize_bilinear; column_permutation; smart_resize).
+ *
+ * Precision: the pages fix the resize as torch F.interpolate(bilinear,
+ * align_corners=False) on a float32 tensor of 0-255 values, so the resize and
+ * standardisation are carried out in float32 with the coordinate and weight
+ * arithmetic torch uses (fp32 scale, single-rounded fused multiply-add for the
+ * source coordinate, fp32 weights, W taps nested inside H taps).  Geometry is
+ * done in float64 exactly as Python evaluates it.  Build with
+ * -ffp-contract=off so that the only fused operations are the explicit fmaf.
+ *
+ * Parity pins (tests/test_oracle_*.py): geometry against the transformers
+ * Qwen2-VL smart_resize and hand-derived cases; flatten against PIL on all
+ * 65,536 (value, alpha) pairs; resize against torch CPU F.interpolate and
+ * against a float64 evaluation within a derived bound; layout against a
+ * coded image and a tensor reshape formulation; permutation against brute
+ * force; bf16 rounding against torch.  No function here is "parity unpinned".
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_OK 0
+#define ORC_E_INVALID (-1)
+#define ORC_E_ASPECT (-2)
+#define ORC_E_DEGENERATE (-3)
+#define ORC_E_NOMEM (-4)
+
+/* ------------------------------------------------------------------------ */
+/* Geometry: smart_resize with the MiMo / sglang semantics.                  */
+/* ------------------------------------------------------------------------ */
+
+/* Python's built-in round() on a float: nearest integer, ties to even. */
+static double py_round(double v)
+{
+    double f = floor(v);
+    double frac = v - f;
+    if (frac < 0.5)
+        return f;
+    if (frac > 0.5)
+        return f + 1.0;
+    return (fmod(f, 2.0) == 0.0) ? f : f + 1.0;
+}
+
+/*
+ * smart_resize(height, width, factor, min_pixels, max_pixels) -> (h, w).
+ *
+ * processing page, smart_resize: the Qwen2-VL algorithm (round each side to
+ * a multiple of factor; if the area is above max_pixels shrink by
+ * beta = sqrt(h*w/max) and floor; if below min_pixels grow by
+ * beta = sqrt(min/(h*w)) and ceil) with two changes:
+ *   (i)  a short side below factor is first scaled up to factor, both sides
+ *        by the same ratio, and that branch skips the aspect guard;
+ *   (ii) a shrink that floors a side to zero is rejected, not clamped.
+ * Readings where the pages are silent: the aspect guard rejects a long/short
+ * ratio strictly above max_aspect (200 in the Qwen2-VL routine); the
+ * upscaled sides are the exact ratios side*factor/short, rounded once to
+ * float64, and they replace the originals in every later step.
+ */
+int oracle_smart_resize(int64_t height, int64_t width, int64_t factor,
+                        int64_t min_pixels, int64_t max_pixels,
+                        double max_aspect, int64_t *out_h, int64_t *out_w)
+{
+    if (height < 1 || width < 1 || factor < 1 || min_pixels < 0 ||
+        max_pixels < 1 || min_pixels > max_pixels)
+        return ORC_E_INVALID;
+
+    int64_t short_side = height < width ? height : width;
+    int64_t long_side = height < width ? width : height;
+    double h, w;
+    if (short_side < factor) {
+        /* upscale branch: the short side becomes exactly factor */
+        h = (double)(height * factor) / (double)short_side;
+        w = (double)(width * factor) / (double)short_side;
+    } else {
+        if ((double)long_side / (double)short_side > max_aspect)
+            return ORC_E_ASPECT;
+        h = (double)height;
+        w = (double)width;
+    }
+
+    double f = (double)factor;
+    double h_bar = py_round(h / f) * f;
+    double w_bar = py_round(w / f) * f;
+    if (h_bar * w_bar > (double)max_pixels) {
+        double beta = sqrt(h * w / (double)max_pixels);
+        h_bar = floor(h / beta / f) * f;
+        w_bar = floor(w / beta / f) * f;
+        if (h_bar == 0.0 || w_bar == 0.0)
+            return ORC_E_DEGENERATE;
+    } else if (h_bar * w_bar < (double)min_pixels) {
+        double beta = sqrt((double)min_pixels / (h * w));
+        h_bar = ceil(h * beta / f) * f;
+        w_bar = ceil(w * beta / f) * f;
+    }
+    *out_h = (int64_t)h_bar;
+    *out_w = (int64_t)w_bar;
+    return ORC_OK;
+}
+
+/*
+ * Grid, patch and token counts for one image.
+ * get_number_of_image_patches: grid_h*grid_w patches before the merge**2
+ * reduction; rows of pixel_values = grid_t*grid_h*grid_w; each image is
+ * temporal_patch_size identical frames, so grid_t = 1; placeholder tokens
+ * are patches / merge**2.
+ */
+int oracle_image_grid(int64_t height, int64_t width, int64_t patch,
+                      int64_t merge, int64_t min_pixels, int64_t max_pixels,
+                      double max_aspect, int64_t *grid_thw /* [3] */,
+                      int64_t *rows, int64_t *tokens)
+{
+    int64_t rh, rw;
+    int st = oracle_smart_resize(height, width, patch * merge, min_pixels,
+                                 max_pixels, max_aspect, &rh, &rw);
+    if (st != ORC_OK)
+        return st;
+    grid_thw[0] = 1;
+    grid_thw[1] = rh / patch;
+    grid_thw[2] = rw / patch;
+    *rows = grid_thw[0] * grid_thw[1] * grid_thw[2];
+    *tokens = *rows / (merge * merge);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Colour: RGBA flattened onto white (_to_rgb).                               */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * One channel of a pixel composited over an opaque white background with
+ * coverage a/255, rounded to the nearest 8-bit value:
+ *   out = value * a/255 + 255 * (1 - a/255).
+ * The compositing happens on 8-bit pixels, before the float cast.
+ */
+static uint8_t flatten_on_white(uint8_t value, uint8_t alpha)
+{
+    double cover = (double)alpha / 255.0;
+    double mixed = (double)value * cover + 255.0 * (1.0 - cover);
+    return (uint8_t)floor(mixed + 0.5);
+}
+
+void oracle_flatten_rgba(const uint8_t *rgba, int64_t npix, uint8_t *rgb)
+{
+    for (int64_t i = 0; i < npix; ++i) {
+        uint8_t a = rgba[4 * i + 3];
+        for (int c = 0; c < 3; ++c)
+            rgb[3 * i + c] = flatten_on_white(rgba[4 * i + c], a);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Resize: F.interpolate(bilinear, align_corners=False), no antialias.       */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Half-pixel source coordinate for destination index d on an axis mapped
+ * from n_in to n_out samples, clamped below at zero, and its two taps:
+ *   scale = n_in / n_out                     (float32 division)
+ *   src   = scale * (d + 0.5) - 0.5          (one fused multiply-add)
+ *   i0 = floor(src), l1 = src - i0, l0 = 1 - l1,
+ *   i1 = i0 + 1, or i0 at the last sample.
+ */
+static void bilinear_tap(int64_t n_in, int64_t n_out, int64_t d, int64_t *i0,
+                         int64_t *i1, float *l0, float *l1)
+{
+    float scale = (float)n_in / (float)n_out;
+    float src = fmaf(scale, (float)d + 0.5f, -0.5f);
+    if (src < 0.0f)
+        src = 0.0f;
+    float fl = floorf(src);
+    int64_t lo = (int64_t)fl;
+    if (lo > n_in - 1)
+        lo = n_in - 1;
+    *i0 = lo;
+    *i1 = lo < n_in - 1 ? lo + 1 : lo;
+    *l1 = src - (float)lo;
+    *l0 = 1.0f - *l1;
+}
+
+/*
+ * Planar float32 [C][H][W] -> [C][OH][OW].  For each output sample:
+ * interpolate along W on the two source rows, then along H:
+ *   t_y = l0x * v[y][x0] + l1x * v[y][x1]
+ *   out = l0y * t_y0    + l1y * t_y1
+ * each evaluated as fmaf(first weight, first value, second product).
+ */
+void oracle_resize_bilinear(const float *src, int64_t C, int64_t H, int64_t W,
+                            float *dst, int64_t OH, int64_t OW)
+{
+    for (int64_t c = 0; c < C; ++c) {
+        const float *plane = src + c * H * W;
+        for (int64_t y = 0; y < OH; ++y) {
+            int64_t y0, y1;
+            float ly0, ly1;
+            bilinear_tap(H, OH, y, &y0, &y1, &ly0, &ly1);
+            for (int64_t x = 0; x < OW; ++x) {
+                int64_t x0, x1;
+                float lx0, lx1;
+                bilinear_tap(W, OW, x, &x0, &x1, &lx0, &lx1);
+                float top = fmaf(lx0, plane[y0 * W + x0],
+                                 lx1 * plane[y0 * W + x1]);
+                float bot = fmaf(lx0, plane[y1 * W + x0],
+                                 lx1 * plane[y1 * W + x1]);
+                dst[(c * OH + y) * OW + x] = fmaf(ly0, top, ly1 * bot);
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* bf16: round to nearest, ties to even.                                      */
+/* ------------------------------------------------------------------------ */
+
+static float bits_to_float(uint32_t u)
+{
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/*
+ * The two bf16 values bracketing x are the float32 values whose low 16
+ * mantissa bits are zero: truncation toward zero and the next one away from
+ * zero.  Pick the nearer; on a tie pick the one with an even last bit.
+ * (Inputs here are finite.)
+ */
+void oracle_to_bf16(const float *x, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        uint32_t u;
+        memcpy(&u, &x[i], 4);
+        uint32_t toward = u >> 16;
+        uint32_t away = toward + 1;
+        double dx = (double)x[i];
+        double d_toward = fabs(dx - (double)bits_to_float(toward << 16));
+        double d_away = fabs((double)bits_to_float(away << 16) - dx);
+        uint32_t pick;
+        if (d_toward < d_away)
+            pick = toward;
+        else if (d_away < d_toward)
+            pick = away;
+        else
+            pick = (toward & 1u) ? away : toward;
+        out[i] = (uint16_t)pick;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* One image through the whole pixel path (_process_one / prepare_image).    */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * hwc: uint8 [H][W][C], C = 3 (RGB) or 4 (RGBA).  (OH, OW) is the
+ * smart_resize target.  mean255/std255 are the per-channel statistics in
+ * 0-255 units.  Output: (OH/patch)*(OW/patch) rows of
+ * 3*temporal*patch*patch float32 values.
+ *
+ * Steps, in the order of the MimoV2ImageProcessor docstring:
+ *  1. RGBA flattened onto white (RGB passes through);
+ *  2. cast to float32, 0-255, planar [3][H][W];
+ *  3. bilinear resize to [3][OH][OW];
+ *  4. standardise (x - mean255[c]) / std255[c] in float32;
+ *  5. duplicate the frame temporal times (T identical frames);
+ *  6. patchify: row r = ((br*Bw + bc)*merge + mh)*merge + mw lists the patch
+ *     at patch row br*merge+mh, patch column bc*merge+mw (merge-block order,
+ *     (t, block row, block col, mh, mw)); element
+ *     e = ((c*temporal + tt)*patch + py)*patch + px is the Conv3d kernel
+ *     flattened as (c, tt, py, px).
+ */
+int oracle_preprocess_image(const uint8_t *hwc, int64_t H, int64_t W,
+                            int64_t C, int64_t OH, int64_t OW, int64_t patch,
+                            int64_t merge, int64_t temporal,
+                            const float *mean255, const float *std255,
+                            float *rows_out)
+{
+    if (H < 1 || W < 1 || (C != 3 && C != 4) || patch < 1 || merge < 1 ||
+        temporal < 1 || OH % (patch * merge) != 0 || OW % (patch * merge) != 0 ||
+        OH < 1 || OW < 1)
+        return ORC_E_INVALID;
+
+    int64_t npix = H * W;
+    uint8_t *rgb = (uint8_t *)malloc((size_t)(npix * 3));
+    float *planar = (float *)malloc(sizeof(float) * (size_t)(3 * npix));
+    float *resized = (float *)malloc(sizeof(float) * (size_t)(3 * OH * OW));
+    float *frames = (float *)malloc(sizeof(float) * (size_t)(temporal * 3 * OH * OW));
+    if (!rgb || !planar || !resized || !frames) {
+        free(rgb);
+        free(planar);
+        free(resized);
+        free(frames);
+        return ORC_E_NOMEM;
+    }
+
+    /* 1. colour */
+    if (C == 4)
+        oracle_flatten_rgba(hwc, npix, rgb);
+    else
+        memcpy(rgb, hwc, (size_t)(npix * 3));
+
+    /* 2. cast, HWC -> planar CHW */
+    for (int64_t c = 0; c < 3; ++c)
+        for (int64_t i = 0; i < npix; ++i)
+            planar[c * npix + i] = (float)rgb[3 * i + c];
+
+    /* 3. resize */
+    oracle_resize_bilinear(planar, 3, H, W, resized, OH, OW);
+
+    /* 4. standardise */
+    for (int64_t c = 0; c < 3; ++c)
+        for (int64_t i = 0; i < OH * OW; ++i)
+            resized[c * OH * OW + i] = (resized[c * OH * OW + i] - mean255[c]) / std255[c];
+
+    /* 5. duplicate along the temporal axis */
+    for (int64_t t = 0; t < temporal; ++t)
+        memcpy(frames + t * 3 * OH * OW, resized, sizeof(float) * (size_t)(3 * OH * OW));
+
+    /* 6. patchify in merge-block order */
+    int64_t gh = OH / patch, gw = OW / patch;
+    int64_t bh = gh / merge, bw = gw / merge;
+    int64_t row_len = 3 * temporal * patch * patch;
+    for (int64_t br = 0; br < bh; ++br)
+        for (int64_t bc = 0; bc < bw; ++bc)
+            for (int64_t mh = 0; mh < merge; ++mh)
+                for (int64_t mw = 0; mw < merge; ++mw) {
+                    int64_t r = ((br * bw + bc) * merge + mh) * merge + mw;
+                    float *row = rows_out + r * row_len;
+                    for (int64_t c = 0; c < 3; ++c)
+                        for (int64_t tt = 0; tt < temporal; ++tt)
+                            for (int64_t py = 0; py < patch; ++py)
+                                for (int64_t px = 0; px < patch; ++px) {
+                                    int64_t y = (br * merge + mh) * patch + py;
+                                    int64_t x = (bc * merge + mw) * patch + px;
+                                    int64_t e = ((c * temporal + tt) * patch + py) * patch + px;
+                                    row[e] = frames[((tt * 3 + c) * OH + y) * OW + x];
+                                }
+                }
+
+    free(rgb);
+    free(planar);
+    free(resized);
+    free(frames);
+    return ORC_OK;
+}
+
+/*
+ * The same values as oracle_preprocess_image, computed one output element at
+ * a time for a range of rows, without materialising the image.  Used to
+ * check sampled rows of batches too large to run through the full path.
+ */
+static float source_value(const uint8_t *hwc, int64_t W, int64_t C, int64_t y,
+                          int64_t x, int64_t c)
+{
+    const uint8_t *p = hwc + (y * W + x) * C;
+    uint8_t v = C == 4 ? flatten_on_white(p[c], p[3]) : p[c];
+    return (float)v;
+}
+
+int oracle_preprocess_rows(const uint8_t *hwc, int64_t H, int64_t W, int64_t C,
+                           int64_t OH, int64_t OW, int64_t patch,
+                           int64_t merge, int64_t temporal,
+                           const float *mean255, const float *std255,
+                           int64_t row_begin, int64_t row_count,
+                           float *rows_out)
+{
+    if (H < 1 || W < 1 || (C != 3 && C != 4) || patch < 1 || merge < 1 ||
+        temporal < 1 || OH % (patch * merge) != 0 || OW % (patch * merge) != 0)
+        return ORC_E_INVALID;
+    int64_t gh = OH / patch, gw = OW / patch;
+    int64_t bw = gw / merge;
+    int64_t unit = merge * merge;
+    int64_t row_len = 3 * temporal * patch * patch;
+    if (row_begin < 0 || row_count < 0 || row_begin + row_count > gh * gw)
+        return ORC_E_INVALID;
+
+    for (int64_t k = 0; k < row_count; ++k) {
+        int64_t r = row_begin + k;
+        /* invert r = ((br*bw + bc)*merge + mh)*merge + mw */
+        int64_t block = r / unit, in_unit = r % unit;
+        int64_t br = block / bw, bc = block % bw;
+        int64_t mh = in_unit / merge, mw = in_unit % merge;
+        float *row = rows_out + k * row_len;
+        for (int64_t c = 0; c < 3; ++c)
+            for (int64_t tt = 0; tt < temporal; ++tt)
+                for (int64_t py = 0; py < patch; ++py)
+                    for (int64_t px = 0; px < patch; ++px) {
+                        int64_t y = (br * merge + mh) * patch + py;
+                        int64_t x = (bc * merge + mw) * patch + px;
+                        int64_t y0, y1, x0, x1;
+                        float ly0, ly1, lx0, lx1;
+                        bilinear_tap(H, OH, y, &y0, &y1, &ly0, &ly1);
+                        bilinear_tap(W, OW, x, &x0, &x1, &lx0, &lx1);
+                        float top = fmaf(lx0, source_value(hwc, W, C, y0, x0, c),
+                                         lx1 * source_value(hwc, W, C, y0, x1, c));
+                        float bot = fmaf(lx0, source_value(hwc, W, C, y1, x0, c),
+                                         lx1 * source_value(hwc, W, C, y1, x1, c));
+                        float v = fmaf(ly0, top, ly1 * bot);
+                        int64_t e = ((c * temporal + tt) * patch + py) * patch + px;
+                        row[e] = (v - mean255[c]) / std255[c];
+                    }
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* column_permutation (cortiq_engine::mimo_vision).                           */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Rows of one image reordered into column order: merge units listed by
+ * (t, block col, block row) instead of (t, block row, block col), each
+ * unit's merge**2 rows kept together in their own order.  perm[dst] = src.
+ */
+int oracle_column_permutation(int64_t grid_t, int64_t grid_h, int64_t grid_w,
+                              int64_t merge, int64_t *perm)
+{
+    if (grid_t < 1 || grid_h < 1 || grid_w < 1 || merge < 1 ||
+        grid_h % merge != 0 || grid_w % merge != 0)
+        return ORC_E_INVALID;
+    int64_t bh = grid_h / merge, bw = grid_w / merge, unit = merge * merge;
+    int64_t dst = 0;
+    for (int64_t t = 0; t < grid_t; ++t)
+        for (int64_t bc = 0; bc < bw; ++bc)
+            for (int64_t br = 0; br < bh; ++br)
+                for (int64_t k = 0; k < unit; ++k)
+                    perm[dst++] = ((t * bh + br) * bw + bc) * unit + k;
+    return ORC_OK;
+}
