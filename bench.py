@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Throughput of the MiMo-V2 image pixel path on one MI355X.
+
+A step is one pass of the whole pixel path over one batch: one call of
+mimo_preprocess_batch, which uploads the batch's descriptor table and runs
+the fused kernel (flatten, cast, bilinear resize, standardise, two frames,
+patch rows in merge-block order and, for the throughput batch, the same rows
+in column order).  Inputs are resident in HBM before timing starts.
+
+Default workload: 512 RGB uint8 1024x1024 images (seeded uniform pixels),
+ImageNet statistics, float32 rows in merge-block and column order.
+
+Prints one JSON line: images/s, step time, achieved algorithmic HBM
+bandwidth of the fused kernel against the 8 TB/s peak, and the CPU oracle
+timed on a bounded sample of the same batch.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "images/s and achieved HBM GB/s (% of peak), 1×MI355X, preprocess_batch"
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "vision_image_preprocessing_amd", "csrc", "preprocess.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def algorithmic_bytes(plan, out_bytes_per_value: int, outputs: int) -> dict:
+    """uint8 sources read once + every output row written once per output
+    (1536 values per row, both frames counted)."""
+    read = int(plan.total_src_bytes)
+    write = int(plan.total_rows) * 1536 * out_bytes_per_value * outputs
+    return {"read": read, "write": write, "total": read + write}
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE counters,
+    scaled by the copy-kernel calibration, if they were taken on the
+    current kernel source; else None."""
+    path = os.path.join(PROFILES, f"preprocess_kernel_{workload}.traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(batch, plan, sample: int, threads: int) -> dict:
+    """The oracle, as it is, on the first `sample` images, one image per
+    thread at a time."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+
+    m, s = oracle.stats255(batch.mean, batch.std)
+    idx = list(range(min(sample, len(batch))))
+
+    def one(i):
+        d = plan.desc[i]
+        oracle.preprocess_image(batch.image(i), int(d["dst_h"]), int(d["dst_w"]), m, s)
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(one, idx))
+    dt = time.perf_counter() - t0
+    return {"value": len(idx) / dt, "unit": "images/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {len(idx)} of {len(batch)} images of the same batch, one image per "
+                      f"thread, {threads} threads, {dt:.2f} s wall",
+            "seconds": dt, "cpu_model": platform.processor() or platform.machine()}
+
+
+def calibrate_copy(gib: float, reps: int):
+    """A plain elementwise copy kernel of known size (read N bytes, write N
+    bytes) for scaling the HBM byte counters."""
+    import torch
+
+    n = int(gib * (1 << 30)) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        torch.mul(a, 1.0, out=b)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "elementwise copy", "bytes_read": 4 * n,
+                      "bytes_written": 4 * n, "launches": reps}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="throughput_512_1024")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=96)
+    ap.add_argument("--gather", action="store_true",
+                    help="also time the standalone column_permute gather kernel")
+    ap.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GIB",
+                    help="only run a plain copy kernel of this size (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this pixel path runs on one GPU only (asked for {args.gpus} GPUs, "
+              f"WORLD_SIZE={world}); run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    if args.calibrate_copy > 0:
+        calibrate_copy(args.calibrate_copy, max(args.steps, 1))
+        return
+
+    import vision_image_preprocessing_amd as V
+    import workloads
+
+    V.load()  # fails loudly if the HIP library is not built
+    log("generating", args.workload)
+    batch = workloads.WORKLOADS[args.workload]()
+    plan = V.plan_batch(batch.shapes)
+    src = V.processor.upload_sources(batch.packed, plan)
+    out_dtype = batch.out_dtype
+    tdtype = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    bpv = 4 if out_dtype == "f32" else 2
+    rows = torch.empty((plan.total_rows, 1536), dtype=tdtype, device="cuda")
+    rows_col = torch.empty_like(rows) if batch.column_order else None
+    ws = torch.empty(V.workspace_bytes(len(plan)), dtype=torch.uint8, device="cuda")
+    alg = algorithmic_bytes(plan, bpv, 2 if batch.column_order else 1)
+
+    def step():
+        V.preprocess(src, plan, mean=batch.mean, std=batch.std, out_dtype=out_dtype,
+                     merge_order=True, column_order=batch.column_order, rows=rows,
+                     rows_col=rows_col, workspace=ws)
+
+    log("warmup", args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    dispatch0 = V.dispatch_count()
+    torch.cuda.synchronize()
+    t_begin.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    assert V.dispatch_count() == dispatch0 + args.steps
+    total_ms = t_begin.elapsed_time(t_end)
+    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    mean_launch_ms = float(np.mean(per_launch_ms))
+    log(f"timed {args.steps} steps: {total_ms:.3f} ms")
+
+    n_img = len(batch)
+    achieved = alg["total"] / (mean_launch_ms * 1e-3) / 1e9
+    traffic = measured_traffic(args.workload)
+    result = {
+        "metric": METRIC,
+        "value": n_img * args.steps / (total_ms * 1e-3),
+        "unit": "images/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": total_ms / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "images": n_img,
+            "source": "uint8 " + ("mixed sizes" if len(set(batch.shapes)) > 1 else
+                                  "{}x{}x{}".format(*batch.shapes[0])),
+            "output": f"{out_dtype} rows [{plan.total_rows}, 1536]" +
+                      (" in merge-block and column order" if batch.column_order else
+                       " in merge-block order"),
+            "statistics": "ImageNet" if tuple(batch.mean) == workloads.IMAGENET_MEAN else "CLIP",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": traffic,
+        },
+        "algorithmic_bytes_per_step": alg,
+        "kernel": "preprocess_kernel<float>" if out_dtype == "f32" else "preprocess_kernel<bf16>",
+        "launch_ms_mean": mean_launch_ms,
+        "launch_ms_min": float(np.min(per_launch_ms)),
+        "launch_ms_median": float(np.median(per_launch_ms)),
+        "published_throughput": "none (the pages publish no throughput for this path)",
+    }
+
+    if args.gather and rows_col is not None:
+        gathered = torch.empty_like(rows)
+        for _ in range(2):
+            V.column_permute(plan.desc, rows, gathered, ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        e0.record(stream)
+        for _ in range(reps):
+            V.column_permute(plan.desc, rows, gathered, ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        gb = 2 * plan.total_rows * 1536 * bpv / (ms * 1e-3) / 1e9
+        result["column_permute_gather"] = {"ms": ms, "GB/s": gb, "frac": gb / HBM_PEAK_GBPS}
+        del gathered
+
+    if not args.no_cpu_baseline:
+        threads = max(1, min(16, os.cpu_count() or 1))
+        log("cpu baseline (oracle)", args.cpu_sample, "images,", threads, "threads")
+        result["cpu_baseline"] = cpu_baseline(batch, plan, args.cpu_sample, threads)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,202 @@
+/*
+ * mimo_pre.h -- C ABI of the MI355X (gfx950) MiMo-V2 image pixel path.
+ *
+ * The pixel path, as defined on the pages this library implements:
+ *   NeMo Automodel "mimo_v2_flash.processing" (module docstring, the
+ *   MimoV2ImageProcessor class docstring and defaults, smart_resize, _to_rgb,
+ *   get_number_of_image_patches) and docs.rs "cortiq_engine::mimo_vision"
+ *   (module conventions, resize_bilinear, column_permutation, smart_resize):
+ *
+ *   uint8 RGB or RGBA image -> RGBA flattened onto white -> float 0-255 ->
+ *   bilinear resize (align_corners=False, no antialias, no 8-bit round trip)
+ *   to the smart_resize target -> (x - mean255[c]) / std255[c] -> two
+ *   identical frames -> rows of 3*2*16*16 = 1536 values, the Conv3d kernel
+ *   flattened as (c, tt, py, px), listed in merge-block order
+ *   (t, block row, block col, mh, mw); optionally also in column order
+ *   (t, block col, block row), each merge unit's 4 rows kept together.
+ *
+ * Conventions for every entry point:
+ *   - Plain C types only.  "device" pointers are HIP device memory on the
+ *     current device; "host" pointers are ordinary host memory.
+ *   - The caller owns every buffer.  The library never frees caller memory.
+ *   - Functions return MIMO_OK (0) or a negative MIMO_E_* code; nothing is
+ *     thrown across the ABI.  mimo_last_error() gives a message for the last
+ *     failure on the calling thread.
+ *   - GPU work is enqueued on the given stream (a hipStream_t passed as
+ *     void*, NULL = the null stream) and is asynchronous: outputs are valid
+ *     once the stream has reached the enqueued work.
+ *   - Thread safety: all entry points may be called concurrently from
+ *     different threads.
+ */
+#ifndef MIMO_PRE_H
+#define MIMO_PRE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define MIMO_OK 0
+#define MIMO_E_INVALID (-1)     /* bad argument: size <= 0, null pointer, std <= 0, ... */
+#define MIMO_E_ASPECT (-2)      /* long/short side ratio above max_aspect (short side >= factor) */
+#define MIMO_E_DEGENERATE (-3)  /* shrink to max_pixels floors a side to zero */
+#define MIMO_E_UNSUPPORTED (-4) /* parameters the kernels do not implement */
+#define MIMO_E_CAPACITY (-5)    /* an output or workspace buffer is too small */
+#define MIMO_E_HIP (-6)         /* HIP runtime error (message in mimo_last_error) */
+#define MIMO_E_TOO_LARGE (-7)   /* a size exceeds the library's index limits */
+
+/* ---- output element types ---------------------------------------------- */
+#define MIMO_F32 0  /* float32 */
+#define MIMO_BF16 1 /* bfloat16, rounded to nearest even from the float32 value */
+
+/*
+ * Processor knobs (processing page, MimoV2ImageProcessor signature; cortiq
+ * MimoProcessorConfig).  factor = patch_size * merge_size.
+ * The kernels implement patch_size 16, merge_size 2, temporal_patch_size 2
+ * (rows of 1536 values); the geometry functions accept any positive values.
+ * max_aspect is the aspect guard of the Qwen2-VL smart_resize (200); a ratio
+ * strictly above it is rejected on the branch whose short side is >= factor.
+ */
+typedef struct mimo_params {
+    int32_t patch_size;          /* 16 */
+    int32_t merge_size;          /* 2 */
+    int32_t temporal_patch_size; /* 2 */
+    int32_t reserved0;           /* must be 0 */
+    int64_t min_pixels;          /* 8192: lower bound on the resized area */
+    int64_t max_pixels;          /* 8388608: upper bound on the resized area */
+    double max_aspect;           /* 200 */
+} mimo_params;
+
+/* Fills *p with the defaults above. */
+void mimo_default_params(mimo_params *p);
+
+/*
+ * Per-image plan, produced by mimo_plan_geometry and consumed unchanged by
+ * mimo_preprocess_batch and mimo_column_permute.  64 bytes.
+ *   src_offset  byte offset of the image in the packed source buffer; images
+ *               are packed back to back in batch order, each row-major
+ *               uint8 [src_h][src_w][channels].
+ *   row_offset  first output row of this image (rows of all images are
+ *               concatenated in batch order).
+ *   rows        grid_t * grid_h * grid_w (get_number_of_image_patches);
+ *               placeholder tokens = rows / merge_size^2.
+ *   dst_h/dst_w smart_resize target; grid_h = dst_h / patch_size,
+ *               grid_w = dst_w / patch_size, grid_t = 1 (two identical
+ *               frames make one temporal patch): image_grid_thw.
+ *   status      MIMO_OK or the image's MIMO_E_* code; a failed image has
+ *               rows = 0 and contributes no output.
+ */
+typedef struct mimo_image_desc {
+    int64_t src_offset;
+    int64_t row_offset;
+    int64_t rows;
+    int32_t src_h, src_w, channels;
+    int32_t dst_h, dst_w;
+    int32_t grid_t, grid_h, grid_w;
+    int32_t status;
+    int32_t reserved;
+} mimo_image_desc;
+
+/*
+ * smart_resize (processing page; cortiq smart_resize): resize target for one
+ * h x w image with factor = patch_size * merge_size.  Round each side to the
+ * nearest multiple of factor (ties to even); if the area exceeds max_pixels
+ * shrink both sides by sqrt(h*w/max_pixels) and floor to the factor; if it
+ * is below min_pixels grow by sqrt(min_pixels/(h*w)) and ceil.  A short side
+ * below factor is first scaled up to factor (both sides by the same ratio)
+ * and that branch skips the aspect guard; a shrink that floors a side to
+ * zero is rejected.
+ * Host only.  Returns MIMO_OK, MIMO_E_INVALID (h, w < 1 or bad params),
+ * MIMO_E_ASPECT or MIMO_E_DEGENERATE; *out_h, *out_w untouched on error.
+ */
+int mimo_smart_resize(int64_t h, int64_t w, const mimo_params *params, int64_t *out_h,
+                      int64_t *out_w);
+
+/*
+ * Plans a batch of n images (host only, no allocation).
+ *   hwc        host int32 [n][3]: height, width, channels (3 = RGB, 4 = RGBA).
+ *   params     NULL for the defaults.
+ *   out        host [n] descriptors, written in batch order.
+ *   total_rows host, nullable: sum of rows (the pixel_values row count).
+ *   total_src_bytes host, nullable: packed source size in bytes.
+ * Every image is planned; a failing image gets its code in out[i].status and
+ * rows = 0.  Returns MIMO_OK, or the first failing image's code.
+ */
+int mimo_plan_geometry(int32_t n, const int32_t *hwc, const mimo_params *params,
+                       mimo_image_desc *out, int64_t *total_rows, int64_t *total_src_bytes);
+
+/* Bytes of device workspace mimo_preprocess_batch / mimo_column_permute need
+ * for n images (descriptor tables copied from the host on each call). */
+size_t mimo_workspace_bytes(int32_t n);
+
+/*
+ * The fused pixel path for a whole batch: flatten, cast, bilinear resize,
+ * standardise, two frames, patch rows -- one kernel launch (after one
+ * asynchronous host-to-device copy of the descriptor tables into the
+ * workspace).
+ *   n, desc      host: the plan from mimo_plan_geometry (params must be the
+ *                defaults' patch/merge/temporal sizes).  Images whose status
+ *                is not MIMO_OK are skipped.
+ *   src          device: packed uint8 sources, 4-byte aligned.
+ *   src_capacity bytes readable at src; must be >= the packed size rounded
+ *                up to a multiple of 16 (the kernels read whole 16-byte
+ *                words; bytes past the images are read and ignored).
+ *   mean255, std255  host float[3]: per-channel statistics in 0-255 units
+ *                (255 * mean, 255 * std); std255 > 0.
+ *   out_dtype    MIMO_F32 or MIMO_BF16.
+ *   rows         device, nullable: [capacity_rows][1536] merge-block order.
+ *   rows_col     device, nullable: [capacity_rows][1536] column order.  At
+ *                least one of rows / rows_col is non-null.  16-byte aligned.
+ *   capacity_rows rows available in each non-null output (>= total rows).
+ *   workspace    device, >= mimo_workspace_bytes(n) bytes, 16-byte aligned;
+ *                must stay untouched until the kernel has run.
+ *   stream       hipStream_t.
+ * Returns MIMO_OK, MIMO_E_INVALID, MIMO_E_UNSUPPORTED, MIMO_E_CAPACITY,
+ * MIMO_E_TOO_LARGE or MIMO_E_HIP.
+ */
+int mimo_preprocess_batch(int32_t n, const mimo_image_desc *desc, const uint8_t *src,
+                          int64_t src_capacity, const float *mean255, const float *std255,
+                          int32_t out_dtype, void *rows, void *rows_col, int64_t capacity_rows,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * column_permutation (cortiq mimo_vision): for one image with grid
+ * (grid_t, grid_h, grid_w) and merge size m, perm[dst] = src lists the merge
+ * units by (t, block col, block row), each unit's m*m rows kept together.
+ * Host only.  perm: host int64 [grid_t*grid_h*grid_w].  Returns MIMO_OK or
+ * MIMO_E_INVALID (non-positive sizes, grid not divisible by m).
+ */
+int mimo_column_permutation(int64_t grid_t, int64_t grid_h, int64_t grid_w, int64_t merge,
+                            int64_t *perm);
+
+/*
+ * Gather kernel: rows_out[row_offset_i + d] = rows_in[row_offset_i + perm_i[d]]
+ * for every image i (perm_i from mimo_column_permutation), i.e. merge-order
+ * rows -> column-order rows.  Not in place (rows_out != rows_in).
+ *   n, desc      host plan (as for mimo_preprocess_batch).
+ *   rows_in, rows_out  device [capacity_rows][1536] of out_dtype, 16-byte aligned.
+ *   workspace    device, >= mimo_workspace_bytes(n).
+ * Returns MIMO_OK, MIMO_E_INVALID, MIMO_E_CAPACITY or MIMO_E_HIP.
+ */
+int mimo_column_permute(int32_t n, const mimo_image_desc *desc, const void *rows_in,
+                        void *rows_out, int32_t out_dtype, int64_t capacity_rows,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static text for a status code. */
+const char *mimo_status_string(int status);
+
+/* Message for the last failure on the calling thread ("" if none). */
+const char *mimo_last_error(void);
+
+/* Number of kernel launches this process has made through the library (a
+ * proof that timings come from the GPU path). */
+int64_t mimo_dispatch_count(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MIMO_PRE_H */

@@ -1,0 +1,22 @@
+"""MI355X-native MiMo-V2 image pixel path.
+
+The pixel path of the pages (NeMo Automodel ``mimo_v2_flash.processing``,
+class ``MimoV2ImageProcessor``; docs.rs ``cortiq_engine::mimo_vision``):
+RGBA flattened onto white, cast to 0-255 float, bilinear resize
+(align_corners=False, no antialias) to the smart_resize target, per-channel
+standardisation in 0-255 units, two identical frames, Conv3d patch rows of
+1536 values in merge-block order, and optionally the column-order
+permutation.  All of it runs in hand-written HIP kernels for gfx950 behind
+the C ABI in ``include/mimo_pre.h``; this package is the ctypes binding plus
+a batch helper that allocates torch device buffers.
+"""
+from __future__ import annotations
+
+from ._abi import (  # noqa: F401
+    IMAGE_DESC_DTYPE, MIMO_BF16, MIMO_E_ASPECT, MIMO_E_CAPACITY, MIMO_E_DEGENERATE,
+    MIMO_E_HIP, MIMO_E_INVALID, MIMO_E_TOO_LARGE, MIMO_E_UNSUPPORTED, MIMO_F32, MIMO_OK,
+    ROW_LEN, LibraryNotBuilt, MimoError, MimoParams, column_permutation, column_permute,
+    default_params, dispatch_count, last_error, load, make_params, plan_geometry,
+    preprocess_batch, smart_resize, status_string, workspace_bytes,
+)
+from .processor import BatchPlan, plan_batch, preprocess, stats255  # noqa: F401

@@ -1,0 +1,244 @@
+"""ctypes binding of libmimopre.so (the C ABI declared in include/mimo_pre.h).
+
+Argument marshalling only: every step of the pixel path runs in the HIP
+library.  PyTorch supplies device memory (``data_ptr()``) and the current
+HIP stream.  Importing this module does not need a GPU; loading the library
+fails loudly if it has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import numpy as np
+
+from .build import LIB_PATH
+
+MIMO_OK = 0
+MIMO_E_INVALID = -1
+MIMO_E_ASPECT = -2
+MIMO_E_DEGENERATE = -3
+MIMO_E_UNSUPPORTED = -4
+MIMO_E_CAPACITY = -5
+MIMO_E_HIP = -6
+MIMO_E_TOO_LARGE = -7
+
+MIMO_F32 = 0
+MIMO_BF16 = 1
+
+ROW_LEN = 1536  # 3 channels x 2 frames x 16 x 16
+
+# mimo_image_desc, 64 bytes (include/mimo_pre.h)
+IMAGE_DESC_DTYPE = np.dtype([
+    ("src_offset", "<i8"), ("row_offset", "<i8"), ("rows", "<i8"),
+    ("src_h", "<i4"), ("src_w", "<i4"), ("channels", "<i4"),
+    ("dst_h", "<i4"), ("dst_w", "<i4"),
+    ("grid_t", "<i4"), ("grid_h", "<i4"), ("grid_w", "<i4"),
+    ("status", "<i4"), ("reserved", "<i4"),
+])
+assert IMAGE_DESC_DTYPE.itemsize == 64
+
+
+class MimoParams(ctypes.Structure):
+    """mimo_params: processor knobs (patch, merge, temporal, pixel bounds,
+    aspect guard)."""
+    _fields_ = [
+        ("patch_size", ctypes.c_int32),
+        ("merge_size", ctypes.c_int32),
+        ("temporal_patch_size", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32),
+        ("min_pixels", ctypes.c_int64),
+        ("max_pixels", ctypes.c_int64),
+        ("max_aspect", ctypes.c_double),
+    ]
+
+
+class MimoError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{message} [status {code}]")
+        self.code = code
+
+
+class LibraryNotBuilt(RuntimeError):
+    pass
+
+
+# exported symbol -> (argtypes, restype)
+_P, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+SIGNATURES = {
+    "mimo_default_params": ([_P], None),
+    "mimo_smart_resize": ([_I64, _I64, _P, _P, _P], ctypes.c_int),
+    "mimo_plan_geometry": ([_I32, _P, _P, _P, _P, _P], ctypes.c_int),
+    "mimo_workspace_bytes": ([_I32], _SZ),
+    "mimo_preprocess_batch": ([_I32, _P, _P, _I64, _P, _P, _I32, _P, _P, _I64, _P, _SZ, _P],
+                              ctypes.c_int),
+    "mimo_column_permutation": ([_I64, _I64, _I64, _I64, _P], ctypes.c_int),
+    "mimo_column_permute": ([_I32, _P, _P, _P, _I32, _I64, _P, _SZ, _P], ctypes.c_int),
+    "mimo_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "mimo_last_error": ([], ctypes.c_char_p),
+    "mimo_dispatch_count": ([], _I64),
+}
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Loads the in-tree HIP library; raises LibraryNotBuilt if it is missing."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise LibraryNotBuilt(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -c 'import __graft_entry__ as g; g.build()'` (hipcc, gfx950)")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = lib
+        return lib
+
+
+def _check(code: int, what: str):
+    if code != MIMO_OK:
+        raise MimoError(code, f"{what}: {last_error() or status_string(code)}")
+
+
+def status_string(code: int) -> str:
+    return load().mimo_status_string(code).decode()
+
+
+def last_error() -> str:
+    return load().mimo_last_error().decode()
+
+
+def dispatch_count() -> int:
+    return int(load().mimo_dispatch_count())
+
+
+def default_params() -> MimoParams:
+    p = MimoParams()
+    load().mimo_default_params(ctypes.byref(p))
+    return p
+
+
+def make_params(min_pixels=None, max_pixels=None, **kw) -> MimoParams:
+    """Defaults with per-call pixel-bound overrides (MimoV2ImageProcessor
+    __call__ accepts min_pixels / max_pixels per call)."""
+    p = default_params()
+    if min_pixels is not None:
+        p.min_pixels = int(min_pixels)
+    if max_pixels is not None:
+        p.max_pixels = int(max_pixels)
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def smart_resize(height: int, width: int, params: MimoParams | None = None):
+    """mimo_smart_resize -> (resized_height, resized_width)."""
+    oh, ow = ctypes.c_int64(), ctypes.c_int64()
+    code = load().mimo_smart_resize(int(height), int(width),
+                                    ctypes.byref(params) if params is not None else None,
+                                    ctypes.byref(oh), ctypes.byref(ow))
+    _check(code, "smart_resize")
+    return oh.value, ow.value
+
+
+def plan_geometry(hwc, params: MimoParams | None = None, check: bool = True):
+    """mimo_plan_geometry over an [n, 3] (height, width, channels) table.
+
+    Returns (desc, total_rows, total_src_bytes, status) where desc is a
+    structured numpy array of IMAGE_DESC_DTYPE.  With check=True a failing
+    image raises MimoError; otherwise per-image codes are in desc['status'].
+    """
+    hwc = np.ascontiguousarray(np.asarray(hwc, dtype=np.int32).reshape(-1, 3))
+    n = hwc.shape[0]
+    desc = np.zeros(n, dtype=IMAGE_DESC_DTYPE)
+    total_rows, total_src = ctypes.c_int64(), ctypes.c_int64()
+    code = load().mimo_plan_geometry(n, hwc.ctypes.data,
+                                     ctypes.byref(params) if params is not None else None,
+                                     desc.ctypes.data, ctypes.byref(total_rows),
+                                     ctypes.byref(total_src))
+    if check:
+        _check(code, "plan_geometry")
+    return desc, total_rows.value, total_src.value, code
+
+
+def workspace_bytes(n: int) -> int:
+    return int(load().mimo_workspace_bytes(int(n)))
+
+
+def column_permutation(grid_t: int, grid_h: int, grid_w: int, merge: int = 2) -> np.ndarray:
+    """mimo_column_permutation: perm[dst] = src (int64)."""
+    perm = np.empty(int(grid_t) * int(grid_h) * int(grid_w), dtype=np.int64)
+    code = load().mimo_column_permutation(grid_t, grid_h, grid_w, merge, perm.ctypes.data)
+    _check(code, "column_permutation")
+    return perm
+
+
+def _stream_handle(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(int(stream.cuda_stream))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return MIMO_F32
+    if t.dtype == torch.bfloat16:
+        return MIMO_BF16
+    raise MimoError(MIMO_E_INVALID, f"output dtype {t.dtype} is not float32 or bfloat16")
+
+
+def preprocess_batch(desc: np.ndarray, src, mean255, std255, rows=None, rows_col=None,
+                     workspace=None, stream=None):
+    """mimo_preprocess_batch.  src: uint8 device tensor (packed images,
+    length >= packed size rounded up to 16); rows / rows_col: float32 or
+    bfloat16 device tensors [capacity, 1536] (either may be None);
+    workspace: uint8 device tensor of >= workspace_bytes(n) bytes.
+    Enqueues on `stream` (default: torch's current stream)."""
+    desc = np.ascontiguousarray(desc, dtype=IMAGE_DESC_DTYPE)
+    n = desc.shape[0]
+    out = rows if rows is not None else rows_col
+    if out is None:
+        raise MimoError(MIMO_E_INVALID, "preprocess_batch: both outputs are None")
+    code_dtype = _dtype_code(out)
+    cap = None
+    for t in (rows, rows_col):
+        if t is None:
+            continue
+        if _dtype_code(t) != code_dtype or t.dim() != 2 or t.shape[1] != ROW_LEN or not t.is_contiguous():
+            raise MimoError(MIMO_E_INVALID, "preprocess_batch: outputs must be contiguous "
+                                            "[capacity, 1536] tensors of one dtype")
+        cap = t.shape[0] if cap is None else min(cap, t.shape[0])
+    m = (ctypes.c_float * 3)(*[float(v) for v in mean255])
+    s = (ctypes.c_float * 3)(*[float(v) for v in std255])
+    code = load().mimo_preprocess_batch(
+        n, desc.ctypes.data, src.data_ptr(), src.numel(), m, s, code_dtype,
+        rows.data_ptr() if rows is not None else None,
+        rows_col.data_ptr() if rows_col is not None else None,
+        cap, workspace.data_ptr() if workspace is not None else None,
+        workspace.numel() if workspace is not None else 0,
+        _stream_handle(stream, out.device))
+    _check(code, "preprocess_batch")
+
+
+def column_permute(desc: np.ndarray, rows_in, rows_out, workspace, stream=None):
+    """mimo_column_permute: merge-order rows -> column-order rows (gather)."""
+    desc = np.ascontiguousarray(desc, dtype=IMAGE_DESC_DTYPE)
+    n = desc.shape[0]
+    code_dtype = _dtype_code(rows_in)
+    if _dtype_code(rows_out) != code_dtype:
+        raise MimoError(MIMO_E_INVALID, "column_permute: dtype mismatch")
+    cap = min(rows_in.shape[0], rows_out.shape[0])
+    code = load().mimo_column_permute(n, desc.ctypes.data, rows_in.data_ptr(), rows_out.data_ptr(),
+                                      code_dtype, cap, workspace.data_ptr(), workspace.numel(),
+                                      _stream_handle(stream, rows_in.device))
+    _check(code, "column_permute")

@@ -1,0 +1,232 @@
+// plan.cpp -- host-side geometry of the MiMo-V2 pixel path: smart_resize,
+// the per-image plan of a batch, and the column permutation indices.
+//
+// Pages: NeMo Automodel "mimo_v2_flash.processing" (smart_resize,
+// get_number_of_image_patches, MimoV2ImageProcessor defaults) and docs.rs
+// "cortiq_engine::mimo_vision" (smart_resize, column_permutation).
+#include <algorithm>
+#include <cfenv>
+#include <cmath>
+#include <cstring>
+#include <string>
+
+#include "internal.h"
+
+namespace mimo {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+int set_error(int code, const std::string &msg) {
+    g_last_error = msg;
+    return code;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+namespace {
+
+bool params_ok(const mimo_params &p) {
+    return p.patch_size > 0 && p.merge_size > 0 && p.temporal_patch_size > 0 &&
+           p.reserved0 == 0 && p.min_pixels >= 0 && p.max_pixels > 0 &&
+           p.min_pixels <= p.max_pixels && p.max_aspect > 0.0;
+}
+
+// Nearest integer with ties to even -- the rounding of Python's round(),
+// which the Qwen2-VL smart_resize applies to side / factor.  nearbyint()
+// rounds in the current mode, which is round-to-nearest-even by default.
+double round_ties_even(double v) {
+    const int mode = std::fegetround();
+    if (mode != FE_TONEAREST) std::fesetround(FE_TONEAREST);
+    const double r = std::nearbyint(v);
+    if (mode != FE_TONEAREST) std::fesetround(mode);
+    return r;
+}
+
+// smart_resize with factor f.  Sides are carried as float64 the way the
+// Python routine carries them; a short side below f is first scaled to f
+// (the long side by the same ratio, one float64 rounding) and that branch
+// skips the aspect guard; a shrink that floors a side to zero is rejected.
+int smart_resize_impl(int64_t h, int64_t w, int64_t f, int64_t min_px, int64_t max_px,
+                      double max_aspect, int64_t *oh, int64_t *ow) {
+    const int64_t lo = std::min(h, w);
+    const int64_t hi = std::max(h, w);
+    double sh, sw;
+    if (lo < f) {
+        sh = double(h * f) / double(lo);
+        sw = double(w * f) / double(lo);
+    } else {
+        if (double(hi) / double(lo) > max_aspect) return MIMO_E_ASPECT;
+        sh = double(h);
+        sw = double(w);
+    }
+    const double fd = double(f);
+    double th = round_ties_even(sh / fd) * fd;
+    double tw = round_ties_even(sw / fd) * fd;
+    if (th * tw > double(max_px)) {
+        const double beta = std::sqrt(sh * sw / double(max_px));
+        th = std::floor(sh / beta / fd) * fd;
+        tw = std::floor(sw / beta / fd) * fd;
+        if (th < fd || tw < fd) return MIMO_E_DEGENERATE;
+    } else if (th * tw < double(min_px)) {
+        const double beta = std::sqrt(double(min_px) / (sh * sw));
+        th = std::ceil(sh * beta / fd) * fd;
+        tw = std::ceil(sw * beta / fd) * fd;
+    }
+    *oh = int64_t(th);
+    *ow = int64_t(tw);
+    return MIMO_OK;
+}
+
+}  // namespace
+}  // namespace mimo
+
+using namespace mimo;
+
+extern "C" {
+
+void mimo_default_params(mimo_params *p) {
+    if (!p) return;
+    std::memset(p, 0, sizeof(*p));
+    p->patch_size = 16;
+    p->merge_size = 2;
+    p->temporal_patch_size = 2;
+    p->min_pixels = 8192;
+    p->max_pixels = 8388608;
+    p->max_aspect = 200.0;
+}
+
+int mimo_smart_resize(int64_t h, int64_t w, const mimo_params *params, int64_t *out_h,
+                      int64_t *out_w) {
+    clear_error();
+    mimo_params def;
+    mimo_default_params(&def);
+    const mimo_params &p = params ? *params : def;
+    if (!out_h || !out_w) return set_error(MIMO_E_INVALID, "smart_resize: null output pointer");
+    if (!params_ok(p)) return set_error(MIMO_E_INVALID, "smart_resize: invalid parameters");
+    if (h < 1 || w < 1)
+        return set_error(MIMO_E_INVALID, "smart_resize: sides must be >= 1, got " +
+                                             std::to_string(h) + "x" + std::to_string(w));
+    const int64_t f = int64_t(p.patch_size) * p.merge_size;
+    // keep h*f and h*w exact in int64 / float64
+    if (h > (int64_t(1) << 31) || w > (int64_t(1) << 31))
+        return set_error(MIMO_E_TOO_LARGE, "smart_resize: side above 2^31");
+    int64_t oh = 0, ow = 0;
+    const int st = smart_resize_impl(h, w, f, p.min_pixels, p.max_pixels, p.max_aspect, &oh, &ow);
+    if (st == MIMO_E_ASPECT)
+        return set_error(st, "smart_resize: aspect ratio of " + std::to_string(h) + "x" +
+                                 std::to_string(w) + " exceeds max_aspect");
+    if (st == MIMO_E_DEGENERATE)
+        return set_error(st, "smart_resize: shrinking " + std::to_string(h) + "x" +
+                                 std::to_string(w) + " to max_pixels floors a side to zero");
+    *out_h = oh;
+    *out_w = ow;
+    return MIMO_OK;
+}
+
+int mimo_plan_geometry(int32_t n, const int32_t *hwc, const mimo_params *params,
+                       mimo_image_desc *out, int64_t *total_rows, int64_t *total_src_bytes) {
+    clear_error();
+    if (n < 0 || (n > 0 && (!hwc || !out)))
+        return set_error(MIMO_E_INVALID, "plan_geometry: bad n or null pointer");
+    mimo_params def;
+    mimo_default_params(&def);
+    const mimo_params &p = params ? *params : def;
+    if (!params_ok(p)) return set_error(MIMO_E_INVALID, "plan_geometry: invalid parameters");
+    const int64_t patch = p.patch_size;
+    const int64_t merge = p.merge_size;
+
+    int first_error = MIMO_OK;
+    std::string first_msg;
+    int64_t src_off = 0, row_off = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        mimo_image_desc d;
+        std::memset(&d, 0, sizeof(d));
+        const int32_t h = hwc[3 * i], w = hwc[3 * i + 1], c = hwc[3 * i + 2];
+        d.src_h = h;
+        d.src_w = w;
+        d.channels = c;
+        d.src_offset = src_off;
+        d.row_offset = row_off;
+        int st = MIMO_OK;
+        std::string msg;
+        if (h < 1 || w < 1 || (c != 3 && c != 4)) {
+            st = MIMO_E_INVALID;
+            msg = "image " + std::to_string(i) + ": bad shape";
+        } else if (h > kMaxSide || w > kMaxSide) {
+            st = MIMO_E_TOO_LARGE;
+            msg = "image " + std::to_string(i) + ": side above 2^23 - 1";
+        } else {
+            int64_t oh = 0, ow = 0;
+            st = smart_resize_impl(h, w, patch * merge, p.min_pixels, p.max_pixels, p.max_aspect,
+                                   &oh, &ow);
+            if (st == MIMO_OK && (oh > kMaxSide || ow > kMaxSide)) {
+                st = MIMO_E_TOO_LARGE;
+                msg = "image " + std::to_string(i) + ": resized side above 2^23 - 1";
+            } else if (st != MIMO_OK) {
+                msg = "image " + std::to_string(i) + ": " + mimo_status_string(st);
+            } else {
+                d.dst_h = int32_t(oh);
+                d.dst_w = int32_t(ow);
+                d.grid_t = 1;
+                d.grid_h = int32_t(oh / patch);
+                d.grid_w = int32_t(ow / patch);
+                d.rows = int64_t(d.grid_t) * d.grid_h * d.grid_w;
+            }
+        }
+        d.status = st;
+        if (st != MIMO_OK && first_error == MIMO_OK) {
+            first_error = st;
+            first_msg = msg;
+        }
+        if (h > 0 && w > 0 && c > 0) src_off += int64_t(h) * w * c;
+        row_off += d.rows;
+        out[i] = d;
+    }
+    if (total_rows) *total_rows = row_off;
+    if (total_src_bytes) *total_src_bytes = src_off;
+    if (first_error != MIMO_OK) return set_error(first_error, "plan_geometry: " + first_msg);
+    return MIMO_OK;
+}
+
+size_t mimo_workspace_bytes(int32_t n) { return n < 0 ? 0 : ws_total_bytes(n); }
+
+int mimo_column_permutation(int64_t grid_t, int64_t grid_h, int64_t grid_w, int64_t merge,
+                            int64_t *perm) {
+    clear_error();
+    if (grid_t < 1 || grid_h < 1 || grid_w < 1 || merge < 1 || !perm || grid_h % merge ||
+        grid_w % merge)
+        return set_error(MIMO_E_INVALID, "column_permutation: bad grid or null output");
+    const int64_t bh = grid_h / merge, bw = grid_w / merge, unit = merge * merge;
+    // destination unit j of frame t is (block col, block row) = divmod(j, bh);
+    // its source unit is block row * bw + block col of the same frame.
+    for (int64_t t = 0; t < grid_t; ++t) {
+        const int64_t frame = t * bh * bw;
+        for (int64_t j = 0; j < bh * bw; ++j) {
+            const int64_t bc = j / bh, br = j % bh;
+            const int64_t src_unit = frame + br * bw + bc;
+            int64_t *dst = perm + (frame + j) * unit;
+            for (int64_t k = 0; k < unit; ++k) dst[k] = src_unit * unit + k;
+        }
+    }
+    return MIMO_OK;
+}
+
+const char *mimo_status_string(int status) {
+    switch (status) {
+        case MIMO_OK: return "ok";
+        case MIMO_E_INVALID: return "invalid argument";
+        case MIMO_E_ASPECT: return "aspect ratio above max_aspect";
+        case MIMO_E_DEGENERATE: return "degenerate shrink (a side floors to zero)";
+        case MIMO_E_UNSUPPORTED: return "unsupported parameters";
+        case MIMO_E_CAPACITY: return "buffer too small";
+        case MIMO_E_HIP: return "HIP runtime error";
+        case MIMO_E_TOO_LARGE: return "size above the library's index limits";
+        default: return "unknown status";
+    }
+}
+
+const char *mimo_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,98 @@
+"""Batch helper over the C ABI: plan a batch, place its packed uint8 sources
+in device memory, allocate outputs with torch, and run the fused kernel.
+
+This is the equivalent of MimoV2ImageProcessor.__call__ (processing page):
+images in, ``pixel_values`` [total_patches, 1536] and ``image_grid_thw``
+[n, 3] out, in input order.  Decoding is out of scope: images arrive as
+uint8 HWC arrays (RGB or RGBA).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from . import _abi
+
+# MimoV2ImageProcessor defaults (processing page): ImageNet statistics.
+IMAGENET_MEAN = (0.485, 0.456, 0.406)
+IMAGENET_STD = (0.229, 0.224, 0.225)
+
+
+def stats255(mean, std):
+    """Statistics in 0-255 units as float32 (products formed in float64)."""
+    m = [float(np.float32(255.0 * float(v))) for v in mean]
+    s = [float(np.float32(255.0 * float(v))) for v in std]
+    return m, s
+
+
+@dataclass
+class BatchPlan:
+    desc: np.ndarray          # IMAGE_DESC_DTYPE [n]
+    total_rows: int
+    total_src_bytes: int
+
+    @property
+    def src_capacity(self) -> int:
+        """Device bytes for the packed sources: the kernels read whole
+        16-byte words, so the buffer is padded to a multiple of 16."""
+        return max(16, (self.total_src_bytes + 15) // 16 * 16)
+
+    @property
+    def image_grid_thw(self) -> np.ndarray:
+        return np.stack([self.desc["grid_t"], self.desc["grid_h"], self.desc["grid_w"]],
+                        axis=1).astype(np.int64)
+
+    def __len__(self):
+        return int(self.desc.shape[0])
+
+
+def plan_batch(shapes, min_pixels=None, max_pixels=None, check: bool = True) -> BatchPlan:
+    """Plans images given as (height, width, channels) tuples."""
+    params = _abi.make_params(min_pixels, max_pixels)
+    desc, rows, src, _ = _abi.plan_geometry(np.asarray(shapes, dtype=np.int32).reshape(-1, 3),
+                                            params, check=check)
+    return BatchPlan(desc=desc, total_rows=rows, total_src_bytes=src)
+
+
+def upload_sources(packed: np.ndarray, plan: BatchPlan, device="cuda"):
+    """Copies packed uint8 images (back to back, batch order) into a padded
+    device buffer."""
+    import torch
+    buf = torch.zeros(plan.src_capacity, dtype=torch.uint8, device=device)
+    flat = torch.from_numpy(np.ascontiguousarray(packed).reshape(-1))
+    buf[:flat.numel()].copy_(flat)
+    return buf
+
+
+def preprocess(src_dev, plan: BatchPlan, mean=IMAGENET_MEAN, std=IMAGENET_STD,
+               out_dtype: str = "f32", merge_order: bool = True, column_order: bool = False,
+               stream=None, rows=None, rows_col=None, workspace=None):
+    """Runs the fused pixel path on a planned batch.
+
+    Returns a dict with ``pixel_values`` (merge-block order, or None),
+    ``pixel_values_col`` (column order, or None) and ``image_grid_thw``.
+    Preallocated ``rows`` / ``rows_col`` / ``workspace`` tensors may be
+    passed to keep allocation out of a timed loop.
+    """
+    import torch
+    dev = src_dev.device
+    tdtype = {"f32": torch.float32, "bf16": torch.bfloat16}[out_dtype]
+    n_rows = max(plan.total_rows, 1)
+    if merge_order and rows is None:
+        rows = torch.empty((n_rows, _abi.ROW_LEN), dtype=tdtype, device=dev)
+    if column_order and rows_col is None:
+        rows_col = torch.empty((n_rows, _abi.ROW_LEN), dtype=tdtype, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(_abi.workspace_bytes(len(plan)), 16), dtype=torch.uint8,
+                                device=dev)
+    m255, s255 = stats255(mean, std)
+    _abi.preprocess_batch(plan.desc, src_dev, m255, s255,
+                          rows=rows if merge_order else None,
+                          rows_col=rows_col if column_order else None,
+                          workspace=workspace, stream=stream)
+    return {
+        "pixel_values": rows if merge_order else None,
+        "pixel_values_col": rows_col if column_order else None,
+        "image_grid_thw": torch.from_numpy(plan.image_grid_thw),
+    }
