@@ -78,7 +78,8 @@ def _to_np(t):
     return t.float().cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy()
 
 
-def _check_full(V, batch, plan, out, out_dtype, images=None, column=False):
+def _check_full(V, batch, plan, out, out_dtype, images=None, column=False, min_pixels=None,
+                max_pixels=None):
     m, s = _stats(batch)
     rows = out["pixel_values"]
     rows_col = out["pixel_values_col"]
@@ -88,7 +89,9 @@ def _check_full(V, batch, plan, out, out_dtype, images=None, column=False):
         if d["status"] != 0:
             continue
         h, w, c = batch.shapes[i]
-        g, nrows, _ = oracle.image_grid(h, w)
+        bounds = dict(min_pixels=oracle.MIN_PIXELS if min_pixels is None else min_pixels,
+                      max_pixels=oracle.MAX_PIXELS if max_pixels is None else max_pixels)
+        g, nrows, _ = oracle.image_grid(h, w, **bounds)
         assert (d["grid_t"], d["grid_h"], d["grid_w"]) == g and d["rows"] == nrows
         ref = oracle.preprocess_image(batch.image(i), int(d["dst_h"]), int(d["dst_w"]), m, s)
         r0, r1 = int(d["row_offset"]), int(d["row_offset"] + d["rows"])
@@ -147,7 +150,7 @@ def test_large_downscale_uses_global_taps(V):
     b = W.uniform_images([(3000, 2600, 3), (2048, 4000, 4)], seed=8)
     plan, out = _run(V, b, max_pixels=40000)
     assert plan.desc["dst_h"][0] < 3000 / 8
-    _check_full(V, b, plan, out, "f32")
+    _check_full(V, b, plan, out, "f32", max_pixels=40000)
     _check_properties(out)
 
 

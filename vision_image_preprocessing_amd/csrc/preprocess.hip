@@ -31,8 +31,11 @@
 // float(n_in)/float(n_out) (host), src = fma(scale, d + 0.5, -0.5) clamped
 // at 0, i0 = floor(src), l1 = src - i0, l0 = 1 - l1, i1 = min(i0+1, n_in-1);
 // t = fma(l0x, v00, l1x*v01) per source row, out = fma(l0y, t0, l1y*t1).
-// Standardisation is one fma: out * (1/std255) + (-mean255/std255), within
-// a few float32 ulps of (out - mean255) / std255.
+// Standardisation is (out - mean255) * (1/std255): the subtraction is the
+// same as in (out - mean255) / std255 (exact near the mean), and the product
+// with the rounded reciprocal stays within two float32 ulps of the quotient
+// (relative), so a bf16 rounding of it is within one bf16 ulp even for
+// outputs near zero.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -64,8 +67,8 @@ struct PreArgs {
     int64_t src_end;            // bytes readable from src
     int32_t n;
     int32_t band_capacity;      // dwords of dynamic LDS
-    float coef_a[3];            // 1 / std255
-    float coef_b[3];            // -mean255 / std255
+    float inv_std[3];           // 1 / std255, rounded once
+    float mean[3];              // mean255
 };
 
 struct PermArgs {
@@ -212,7 +215,7 @@ __device__ __forceinline__ void compute_patch(const Pixels &px, const DevImage &
         for (int j = 0; j < 4; ++j) {
             const uint32_t p = px.at(oy, ox0 + j);
 #pragma unroll
-            for (int c = 0; c < 3; ++c) v[c][j] = __builtin_fmaf(chan(p, c), a.coef_a[c], a.coef_b[c]);
+            for (int c = 0; c < 3; ++c) v[c][j] = (chan(p, c) - a.mean[c]) * a.inv_std[c];
         }
     } else {
         const Tap ty = make_tap(d.scale_y, oy, d.src_h);
@@ -228,7 +231,7 @@ __device__ __forceinline__ void compute_patch(const Pixels &px, const DevImage &
                 const float top = __builtin_fmaf(tx.l0, chan(p00, c), tx.l1 * chan(p01, c));
                 const float bot = __builtin_fmaf(tx.l0, chan(p10, c), tx.l1 * chan(p11, c));
                 const float val = __builtin_fmaf(ty.l0, top, ty.l1 * bot);
-                v[c][j] = __builtin_fmaf(val, a.coef_a[c], a.coef_b[c]);
+                v[c][j] = (val - a.mean[c]) * a.inv_std[c];
             }
         }
     }
@@ -554,8 +557,8 @@ int mimo_preprocess_batch(int32_t n, const mimo_image_desc *desc, const uint8_t 
     for (int c = 0; c < 3; ++c) {
         if (!(std255[c] > 0.0f) || !std::isfinite(std255[c]) || !std::isfinite(mean255[c]))
             return set_error(MIMO_E_INVALID, "preprocess_batch: std255 must be > 0 and finite");
-        a.coef_a[c] = float(1.0 / double(std255[c]));
-        a.coef_b[c] = float(-double(mean255[c]) / double(std255[c]));
+        a.inv_std[c] = float(1.0 / double(std255[c]));
+        a.mean[c] = mean255[c];
     }
     BuiltTables t;
     int st = build_tables(n, desc, t);
