@@ -95,11 +95,18 @@ def calibrate_copy(gib: float, reps: int):
     n = int(gib * (1 << 30)) // 4
     a = torch.ones(n, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
+    torch.mul(a, 1.0, out=b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
     for _ in range(reps):
         torch.mul(a, 1.0, out=b)
+    e1.record()
     torch.cuda.synchronize()
-    print(json.dumps({"calibration": "elementwise copy", "bytes_read": 4 * n,
-                      "bytes_written": 4 * n, "launches": reps}), flush=True)
+    ms = e0.elapsed_time(e1) / reps
+    print(json.dumps({"calibration": "elementwise copy (torch.mul by 1.0)", "bytes_read": 4 * n,
+                      "bytes_written": 4 * n, "launches": reps + 1, "ms_per_launch": ms,
+                      "GB/s": 8 * n / (ms * 1e-3) / 1e9}), flush=True)
 
 
 def main():
@@ -109,7 +116,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="throughput_512_1024")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=96)
+    ap.add_argument("--cpu-sample", type=int, default=512)
     ap.add_argument("--gather", action="store_true",
                     help="also time the standalone column_permute gather kernel")
     ap.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GIB",

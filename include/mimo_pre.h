@@ -46,7 +46,7 @@ extern "C" {
 #define MIMO_E_UNSUPPORTED (-4) /* parameters the kernels do not implement */
 #define MIMO_E_CAPACITY (-5)    /* an output or workspace buffer is too small */
 #define MIMO_E_HIP (-6)         /* HIP runtime error (message in mimo_last_error) */
-#define MIMO_E_TOO_LARGE (-7)   /* a size exceeds the library's index limits */
+#define MIMO_E_TOO_LARGE (-7)   /* a side >= 2^23 or an image of more than 2^24 rows */
 
 /* ---- output element types ---------------------------------------------- */
 #define MIMO_F32 0  /* float32 */

@@ -222,6 +222,27 @@ def test_back_to_back_calls_with_different_batches(V):
         assert torch.equal(o2["pixel_values"], outs[0][1]["pixel_values"])
 
 
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_output_order_choices_agree(V, out_dtype):
+    """Merge-only, column-only and both-orders calls write the same rows; the
+    gather kernel maps merge order to the same column order."""
+    _say("output order choices", out_dtype)
+    b = W.uniform_images(RAGGED_SHAPES[:12] + [(700, 1000, 4), (64, 2048, 3)], seed=41)
+    plan_m, out_m = _run(V, b, out_dtype, merge=True, column=False)
+    plan_c, out_c = _run(V, b, out_dtype, merge=False, column=True)
+    plan_b, out_b = _run(V, b, out_dtype, merge=True, column=True)
+    assert torch.equal(out_m["pixel_values"], out_b["pixel_values"])
+    assert torch.equal(out_c["pixel_values_col"], out_b["pixel_values_col"])
+    _check_properties(out_c)
+    ws = torch.empty(V.workspace_bytes(len(plan_m)), dtype=torch.uint8, device="cuda")
+    gathered = torch.full_like(out_m["pixel_values"], float("nan"))
+    V.column_permute(plan_m.desc, out_m["pixel_values"], gathered, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(gathered, out_c["pixel_values_col"])
+    # column order against the oracle's permutation, image by image
+    _check_full(V, b, plan_c, out_c, out_dtype, column=True, images=range(len(b)))
+
+
 # ------------------------------------------------------ workloads, full size
 def test_workload_single_rgb_300x200(V):
     _say("single_rgb_300x200")

@@ -23,6 +23,9 @@ constexpr int kPlane = kPatch * kPatch;                         // 256 values pe
 // Largest side the kernels index: coordinates are formed as float(d) + 0.5
 // and float(n_in), which are exact below 2^23.
 constexpr int64_t kMaxSide = (int64_t(1) << 23) - 1;
+// Largest row count of one image: per-image row and tile indices are formed
+// in 32-bit arithmetic with float-reciprocal quotients, exact below 2^24.
+constexpr int64_t kMaxRowsPerImage = int64_t(1) << 24;
 
 // Per-image record the fused kernel reads (64 bytes, one per image).
 struct DevImage {
@@ -33,11 +36,12 @@ struct DevImage {
     int32_t flags;          // kFlag* bits
     int32_t blocks_h;       // merge units per column  (grid_h / 2)
     int32_t blocks_w;       // merge units per row     (grid_w / 2)
-    int32_t units_per_tile; // merge units one workgroup covers along a block row
-    int32_t tiles_per_brow; // ceil(blocks_w / units_per_tile)
+    int32_t tiles_per_brow; // tiles along one block row (4 * blocks_w rows)
+    float inv_tiles_per_brow;  // 1 / tiles_per_brow (quotient estimate, corrected exactly)
     float scale_y;          // float32(src_h) / float32(dst_h)
     float scale_x;          // float32(src_w) / float32(dst_w)
-    int32_t reserved[2];
+    float inv_blocks_h;     // 1 / blocks_h
+    int32_t reserved;
 };
 static_assert(sizeof(DevImage) == 64, "DevImage must stay 64 bytes");
 

@@ -161,9 +161,10 @@ int mimo_plan_geometry(int32_t n, const int32_t *hwc, const mimo_params *params,
             int64_t oh = 0, ow = 0;
             st = smart_resize_impl(h, w, patch * merge, p.min_pixels, p.max_pixels, p.max_aspect,
                                    &oh, &ow);
-            if (st == MIMO_OK && (oh > kMaxSide || ow > kMaxSide)) {
+            if (st == MIMO_OK && (oh > kMaxSide || ow > kMaxSide ||
+                                  (oh / patch) * (ow / patch) > kMaxRowsPerImage)) {
                 st = MIMO_E_TOO_LARGE;
-                msg = "image " + std::to_string(i) + ": resized side above 2^23 - 1";
+                msg = "image " + std::to_string(i) + ": resized side above 2^23 - 1 or more than 2^24 rows";
             } else if (st != MIMO_OK) {
                 msg = "image " + std::to_string(i) + ": " + mimo_status_string(st);
             } else {

@@ -52,9 +52,9 @@ namespace mimo {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
+constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
 // LDS budget for one tile's source band, in dwords (one dword per pixel).
 constexpr int kBandBudgetDwords = 12288;  // 48 KB
-constexpr int kMaxUnitsPerTile = 4;
 // Buffer resource word 3 for raw (untyped) buffer loads on gfx9-family parts.
 constexpr int kBufferWord3 = 0x00020000;
 
@@ -65,8 +65,11 @@ struct PreArgs {
     void *rows;                 // merge-block order, nullable
     void *rows_col;             // column order, nullable
     int64_t src_end;            // bytes readable from src
+    int64_t tiles_per_pass;     // tiles of one output; a second pass follows for rows_col
     int32_t n;
     int32_t band_capacity;      // dwords of dynamic LDS
+    int32_t rows_per_tile;      // 1, 2 or a multiple of 4 (at most 4 with two outputs)
+    int32_t xcd_order;          // map workgroups to XCD-contiguous tile runs
     float inv_std[3];           // 1 / std255, rounded once
     float mean[3];              // mean255
 };
@@ -81,6 +84,11 @@ struct PermArgs {
 };
 
 // ---------------------------------------------------------------- helpers
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Largest i in [0, n) with begin[i] <= key (begin non-decreasing,
 // begin[0] = 0 <= key).  Each round one wavefront compares 64 evenly spaced
@@ -100,13 +108,23 @@ __device__ __forceinline__ int find_segment(const int64_t *__restrict__ begin, i
     return __builtin_amdgcn_readfirstlane(lo);
 }
 
+// n / d for 0 <= n < 2^24 and d >= 1, given inv = float(1 / d): the float
+// estimate is within one of the quotient and is corrected exactly.
+__device__ __forceinline__ int div_small(int n, int d, float inv) {
+    int q = int(float(n) * inv);
+    const int r = n - q * d;
+    q += (r >= d) - (r < 0);
+    return q;
+}
+
 struct Tap {
-    int i0, i1;
+    int i0;
     float l0, l1;
 };
 
-// Half-pixel source taps for destination index d on an axis of n_in source
-// samples (align_corners=False, clamped below at 0).
+// Half-pixel source coordinate for destination index d on an axis of n_in
+// source samples (align_corners=False, clamped below at 0): the first tap
+// and the two weights.  The second tap is i0 + 1, or i0 at the last sample.
 __device__ __forceinline__ Tap make_tap(float scale, int d, int n_in) {
     float s = __builtin_fmaf(scale, float(d) + 0.5f, -0.5f);
     s = s < 0.0f ? 0.0f : s;
@@ -114,7 +132,6 @@ __device__ __forceinline__ Tap make_tap(float scale, int d, int n_in) {
     i0 = i0 < n_in - 1 ? i0 : n_in - 1;
     Tap t;
     t.i0 = i0;
-    t.i1 = i0 < n_in - 1 ? i0 + 1 : i0;
     t.l1 = s - float(i0);
     t.l0 = 1.0f - t.l1;
     return t;
@@ -138,10 +155,6 @@ __device__ __forceinline__ uint32_t flatten_rgba(uint32_t px) {
 __device__ __forceinline__ float chan(uint32_t px, int c) {
     return float((px >> (8 * c)) & 255u);
 }
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -171,8 +184,102 @@ __device__ __forceinline__ void store_both_frames<uint16_t>(uint16_t *row_ptr, i
     __builtin_nontemporal_store(q, reinterpret_cast<u32x2 *>(p + kPlane));
 }
 
-// Pixel sources for the compute loop: LDS band or direct global reads.
-struct LdsPixels {
+// A raw buffer resource over [first & ~3, src_end): `lead` is first's offset
+// in it.  Reads past the end return zero.
+struct SourceWindow {
+    __amdgpu_buffer_rsrc_t rsrc;
+    uint32_t lead;
+};
+
+__device__ __forceinline__ SourceWindow source_window(const PreArgs &a, uint64_t first) {
+    const uint64_t base = first & ~uint64_t(3);
+    const uint64_t end = reinterpret_cast<uint64_t>(a.src) + uint64_t(a.src_end);
+    const uint64_t avail = end - base;
+    const int num = avail > 0x7FFFFFF0ull ? 0x7FFFFFF0 : int(avail);
+    SourceWindow w;
+    w.rsrc = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(base), 0, num, kBufferWord3);
+    w.lead = uint32_t(first - base);
+    return w;
+}
+
+// Four consecutive pixels starting `off` bytes into the window, as dwords
+// R | G<<8 | B<<16 (RGBA flattened onto white).  One buffer load of exactly
+// 12 (RGB) or 16 (RGBA) bytes when `off` is dword aligned, else a 16-byte
+// load (plus a dword for RGBA) realigned with v_alignbyte.
+__device__ __forceinline__ void load_4px(const SourceWindow &w, uint32_t off, int channels,
+                                         uint32_t (&p)[4]) {
+    const uint32_t al = off & ~3u;
+    const uint32_t sh = off & 3u;
+    if (channels == 3) {
+        uint32_t u0, u1, u2;
+        if (sh == 0) {
+            const u32x3 v = __builtin_bit_cast(u32x3, __builtin_amdgcn_raw_buffer_load_b96(w.rsrc, int(al), 0, 0));
+            u0 = v.x; u1 = v.y; u2 = v.z;
+        } else {
+            const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.rsrc, int(al), 0, 0));
+            u0 = __builtin_amdgcn_alignbyte(v.y, v.x, sh);
+            u1 = __builtin_amdgcn_alignbyte(v.z, v.y, sh);
+            u2 = __builtin_amdgcn_alignbyte(v.w, v.z, sh);
+        }
+        // bytes R0 G0 B0 R1 | G1 B1 R2 G2 | B2 R3 G3 B3 -> one pixel per dword
+        p[0] = u0 & 0x00FFFFFFu;
+        p[1] = __builtin_amdgcn_perm(u1, u0, 0x0C050403u);
+        p[2] = __builtin_amdgcn_perm(u2, u1, 0x0C040302u);
+        p[3] = u2 >> 8;
+    } else {
+        const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.rsrc, int(al), 0, 0));
+        if (sh == 0) {
+            p[0] = flatten_rgba(v.x); p[1] = flatten_rgba(v.y);
+            p[2] = flatten_rgba(v.z); p[3] = flatten_rgba(v.w);
+        } else {
+            const uint32_t v4 = __builtin_amdgcn_raw_buffer_load_b32(w.rsrc, int(al) + 16, 0, 0);
+            p[0] = flatten_rgba(__builtin_amdgcn_alignbyte(v.y, v.x, sh));
+            p[1] = flatten_rgba(__builtin_amdgcn_alignbyte(v.z, v.y, sh));
+            p[2] = flatten_rgba(__builtin_amdgcn_alignbyte(v.w, v.z, sh));
+            p[3] = flatten_rgba(__builtin_amdgcn_alignbyte(v4, v.w, sh));
+        }
+    }
+}
+
+// Destination of output row (br, bc, mh, mw): its merge-block position, or
+// its column-order position when `column`.
+template <typename OutT>
+__device__ __forceinline__ OutT *row_dest(OutT *out, const DevImage &d, int br, int bc, int mh,
+                                          int mw, bool column) {
+    const int64_t unit = column ? int64_t(bc) * d.blocks_h + br : int64_t(br) * d.blocks_w + bc;
+    const int64_t row = d.row_offset + unit * kRowsPerUnit + mh * kMerge + mw;
+    const int lane = threadIdx.x & 63;
+    return out + row * kRowLen + (lane >> 2) * kPatch + 4 * (lane & 3);
+}
+
+// Identity resize (dst == src): output pixel (y, x) is source pixel (y, x).
+// Each lane reads its 4 pixels straight from HBM; no LDS.
+template <typename OutT>
+__device__ __forceinline__ void identity_patch(const PreArgs &a, const DevImage &d,
+                                               const SourceWindow &w, int64_t row_bytes, int oy0,
+                                               int ox0, int br, int bc, int mh, int mw, OutT *out,
+                                               bool column) {
+    const int lane = threadIdx.x & 63;
+    const int py = lane >> 2, q = lane & 3;
+    const int oy = (br * kMerge + mh) * kPatch + py;
+    const int ox = (bc * kMerge + mw) * kPatch + 4 * q;
+    const uint32_t off = w.lead + uint32_t(int64_t(oy - oy0) * row_bytes) + uint32_t((ox - ox0) * d.channels);
+    uint32_t p[4];
+    load_4px(w, off, d.channels, p);
+    float v[3][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int c = 0; c < 3; ++c) v[c][j] = (chan(p[j], c) - a.mean[c]) * a.inv_std[c];
+    OutT *dst = row_dest(out, d, br, bc, mh, mw, column);
+#pragma unroll
+    for (int c = 0; c < 3; ++c) store_both_frames<OutT>(dst, c, v[c]);
+}
+
+// Source pixels for the bilinear taps.  Both give the pixel at (y, x) for
+// y <= n_rows and x <= n_cols, where row n_rows / column n_cols stand for
+// the last row / column (the second tap at the image edge).
+struct BandPixels {  // staged in LDS, edge already replicated
     const uint32_t *band;
     int pitch, r_lo, c_lo;
     __device__ __forceinline__ uint32_t at(int y, int x) const {
@@ -180,163 +287,170 @@ struct LdsPixels {
     }
 };
 
-struct GlobalPixels {
+struct GlobalPixels {  // straight from memory, clamped
     const uint8_t *img;
     int64_t row_bytes;
-    int channels;
+    int channels, h, w;
     __device__ __forceinline__ uint32_t at(int y, int x) const {
+        y = min(y, h - 1);
+        x = min(x, w - 1);
         const uint8_t *p = img + int64_t(y) * row_bytes + int64_t(x) * channels;
         const uint32_t px = uint32_t(p[0]) | (uint32_t(p[1]) << 8) | (uint32_t(p[2]) << 16);
         return channels == 4 ? flatten_rgba(px | (uint32_t(p[3]) << 24)) : px;
     }
 };
 
-// Output rows one wavefront task writes: merge order and column order.
-template <typename OutT>
-struct RowSinks {
-    OutT *merge;   // nullable
-    OutT *column;  // nullable
-};
-
-// One wavefront computes output row (unit u of the tile, mh, mw): a 16x16
-// patch, 3 channels, and stores it for both frames.
-template <typename OutT, bool kIdentity, typename Pixels>
-__device__ __forceinline__ void compute_patch(const Pixels &px, const DevImage &d, const PreArgs &a,
-                                              int br, int bc, int mh, int mw, RowSinks<OutT> sinks) {
+// Bilinear output row (br, bc, mh, mw): a 16x16 patch, 3 channels, both
+// frames.  W taps on the two source rows, then the H tap.
+template <typename OutT, typename Pixels>
+__device__ __forceinline__ void bilinear_patch(const Pixels &px, const DevImage &d, const PreArgs &a,
+                                               int br, int bc, int mh, int mw, OutT *out,
+                                               bool column) {
     const int lane = threadIdx.x & 63;
-    const int py = lane >> 2;
-    const int q = lane & 3;
+    const int py = lane >> 2, q = lane & 3;
     const int oy = (br * kMerge + mh) * kPatch + py;
     const int ox0 = (bc * kMerge + mw) * kPatch + 4 * q;
-
+    const Tap ty = make_tap(d.scale_y, oy, d.src_h);
     float v[3][4];
-    if constexpr (kIdentity) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t p = px.at(oy, ox0 + j);
+    for (int j = 0; j < 4; ++j) {
+        const Tap tx = make_tap(d.scale_x, ox0 + j, d.src_w);
+        const uint32_t p00 = px.at(ty.i0, tx.i0);
+        const uint32_t p01 = px.at(ty.i0, tx.i0 + 1);
+        const uint32_t p10 = px.at(ty.i0 + 1, tx.i0);
+        const uint32_t p11 = px.at(ty.i0 + 1, tx.i0 + 1);
 #pragma unroll
-            for (int c = 0; c < 3; ++c) v[c][j] = (chan(p, c) - a.mean[c]) * a.inv_std[c];
-        }
-    } else {
-        const Tap ty = make_tap(d.scale_y, oy, d.src_h);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const Tap tx = make_tap(d.scale_x, ox0 + j, d.src_w);
-            const uint32_t p00 = px.at(ty.i0, tx.i0);
-            const uint32_t p01 = px.at(ty.i0, tx.i1);
-            const uint32_t p10 = px.at(ty.i1, tx.i0);
-            const uint32_t p11 = px.at(ty.i1, tx.i1);
-#pragma unroll
-            for (int c = 0; c < 3; ++c) {
-                const float top = __builtin_fmaf(tx.l0, chan(p00, c), tx.l1 * chan(p01, c));
-                const float bot = __builtin_fmaf(tx.l0, chan(p10, c), tx.l1 * chan(p11, c));
-                const float val = __builtin_fmaf(ty.l0, top, ty.l1 * bot);
-                v[c][j] = (val - a.mean[c]) * a.inv_std[c];
-            }
+        for (int c = 0; c < 3; ++c) {
+            const float top = __builtin_fmaf(tx.l0, chan(p00, c), tx.l1 * chan(p01, c));
+            const float bot = __builtin_fmaf(tx.l0, chan(p10, c), tx.l1 * chan(p11, c));
+            const float val = __builtin_fmaf(ty.l0, top, ty.l1 * bot);
+            v[c][j] = (val - a.mean[c]) * a.inv_std[c];
         }
     }
-
-    const int within = mh * kMerge + mw;
-    const int elem = py * kPatch + 4 * q;
-    if (sinks.merge) {
-        const int64_t row = d.row_offset + int64_t(br * d.blocks_w + bc) * kRowsPerUnit + within;
-        OutT *base = sinks.merge + row * kRowLen + elem;
+    OutT *dst = row_dest(out, d, br, bc, mh, mw, column);
 #pragma unroll
-        for (int c = 0; c < 3; ++c) store_both_frames<OutT>(base, c, v[c]);
-    }
-    if (sinks.column) {
-        const int64_t row = d.row_offset + int64_t(bc * d.blocks_h + br) * kRowsPerUnit + within;
-        OutT *base = sinks.column + row * kRowLen + elem;
-#pragma unroll
-        for (int c = 0; c < 3; ++c) store_both_frames<OutT>(base, c, v[c]);
-    }
+    for (int c = 0; c < 3; ++c) store_both_frames<OutT>(dst, c, v[c]);
 }
 
-template <typename OutT, bool kIdentity, typename Pixels>
-__device__ __forceinline__ void compute_tile(const Pixels &px, const DevImage &d, const PreArgs &a,
-                                             int br, int bc0, int nb) {
-    const int wave = threadIdx.x >> 6;
-    RowSinks<OutT> sinks{static_cast<OutT *>(a.rows), static_cast<OutT *>(a.rows_col)};
-    for (int p = wave; p < nb * kRowsPerUnit; p += kWaves) {
-        const int u = p >> 2;
-        compute_patch<OutT, kIdentity>(px, d, a, br, bc0 + u, (p >> 1) & 1, p & 1, sinks);
-    }
-}
-
-// Copies source rows [r_lo, r_lo+rows) x columns [c_lo, c_lo + 4*groups) of
-// one image into LDS as one dword per pixel (R | G<<8 | B<<16), flattening
-// RGBA onto white.  Loads are dword-aligned 16-byte buffer loads (plus one
-// dword for RGBA) realigned with v_alignbyte; reads past the buffer end
-// return zero and only feed pixels outside the band.
+// Stages source rows [r_lo, r_lo + rows) x columns [c_lo, c_lo + 4*groups)
+// into LDS, one dword per pixel.  Rows past the last image row repeat it;
+// a column past the last image column is patched afterwards.
 __device__ __forceinline__ void stage_band(uint32_t *band, const PreArgs &a, const DevImage &d,
                                            int r_lo, int c_lo, int rows, int groups, int pitch) {
     const int C = d.channels;
     const int64_t row_bytes = int64_t(d.src_w) * C;
     const uint64_t first = reinterpret_cast<uint64_t>(a.src) + uint64_t(d.src_offset) +
                            uint64_t(int64_t(r_lo) * row_bytes + int64_t(c_lo) * C);
-    const uint64_t base = first & ~uint64_t(3);
-    const uint64_t end = reinterpret_cast<uint64_t>(a.src) + uint64_t(a.src_end);
-    const uint64_t avail = end - base;
-    const int num = avail > 0x7FFFFFF0ull ? 0x7FFFFFF0 : int(avail);
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(base), 0, num, kBufferWord3);
-    const uint32_t lead = uint32_t(first - base);
-    const int total = rows * groups;
-    for (int i = threadIdx.x; i < total; i += kThreads) {
-        const int r = i / groups;
-        const int g = i - r * groups;
-        const uint32_t off = lead + uint32_t(int64_t(r) * row_bytes) + uint32_t(g * 4 * C);
-        const uint32_t al = off & ~3u;
-        const uint32_t sh = off & 3u;
-        const u32x4 w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, int(al), 0, 0));
-        uint32_t p0, p1, p2, p3;
-        if (C == 3) {
-            const uint32_t u0 = __builtin_amdgcn_alignbyte(w.y, w.x, sh);
-            const uint32_t u1 = __builtin_amdgcn_alignbyte(w.z, w.y, sh);
-            const uint32_t u2 = __builtin_amdgcn_alignbyte(w.w, w.z, sh);
-            p0 = u0 & 0x00FFFFFFu;
-            p1 = (u0 >> 24) | ((u1 & 0xFFFFu) << 8);
-            p2 = (u1 >> 16) | ((u2 & 0xFFu) << 16);
-            p3 = u2 >> 8;
-        } else {
-            const uint32_t w4 = __builtin_amdgcn_raw_buffer_load_b32(rsrc, int(al) + 16, 0, 0);
-            p0 = flatten_rgba(__builtin_amdgcn_alignbyte(w.y, w.x, sh));
-            p1 = flatten_rgba(__builtin_amdgcn_alignbyte(w.z, w.y, sh));
-            p2 = flatten_rgba(__builtin_amdgcn_alignbyte(w.w, w.z, sh));
-            p3 = flatten_rgba(__builtin_amdgcn_alignbyte(w4, w.w, sh));
+    const SourceWindow w = source_window(a, first);
+    const int last_row = d.src_h - 1 - r_lo;  // band row of the image's last row
+    const int nthreads = blockDim.x;
+    if (groups <= nthreads) {
+        // thread -> (row phase, group) once; rows advance by nthreads / groups
+        const int step = nthreads / groups;
+        const int r0 = div_small(threadIdx.x, groups, 1.0f / float(groups));
+        const int g = threadIdx.x - r0 * groups;
+        if (r0 < step) {
+            for (int r = r0; r < rows; r += step) {
+                const int sr = min(r, last_row);
+                uint32_t p[4];
+                load_4px(w, w.lead + uint32_t(int64_t(sr) * row_bytes) + uint32_t(g * 4 * C), C, p);
+                const u32x4 o = {p[0], p[1], p[2], p[3]};
+                *reinterpret_cast<u32x4 *>(band + r * pitch + 4 * g) = o;
+            }
         }
-        const u32x4 out = {p0, p1, p2, p3};
-        *reinterpret_cast<u32x4 *>(band + r * pitch + 4 * g) = out;
+    } else {
+        for (int i = threadIdx.x; i < rows * groups; i += nthreads) {
+            const int r = i / groups;
+            const int g = i - r * groups;
+            const int sr = min(r, last_row);
+            uint32_t p[4];
+            load_4px(w, w.lead + uint32_t(int64_t(sr) * row_bytes) + uint32_t(g * 4 * C), C, p);
+            const u32x4 o = {p[0], p[1], p[2], p[3]};
+            *reinterpret_cast<u32x4 *>(band + r * pitch + 4 * g) = o;
+        }
     }
+}
+
+// Tile order: workgroup b is dispatched to XCD b % 8; tile t = (b % 8) * per
+// + b / 8 gives each XCD one contiguous run of tiles (and so of output
+// rows), which keeps each XCD's write stream and its source reads local.
+__device__ __forceinline__ int64_t xcd_contiguous_tile(int64_t b, int64_t grid) {
+    const int64_t per = grid / kXcds;
+    return b < per * kXcds ? (b % kXcds) * per + b / kXcds : b;
 }
 
 template <typename OutT>
 __global__ __launch_bounds__(kThreads) void preprocess_kernel(PreArgs a) {
     extern __shared__ uint32_t band[];
-    const int64_t tile = blockIdx.x;
+    int64_t tile = a.xcd_order ? xcd_contiguous_tile(blockIdx.x, gridDim.x) : int64_t(blockIdx.x);
+    // Pass 0 writes merge-block order (if requested), pass 1 column order:
+    // each workgroup writes one output, in that output's own order.
+    const bool second = tile >= a.tiles_per_pass;
+    if (second) tile -= a.tiles_per_pass;
+    const bool column = second || a.rows == nullptr;
+    OutT *const out = static_cast<OutT *>(column ? a.rows_col : a.rows);
     const int img = find_segment(a.tile_begin, a.n, tile);
     const DevImage d = a.images[img];
     const int local = int(tile - a.tile_begin[img]);
-    const int br = local / d.tiles_per_brow;
-    const int bc0 = (local - br * d.tiles_per_brow) * d.units_per_tile;
-    const int nb = min(d.units_per_tile, d.blocks_w - bc0);
-    const bool identity = (d.flags & kFlagIdentity) != 0;
-
-    // Source band touched by this tile: taps are monotone in the output
-    // index, so the first and last output rows/columns bound it.
-    const int oy_first = br * kUnitPx, oy_last = oy_first + kUnitPx - 1;
-    const int ox_first = bc0 * kUnitPx, ox_last = (bc0 + nb) * kUnitPx - 1;
-    int r_lo, r_hi, c_lo, c_hi;
-    if (identity) {
-        r_lo = oy_first; r_hi = oy_last; c_lo = ox_first; c_hi = ox_last;
+    const int R = a.rows_per_tile;
+    int br, first, count;
+    if (!column) {
+        br = div_small(local, d.tiles_per_brow, d.inv_tiles_per_brow);
+        first = (local - br * d.tiles_per_brow) * R;  // first row within the block row
+        count = min(R, d.blocks_w * kRowsPerUnit - first);
     } else {
-        r_lo = make_tap(d.scale_y, oy_first, d.src_h).i0;
-        r_hi = make_tap(d.scale_y, oy_last, d.src_h).i1;
-        c_lo = make_tap(d.scale_x, ox_first, d.src_w).i0;
-        c_hi = make_tap(d.scale_x, ox_last, d.src_w).i1;
+        // column order lists units by (block col, block row); R <= 4 divides
+        // a unit, so a tile is part of one unit
+        const int rc = local * R;
+        const int unit = rc >> 2;
+        const int bc = div_small(unit, d.blocks_h, d.inv_blocks_h);
+        br = unit - bc * d.blocks_h;
+        first = bc * kRowsPerUnit + (rc & 3);
+        count = R;
     }
-    const int rows = r_hi - r_lo + 1;
-    const int groups = (c_hi - c_lo + 4) >> 2;
+
+    // Output rectangle of the tile: whole merge units when R >= 4, else one
+    // patch row (mh fixed) of one unit, one or both of its patches.
+    int oy_first, oy_last, ox_first, ox_last;
+    if (R >= kRowsPerUnit) {
+        oy_first = br * kUnitPx;
+        oy_last = oy_first + kUnitPx - 1;
+        ox_first = (first >> 2) * kUnitPx;
+        ox_last = ((first + count - 1) >> 2) * kUnitPx + kUnitPx - 1;
+    } else {
+        const int mh = (first >> 1) & 1;
+        oy_first = (br * kMerge + mh) * kPatch;
+        oy_last = oy_first + kPatch - 1;
+        const int bc = first >> 2;
+        ox_first = (bc * kMerge + (first & 1)) * kPatch;
+        ox_last = (bc * kMerge + ((first + count - 1) & 1)) * kPatch + kPatch - 1;
+    }
+    const int wave = threadIdx.x >> 6;
+    const int waves = blockDim.x >> 6;
+
+    if (d.flags & kFlagIdentity) {
+        const int64_t row_bytes = int64_t(d.src_w) * d.channels;
+        const uint64_t first_byte = reinterpret_cast<uint64_t>(a.src) + uint64_t(d.src_offset) +
+                                    uint64_t(int64_t(oy_first) * row_bytes + int64_t(ox_first) * d.channels);
+        const SourceWindow w = source_window(a, first_byte);
+        for (int p = wave; p < count; p += waves) {
+            const int qr = first + p;  // row within the block row: (block col, mh, mw)
+            identity_patch<OutT>(a, d, w, row_bytes, oy_first, ox_first, br, qr >> 2, (qr >> 1) & 1,
+                                 qr & 1, out, column);
+        }
+        return;
+    }
+
+    // Source band touched by the tile: taps are monotone in the output
+    // index, so the first and last output rows/columns bound it.  The band
+    // runs one past the last first-tap so that the second tap is always
+    // i0 + 1; at the image edge that row/column repeats the last one.
+    const int r_lo = make_tap(d.scale_y, oy_first, d.src_h).i0;
+    const int r_end = make_tap(d.scale_y, oy_last, d.src_h).i0 + 1;
+    const int c_lo = make_tap(d.scale_x, ox_first, d.src_w).i0;
+    const int c_end = make_tap(d.scale_x, ox_last, d.src_w).i0 + 1;
+    const int rows = r_end - r_lo + 1;
+    const int groups = (c_end - c_lo + 4) >> 2;
     const int pitch = 4 * groups;
     const int64_t band_bytes = int64_t(rows) * d.src_w * d.channels;
     const bool fits = int64_t(rows) * pitch <= a.band_capacity && band_bytes < 0x7FFF0000ll;
@@ -344,13 +458,23 @@ __global__ __launch_bounds__(kThreads) void preprocess_kernel(PreArgs a) {
     if (fits) {
         stage_band(band, a, d, r_lo, c_lo, rows, groups, pitch);
         __syncthreads();
-        const LdsPixels px{band, pitch, r_lo, c_lo};
-        if (identity) compute_tile<OutT, true>(px, d, a, br, bc0, nb);
-        else compute_tile<OutT, false>(px, d, a, br, bc0, nb);
+        if (c_end == d.src_w) {  // second tap at the right edge: repeat the last column
+            const int xl = d.src_w - 1 - c_lo;
+            for (int r = threadIdx.x; r < rows; r += blockDim.x) band[r * pitch + xl + 1] = band[r * pitch + xl];
+            __syncthreads();
+        }
+        const BandPixels px{band, pitch, r_lo, c_lo};
+        for (int p = wave; p < count; p += waves) {
+            const int qr = first + p;
+            bilinear_patch<OutT>(px, d, a, br, qr >> 2, (qr >> 1) & 1, qr & 1, out, column);
+        }
     } else {
-        const GlobalPixels px{a.src + d.src_offset, int64_t(d.src_w) * d.channels, d.channels};
-        if (identity) compute_tile<OutT, true>(px, d, a, br, bc0, nb);
-        else compute_tile<OutT, false>(px, d, a, br, bc0, nb);
+        const GlobalPixels px{a.src + d.src_offset, int64_t(d.src_w) * d.channels, d.channels,
+                              d.src_h, d.src_w};
+        for (int p = wave; p < count; p += waves) {
+            const int qr = first + p;
+            bilinear_patch<OutT>(px, d, a, br, qr >> 2, (qr >> 1) & 1, qr & 1, out, column);
+        }
     }
 }
 
@@ -365,9 +489,10 @@ __global__ __launch_bounds__(kThreads) void column_permute_kernel(PermArgs a) {
     const int64_t drow = unit * kRowsPerUnit;
     const int img = find_segment(a.row_begin, a.n, drow);
     const DevImage d = a.images[img];
-    const int64_t j = (drow - d.row_offset) / kRowsPerUnit;  // column-order unit index
-    const int64_t bc = j / d.blocks_h, br = j - bc * d.blocks_h;
-    const int64_t src_row = d.row_offset + (br * d.blocks_w + bc) * kRowsPerUnit;
+    const int j = int((drow - d.row_offset) / kRowsPerUnit);  // column-order unit index
+    const int bc = div_small(j, d.blocks_h, d.inv_blocks_h);
+    const int br = j - bc * d.blocks_h;
+    const int64_t src_row = d.row_offset + (int64_t(br) * d.blocks_w + bc) * kRowsPerUnit;
     constexpr int kVecs = kRowsPerUnit * kRowLen * int(sizeof(OutT)) / 16;  // 16-byte vectors per unit
     const u32x4 *in = reinterpret_cast<const u32x4 *>(static_cast<const OutT *>(a.in) + src_row * kRowLen);
     u32x4 *out = reinterpret_cast<u32x4 *>(static_cast<OutT *>(a.out) + drow * kRowLen);
@@ -450,11 +575,44 @@ int hip_error(hipError_t e, const char *what) {
                                      hipGetErrorString(e) + ")");
 }
 
-// Conservative size of the LDS band one tile of k units needs, in dwords.
-int64_t band_estimate(const DevImage &d, int k) {
-    if (d.flags & kFlagIdentity) return int64_t(kUnitPx) * (4 * ((kUnitPx * k + 3) / 4));
-    const double rows = std::min<double>(d.src_h, std::ceil(31.0 * d.scale_y) + 4.0);
-    const double cols = std::min<double>(d.src_w, std::ceil((kUnitPx * k - 1.0) * d.scale_x) + 4.0);
+// Tiling policy: rows per tile (1, 2 or a multiple of 4) and whether
+// workgroups are mapped to XCD-contiguous runs of tiles.  Small tiles keep
+// the output each workgroup writes small, which the HBM write path favours.
+// With both outputs requested the grid holds two passes of tiles (merge
+// order, then column order), so each output is written as a dense stream.
+#ifndef MIMO_ROWS_PER_TILE
+#define MIMO_ROWS_PER_TILE 4
+#endif
+#ifndef MIMO_ROWS_PER_TILE_DUAL
+#define MIMO_ROWS_PER_TILE_DUAL 1
+#endif
+#ifndef MIMO_XCD_ORDER
+#define MIMO_XCD_ORDER 1
+#endif
+struct Tiling {
+    int rows_per_tile = MIMO_ROWS_PER_TILE;
+    int xcd_order = MIMO_XCD_ORDER;
+    int passes = 1;
+    static Tiling choose(bool merge, bool column) {
+        Tiling t;
+        if (merge && column) {
+            t.passes = 2;
+            t.rows_per_tile = std::min(MIMO_ROWS_PER_TILE_DUAL, kRowsPerUnit);
+        } else if (column) {
+            t.rows_per_tile = std::min(t.rows_per_tile, kRowsPerUnit);
+        }
+        return t;
+    }
+    int threads() const { return 64 * std::min(rows_per_tile, kRowsPerUnit); }
+};
+
+// Conservative size of the LDS band one tile of R rows needs, in dwords.
+int64_t band_estimate(const DevImage &d, int R) {
+    const int out_rows = R >= kRowsPerUnit ? kUnitPx : kPatch;
+    const int out_cols = R >= kRowsPerUnit ? kUnitPx * (R / kRowsPerUnit) : kPatch * R;
+    if (d.flags & kFlagIdentity) return int64_t(out_rows) * (4 * ((out_cols + 3) / 4));
+    const double rows = std::min<double>(d.src_h, std::ceil((out_rows - 1.0) * d.scale_y) + 4.0);
+    const double cols = std::min<double>(d.src_w, std::ceil((out_cols - 1.0) * d.scale_x) + 4.0);
     return int64_t(rows) * (4 * ((int64_t(cols) + 3) / 4 + 1));
 }
 
@@ -466,12 +624,13 @@ struct BuiltTables {
 };
 
 // Builds the workspace image: DevImage records, tile prefix, row prefix.
-int build_tables(int32_t n, const mimo_image_desc *desc, BuiltTables &out) {
+int build_tables(int32_t n, const mimo_image_desc *desc, const Tiling &tiling, BuiltTables &out) {
     out.bytes.assign(ws_total_bytes(n), 0);
     DevImage *img = reinterpret_cast<DevImage *>(out.bytes.data());
     int64_t *tile_begin = reinterpret_cast<int64_t *>(out.bytes.data() + ws_images_bytes(n));
     int64_t *row_begin =
         reinterpret_cast<int64_t *>(out.bytes.data() + ws_images_bytes(n) + ws_prefix_bytes(n));
+    const int R = tiling.rows_per_tile;
     int64_t tiles = 0, rows = 0, band = 0;
     for (int32_t i = 0; i < n; ++i) {
         const mimo_image_desc &s = desc[i];
@@ -481,9 +640,8 @@ int build_tables(int32_t n, const mimo_image_desc *desc, BuiltTables &out) {
         row_begin[i] = rows;
         d.src_offset = s.src_offset;
         d.row_offset = rows;
+        d.tiles_per_brow = 1;
         if (s.status != MIMO_OK || s.rows == 0) {
-            d.tiles_per_brow = 1;
-            d.units_per_tile = 1;
             img[i] = d;
             continue;
         }
@@ -503,11 +661,12 @@ int build_tables(int32_t n, const mimo_image_desc *desc, BuiltTables &out) {
         d.scale_y = float(s.src_h) / float(s.dst_h);
         d.scale_x = float(s.src_w) / float(s.dst_w);
         d.flags = (s.src_h == s.dst_h && s.src_w == s.dst_w) ? kFlagIdentity : 0;
-        int k = kMaxUnitsPerTile;
-        while (k > 1 && band_estimate(d, k) > kBandBudgetDwords) k >>= 1;
-        if (band_estimate(d, k) <= kBandBudgetDwords) band = std::max(band, band_estimate(d, k));
-        d.units_per_tile = std::min(k, d.blocks_w);
-        d.tiles_per_brow = (d.blocks_w + d.units_per_tile - 1) / d.units_per_tile;
+        const int64_t est = band_estimate(d, R);
+        if (est <= kBandBudgetDwords) band = std::max(band, est);  // else: direct reads
+        const int64_t brow_rows = int64_t(d.blocks_w) * kRowsPerUnit;
+        d.tiles_per_brow = int32_t((brow_rows + R - 1) / R);
+        d.inv_tiles_per_brow = 1.0f / float(d.tiles_per_brow);
+        d.inv_blocks_h = 1.0f / float(d.blocks_h);
         img[i] = d;
         tiles += int64_t(d.blocks_h) * d.tiles_per_brow;
         rows += s.rows;
@@ -560,8 +719,9 @@ int mimo_preprocess_batch(int32_t n, const mimo_image_desc *desc, const uint8_t 
         a.inv_std[c] = float(1.0 / double(std255[c]));
         a.mean[c] = mean255[c];
     }
+    const Tiling tiling = Tiling::choose(rows != nullptr, rows_col != nullptr);
     BuiltTables t;
-    int st = build_tables(n, desc, t);
+    int st = build_tables(n, desc, tiling, t);
     if (st != MIMO_OK) return st;
     int64_t src_needed = 0;
     for (int32_t i = 0; i < n; ++i)
@@ -574,7 +734,7 @@ int mimo_preprocess_batch(int32_t n, const mimo_image_desc *desc, const uint8_t 
         return set_error(MIMO_E_CAPACITY, "preprocess_batch: capacity_rows " + std::to_string(capacity_rows) +
                                               " < " + std::to_string(t.total_rows) + " rows");
     if (t.total_tiles == 0) return MIMO_OK;
-    if (t.total_tiles > 0x7FFFFFFFll)
+    if (t.total_tiles * tiling.passes > 0x7FFFFFFFll)
         return set_error(MIMO_E_TOO_LARGE, "preprocess_batch: more than 2^31-1 tiles");
 
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -590,8 +750,12 @@ int mimo_preprocess_batch(int32_t n, const mimo_image_desc *desc, const uint8_t 
     a.rows_col = rows_col;
     a.n = n;
     a.band_capacity = t.band_capacity;
+    a.rows_per_tile = tiling.rows_per_tile;
+    a.xcd_order = tiling.xcd_order;
+    a.tiles_per_pass = rows ? t.total_tiles : int64_t(1) << 62;
     const size_t lds = size_t(t.band_capacity) * 4;
-    const dim3 grid{unsigned(t.total_tiles), 1, 1}, block{unsigned(kThreads), 1, 1};
+    const dim3 grid{unsigned(t.total_tiles * tiling.passes), 1, 1},
+        block{unsigned(tiling.threads()), 1, 1};
     if (out_dtype == MIMO_F32)
         hipLaunchKernelGGL(preprocess_kernel<float>, grid, block, lds, s, a);
     else
@@ -619,7 +783,7 @@ int mimo_column_permute(int32_t n, const mimo_image_desc *desc, const void *rows
     if (workspace_bytes < ws_total_bytes(n))
         return set_error(MIMO_E_CAPACITY, "column_permute: workspace smaller than mimo_workspace_bytes(n)");
     BuiltTables t;
-    int st = build_tables(n, desc, t);
+    int st = build_tables(n, desc, Tiling(), t);
     if (st != MIMO_OK) return st;
     if (t.total_rows > capacity_rows)
         return set_error(MIMO_E_CAPACITY, "column_permute: capacity_rows below the total rows");
