@@ -166,19 +166,24 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    # Kernel time: the library records these events on the launch stream
+    # right before and after each fused-kernel launch (the per-call
+    # descriptor upload falls outside).  Step time: events around all steps.
     stream = torch.cuda.current_stream()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    for ev in starts + ends:
+        ev.record(stream)  # creates the underlying hipEvent_t
     t_begin = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     dispatch0 = V.dispatch_count()
     torch.cuda.synchronize()
     t_begin.record(stream)
     for i in range(args.steps):
-        starts[i].record(stream)
+        V.set_launch_events(starts[i], ends[i])
         step()
-        ends[i].record(stream)
     t_end.record(stream)
+    V.set_launch_events(None, None)
     torch.cuda.synchronize()
     assert V.dispatch_count() == dispatch0 + args.steps
     total_ms = t_begin.elapsed_time(t_end)

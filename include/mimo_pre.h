@@ -185,6 +185,17 @@ int mimo_column_permute(int32_t n, const mimo_image_desc *desc, const void *rows
                         void *rows_out, int32_t out_dtype, int64_t capacity_rows,
                         void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Instrumentation.  When start and stop are non-null hipEvent_t handles
+ * (passed as void*), every later kernel launch that mimo_preprocess_batch or
+ * mimo_column_permute makes on the calling thread records `start` on the
+ * launch stream immediately before the kernel and `stop` immediately after
+ * it, so the pair times the kernel alone (the descriptor upload falls
+ * outside).  NULL, NULL switches it off.  Thread-local; the caller owns the
+ * events.  Returns MIMO_OK, or MIMO_E_INVALID if only one is null.
+ */
+int mimo_set_launch_events(void *start, void *stop);
+
 /* Static text for a status code. */
 const char *mimo_status_string(int status);
 

@@ -17,6 +17,6 @@ from ._abi import (  # noqa: F401
     MIMO_E_HIP, MIMO_E_INVALID, MIMO_E_TOO_LARGE, MIMO_E_UNSUPPORTED, MIMO_F32, MIMO_OK,
     ROW_LEN, LibraryNotBuilt, MimoError, MimoParams, column_permutation, column_permute,
     default_params, dispatch_count, last_error, load, make_params, plan_geometry,
-    preprocess_batch, smart_resize, status_string, workspace_bytes,
+    preprocess_batch, set_launch_events, smart_resize, status_string, workspace_bytes,
 )
 from .processor import BatchPlan, plan_batch, preprocess, stats255  # noqa: F401

@@ -78,6 +78,7 @@ SIGNATURES = {
     "mimo_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "mimo_last_error": ([], ctypes.c_char_p),
     "mimo_dispatch_count": ([], _I64),
+    "mimo_set_launch_events": ([_P, _P], ctypes.c_int),
 }
 
 _lock = threading.Lock()
@@ -118,6 +119,16 @@ def last_error() -> str:
 
 def dispatch_count() -> int:
     return int(load().mimo_dispatch_count())
+
+
+def set_launch_events(start=None, stop=None):
+    """mimo_set_launch_events: torch.cuda.Event pair recorded right around
+    each later kernel launch on this thread (None, None to stop).  The events
+    must already exist (record them once first)."""
+    h = lambda e: None if e is None else ctypes.c_void_p(int(e.cuda_event))
+    if start is not None and (not start.cuda_event or not stop.cuda_event):
+        raise MimoError(MIMO_E_INVALID, "set_launch_events: record the events once first")
+    _check(load().mimo_set_launch_events(h(start), h(stop)), "set_launch_events")
 
 
 def default_params() -> MimoParams:

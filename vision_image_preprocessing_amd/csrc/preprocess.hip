@@ -506,6 +506,19 @@ __global__ __launch_bounds__(kThreads) void column_permute_kernel(PermArgs a) {
 // ------------------------------------------------------------- host side
 
 std::atomic<int64_t> g_dispatches{0};
+thread_local hipEvent_t g_launch_start = nullptr;
+thread_local hipEvent_t g_launch_stop = nullptr;
+
+// Records the caller's timing events around one kernel launch.
+template <typename Launch>
+hipError_t timed_launch(hipStream_t s, Launch &&launch) {
+    hipError_t e = hipSuccess;
+    if (g_launch_start && (e = hipEventRecord(g_launch_start, s)) != hipSuccess) return e;
+    launch();
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (g_launch_stop && (e = hipEventRecord(g_launch_stop, s)) != hipSuccess) return e;
+    return hipSuccess;
+}
 
 // Pinned host staging for the per-call descriptor tables: a small ring per
 // device, each slot fenced by an event so a slot is rewritten only after
@@ -691,6 +704,15 @@ extern "C" {
 
 int64_t mimo_dispatch_count(void) { return g_dispatches.load(); }
 
+int mimo_set_launch_events(void *start, void *stop) {
+    clear_error();
+    if ((start == nullptr) != (stop == nullptr))
+        return set_error(MIMO_E_INVALID, "set_launch_events: give both events or neither");
+    g_launch_start = static_cast<hipEvent_t>(start);
+    g_launch_stop = static_cast<hipEvent_t>(stop);
+    return MIMO_OK;
+}
+
 int mimo_preprocess_batch(int32_t n, const mimo_image_desc *desc, const uint8_t *src,
                           int64_t src_capacity, const float *mean255, const float *std255,
                           int32_t out_dtype, void *rows, void *rows_col, int64_t capacity_rows,
@@ -756,11 +778,12 @@ int mimo_preprocess_batch(int32_t n, const mimo_image_desc *desc, const uint8_t 
     const size_t lds = size_t(t.band_capacity) * 4;
     const dim3 grid{unsigned(t.total_tiles * tiling.passes), 1, 1},
         block{unsigned(tiling.threads()), 1, 1};
-    if (out_dtype == MIMO_F32)
-        hipLaunchKernelGGL(preprocess_kernel<float>, grid, block, lds, s, a);
-    else
-        hipLaunchKernelGGL(preprocess_kernel<uint16_t>, grid, block, lds, s, a);
-    e = hipGetLastError();
+    e = timed_launch(s, [&] {
+        if (out_dtype == MIMO_F32)
+            hipLaunchKernelGGL(preprocess_kernel<float>, grid, block, lds, s, a);
+        else
+            hipLaunchKernelGGL(preprocess_kernel<uint16_t>, grid, block, lds, s, a);
+    });
     if (e != hipSuccess) return hip_error(e, "preprocess_batch: kernel launch");
     g_dispatches.fetch_add(1);
     return MIMO_OK;
@@ -805,11 +828,12 @@ int mimo_column_permute(int32_t n, const mimo_image_desc *desc, const void *rows
     a.total_units = units;
     a.n = n;
     const dim3 grid{unsigned(blocks), 1, 1}, block{unsigned(kThreads), 1, 1};
-    if (out_dtype == MIMO_F32)
-        hipLaunchKernelGGL(column_permute_kernel<float>, grid, block, 0, s, a);
-    else
-        hipLaunchKernelGGL(column_permute_kernel<uint16_t>, grid, block, 0, s, a);
-    e = hipGetLastError();
+    e = timed_launch(s, [&] {
+        if (out_dtype == MIMO_F32)
+            hipLaunchKernelGGL(column_permute_kernel<float>, grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL(column_permute_kernel<uint16_t>, grid, block, 0, s, a);
+    });
     if (e != hipSuccess) return hip_error(e, "column_permute: kernel launch");
     g_dispatches.fetch_add(1);
     return MIMO_OK;
