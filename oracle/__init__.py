@@ -94,6 +94,15 @@ def _load():
         lib.oracle_preprocess_rows.restype = ctypes.c_int
         lib.oracle_column_permutation.argtypes = [i64, i64, i64, i64, p]
         lib.oracle_column_permutation.restype = ctypes.c_int
+        lib.oracle_video_max_pixels.argtypes = [i64, i64, i64, i64, i64]
+        lib.oracle_video_max_pixels.restype = i64
+        lib.oracle_smart_nframes.argtypes = [i64, ctypes.c_double, ctypes.c_double, i64, i64]
+        lib.oracle_smart_nframes.restype = i64
+        lib.oracle_sample_frames.argtypes = [i64, i64, ctypes.c_double, p, p]
+        lib.oracle_sample_frames.restype = i64
+        lib.oracle_preprocess_video.argtypes = [p, i64, i64, i64, i64, i64, i64, i64, i64, i64,
+                                                p, p, p]
+        lib.oracle_preprocess_video.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -238,3 +247,48 @@ def stats255(mean, std):
     m = np.asarray([255.0 * float(v) for v in mean], dtype=np.float64).astype(np.float32)
     s = np.asarray([255.0 * float(v) for v in std], dtype=np.float64).astype(np.float32)
     return m, s
+
+
+# ------------------------------------------------------------------ video
+def video_max_pixels(n_sampled: int, total_max: int, temporal: int = TEMPORAL,
+                     min_pixels: int = MIN_PIXELS, max_pixels: int = MAX_PIXELS) -> int:
+    """cortiq video_max_pixels: per-frame pixel ceiling for n sampled frames."""
+    v = _load().oracle_video_max_pixels(n_sampled, total_max, temporal, min_pixels, max_pixels)
+    if v < 0:
+        raise OracleError(v, "video_max_pixels")
+    return int(v)
+
+
+def smart_nframes(total: int, fps_src: float, fps: float, min_frames: int, max_frames: int) -> int:
+    """cortiq smart_nframes: even frame count for `total` frames sampled at fps."""
+    v = _load().oracle_smart_nframes(total, float(fps_src), float(fps), min_frames, max_frames)
+    if v < 0:
+        raise OracleError(v, "smart_nframes")
+    return int(v)
+
+
+def sample_frames(total: int, n: int, fps_src: float):
+    """cortiq sample_frames: (indices int64, timestamps float32)."""
+    idx = np.empty(max(n, 1), dtype=np.int64)
+    ts = np.empty(max(n, 1), dtype=np.float32)
+    k = _load().oracle_sample_frames(total, n, float(fps_src), _ptr(idx), _ptr(ts))
+    if k < 0:
+        raise OracleError(int(k), "sample_frames")
+    return idx[:k].copy(), ts[:k].copy()
+
+
+def preprocess_video(frames: np.ndarray, out_h: int, out_w: int, mean255, std255,
+                     patch: int = PATCH, merge: int = MERGE, temporal: int = TEMPORAL) -> np.ndarray:
+    """prepare_video_frames (pixel part) for uint8 frames [n, H, W, C]:
+    rows [ceil(n/T)*(out_h/patch)*(out_w/patch), 3*T*patch*patch]."""
+    frames = np.ascontiguousarray(frames, dtype=np.uint8)
+    n, h, w, c = frames.shape
+    m, s = _stats(mean255, std255)
+    gt = -(-n // temporal)
+    rows = gt * (out_h // patch) * (out_w // patch)
+    out = np.empty((rows, 3 * temporal * patch * patch), dtype=np.float32)
+    st = _load().oracle_preprocess_video(_ptr(frames), n, h, w, c, out_h, out_w, patch, merge,
+                                         temporal, _ptr(m), _ptr(s), _ptr(out))
+    if st != OK:
+        raise OracleError(st, "preprocess_video")
+    return out

@@ -441,3 +441,147 @@ int oracle_column_permutation(int64_t grid_t, int64_t grid_h, int64_t grid_w,
                     perm[dst++] = ((t * bh + br) * bw + bc) * unit + k;
     return ORC_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Video frames (cortiq_engine::mimo_vision: video_max_pixels, smart_nframes, */
+/* sample_frames, prepare_video_frames).                                     */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Per-frame pixel ceiling for n sampled frames:
+ *   max(min_pixels, min(total_max * T // n, max_pixels)),
+ * with T the temporal patch size and // floor division.
+ */
+int64_t oracle_video_max_pixels(int64_t n_sampled, int64_t total_max, int64_t temporal,
+                                int64_t min_pixels, int64_t max_pixels)
+{
+    if (n_sampled < 1)
+        return ORC_E_INVALID;
+    int64_t per_frame = (total_max * temporal) / n_sampled;
+    int64_t capped = per_frame < max_pixels ? per_frame : max_pixels;
+    return capped > min_pixels ? capped : min_pixels;
+}
+
+/*
+ * Frame count for `total` source frames at `fps_src` sampled at `fps`:
+ * total / fps_src * fps, clamped to [min_frames, max_frames], then to at
+ * most total, then floored to an even count.
+ */
+int64_t oracle_smart_nframes(int64_t total, double fps_src, double fps, int64_t min_frames,
+                             int64_t max_frames)
+{
+    if (total < 1 || !(fps_src > 0.0) || !(fps > 0.0) || min_frames > max_frames)
+        return ORC_E_INVALID;
+    double n = (double)total / fps_src * fps;
+    if (n < (double)min_frames)
+        n = (double)min_frames;
+    if (n > (double)max_frames)
+        n = (double)max_frames;
+    if (n > (double)total)
+        n = (double)total;
+    return (int64_t)(floor(n / 2.0) * 2.0);
+}
+
+/*
+ * Sampled frame indices unique(int64(linspace(0, total - 1, n))) and their
+ * timestamps float32(idx) / fps_src.  linspace as numpy evaluates it:
+ * step = (stop - start) / (n - 1), value_i = i * step + start, and the last
+ * value set to stop exactly.  Returns the number of unique indices.
+ */
+int64_t oracle_sample_frames(int64_t total, int64_t n, double fps_src, int64_t *idx, float *ts)
+{
+    if (total < 1 || n < 1 || !(fps_src > 0.0))
+        return ORC_E_INVALID;
+    double start = 0.0, stop = (double)(total - 1);
+    int64_t count = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        double v;
+        if (n == 1)
+            v = start;
+        else if (i == n - 1)
+            v = stop;
+        else
+            v = (double)i * ((stop - start) / (double)(n - 1)) + start;
+        int64_t k = (int64_t)v; /* truncation toward zero, as an int64 cast */
+        /* values are non-decreasing: unique keeps the first of each run */
+        if (count == 0 || idx[count - 1] != k)
+            idx[count++] = k;
+    }
+    float fps32 = (float)fps_src;
+    for (int64_t j = 0; j < count; ++j)
+        ts[j] = (float)idx[j] / fps32;
+    return count;
+}
+
+/*
+ * prepare_video_frames, pixel part: n frames of one size (uint8 [H][W][C]
+ * each, back to back), all resized to the same (OH, OW).  The frame list
+ * is padded to a multiple of `temporal` by repeating the last frame; frame
+ * f = t*temporal + tt forms temporal slot tt of temporal patch t.  Rows are
+ * listed by (t, block row, block col, mh, mw); each row holds
+ * (c, tt, py, px).  A single frame gives the image path (T identical
+ * frames).
+ */
+int oracle_preprocess_video(const uint8_t *frames, int64_t n_frames, int64_t H, int64_t W,
+                            int64_t C, int64_t OH, int64_t OW, int64_t patch, int64_t merge,
+                            int64_t temporal, const float *mean255, const float *std255,
+                            float *rows_out)
+{
+    if (n_frames < 1 || H < 1 || W < 1 || (C != 3 && C != 4) || patch < 1 || merge < 1 ||
+        temporal < 1 || OH % (patch * merge) != 0 || OW % (patch * merge) != 0 || OH < 1 ||
+        OW < 1)
+        return ORC_E_INVALID;
+    int64_t padded = (n_frames + temporal - 1) / temporal * temporal;
+    int64_t npix = H * W;
+    uint8_t *rgb = (uint8_t *)malloc((size_t)(npix * 3));
+    float *planar = (float *)malloc(sizeof(float) * (size_t)(3 * npix));
+    float *resized = (float *)malloc(sizeof(float) * (size_t)(padded * 3 * OH * OW));
+    if (!rgb || !planar || !resized) {
+        free(rgb);
+        free(planar);
+        free(resized);
+        return ORC_E_NOMEM;
+    }
+    for (int64_t f = 0; f < padded; ++f) {
+        int64_t src_f = f < n_frames ? f : n_frames - 1; /* repeat the last frame */
+        const uint8_t *hwc = frames + src_f * npix * C;
+        if (C == 4)
+            oracle_flatten_rgba(hwc, npix, rgb);
+        else
+            memcpy(rgb, hwc, (size_t)(npix * 3));
+        for (int64_t c = 0; c < 3; ++c)
+            for (int64_t i = 0; i < npix; ++i)
+                planar[c * npix + i] = (float)rgb[3 * i + c];
+        float *out_f = resized + f * 3 * OH * OW;
+        oracle_resize_bilinear(planar, 3, H, W, out_f, OH, OW);
+        for (int64_t c = 0; c < 3; ++c)
+            for (int64_t i = 0; i < OH * OW; ++i)
+                out_f[c * OH * OW + i] = (out_f[c * OH * OW + i] - mean255[c]) / std255[c];
+    }
+    int64_t gt = padded / temporal;
+    int64_t gh = OH / patch, gw = OW / patch;
+    int64_t bh = gh / merge, bw = gw / merge;
+    int64_t row_len = 3 * temporal * patch * patch;
+    for (int64_t t = 0; t < gt; ++t)
+        for (int64_t br = 0; br < bh; ++br)
+            for (int64_t bc = 0; bc < bw; ++bc)
+                for (int64_t mh = 0; mh < merge; ++mh)
+                    for (int64_t mw = 0; mw < merge; ++mw) {
+                        int64_t r = (((t * bh + br) * bw + bc) * merge + mh) * merge + mw;
+                        float *row = rows_out + r * row_len;
+                        for (int64_t c = 0; c < 3; ++c)
+                            for (int64_t tt = 0; tt < temporal; ++tt)
+                                for (int64_t py = 0; py < patch; ++py)
+                                    for (int64_t px = 0; px < patch; ++px) {
+                                        int64_t f = t * temporal + tt;
+                                        int64_t y = (br * merge + mh) * patch + py;
+                                        int64_t x = (bc * merge + mw) * patch + px;
+                                        int64_t e = ((c * temporal + tt) * patch + py) * patch + px;
+                                        row[e] = resized[((f * 3 + c) * OH + y) * OW + x];
+                                    }
+                    }
+    free(rgb);
+    free(planar);
+    free(resized);
+    return ORC_OK;
+}
