@@ -64,8 +64,8 @@ def measured_traffic(workload: str):
 
 
 def cpu_baseline(batch, plan, sample: int, threads: int) -> dict:
-    """The oracle, as it is, on the first `sample` images, one image per
-    thread at a time."""
+    """The oracle, as it is, on the first `sample` items (images, or clips
+    for a video batch), one item per thread at a time."""
     from concurrent.futures import ThreadPoolExecutor
 
     import oracle
@@ -75,15 +75,22 @@ def cpu_baseline(batch, plan, sample: int, threads: int) -> dict:
 
     def one(i):
         d = plan.desc[i]
-        oracle.preprocess_image(batch.image(i), int(d["dst_h"]), int(d["dst_w"]), m, s)
+        if batch.is_media:
+            oracle.preprocess_video(batch.clip(i), int(d["dst_h"]), int(d["dst_w"]), m, s)
+        else:
+            oracle.preprocess_image(batch.image(i), int(d["dst_h"]), int(d["dst_w"]), m, s)
 
     t0 = time.perf_counter()
     with ThreadPoolExecutor(max_workers=threads) as ex:
         list(ex.map(one, idx))
     dt = time.perf_counter() - t0
-    return {"value": len(idx) / dt, "unit": "images/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {len(idx)} of {len(batch)} images of the same batch, one image per "
-                      f"thread, {threads} threads, {dt:.2f} s wall",
+    counts = batch.frame_counts
+    units = sum(counts[i] for i in idx)
+    unit = "frames/s" if batch.is_media else "images/s"
+    what = "clips" if batch.is_media else "images"
+    return {"value": units / dt, "unit": unit, "cores": threads, "kind": "oracle",
+            "sample": f"first {len(idx)} of {len(batch)} {what} of the same batch ({units} "
+                      f"{unit[:-2]}), one item per thread, {threads} threads, {dt:.2f} s wall",
             "seconds": dt, "cpu_model": platform.processor() or platform.machine()}
 
 
@@ -146,7 +153,10 @@ def main():
     V.load()  # fails loudly if the HIP library is not built
     log("generating", args.workload)
     batch = workloads.WORKLOADS[args.workload]()
-    plan = V.plan_batch(batch.shapes)
+    if batch.is_media:
+        plan = V.plan_media(batch.items, video_budget=batch.video_budget)
+    else:
+        plan = V.plan_batch(batch.shapes)
     src = V.processor.upload_sources(batch.packed, plan)
     out_dtype = batch.out_dtype
     tdtype = torch.float32 if out_dtype == "f32" else torch.bfloat16
@@ -191,13 +201,14 @@ def main():
     mean_launch_ms = float(np.mean(per_launch_ms))
     log(f"timed {args.steps} steps: {total_ms:.3f} ms")
 
-    n_img = len(batch)
+    n_img = sum(batch.frame_counts)  # images, or frames of a video batch
+    unit = "frames/s" if batch.is_media else "images/s"
     achieved = alg["total"] / (mean_launch_ms * 1e-3) / 1e9
     traffic = measured_traffic(args.workload)
     result = {
         "metric": METRIC,
         "value": n_img * args.steps / (total_ms * 1e-3),
-        "unit": "images/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -209,9 +220,10 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": args.workload,
-            "images": n_img,
+            ("frames" if batch.is_media else "images"): n_img,
             "source": "uint8 " + ("mixed sizes" if len(set(batch.shapes)) > 1 else
-                                  "{}x{}x{}".format(*batch.shapes[0])),
+                                  "{}x{}x{}".format(*batch.shapes[0])) +
+                      (f", {len(batch)} clips" if batch.is_media else ""),
             "output": f"{out_dtype} rows [{plan.total_rows}, 1536]" +
                       (" in merge-block and column order" if batch.column_order else
                        " in merge-block order"),

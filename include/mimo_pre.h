@@ -74,20 +74,27 @@ typedef struct mimo_params {
 void mimo_default_params(mimo_params *p);
 
 /*
- * Per-image plan, produced by mimo_plan_geometry and consumed unchanged by
- * mimo_preprocess_batch and mimo_column_permute.  64 bytes.
- *   src_offset  byte offset of the image in the packed source buffer; images
- *               are packed back to back in batch order, each row-major
- *               uint8 [src_h][src_w][channels].
+ * Per-item plan, produced by mimo_plan_geometry / mimo_plan_frames and
+ * consumed unchanged by mimo_preprocess_batch and mimo_column_permute.  An
+ * item is a still image (frames = 1) or a video of `frames` frames of one
+ * size.  64 bytes.
+ *   src_offset  byte offset of the item in the packed source buffer; items
+ *               are packed back to back in batch order, each frame row-major
+ *               uint8 [src_h][src_w][channels], the frames of a video back
+ *               to back.
  *   row_offset  first output row of this image (rows of all images are
  *               concatenated in batch order).
  *   rows        grid_t * grid_h * grid_w (get_number_of_image_patches);
  *               placeholder tokens = rows / merge_size^2.
  *   dst_h/dst_w smart_resize target; grid_h = dst_h / patch_size,
- *               grid_w = dst_w / patch_size, grid_t = 1 (two identical
- *               frames make one temporal patch): image_grid_thw.
- *   status      MIMO_OK or the image's MIMO_E_* code; a failed image has
+ *               grid_w = dst_w / patch_size, grid_t = ceil(frames / 2):
+ *               consecutive frames pair into temporal patches, an odd count
+ *               repeating its last frame (so a still image is two identical
+ *               frames, grid_t = 1).  (grid_t, grid_h, grid_w) is
+ *               image_grid_thw / video_grid_thw.
+ *   status      MIMO_OK or the item's MIMO_E_* code; a failed item has
  *               rows = 0 and contributes no output.
+ *   frames      source frames of the item (1 for a still image).
  */
 typedef struct mimo_image_desc {
     int64_t src_offset;
@@ -97,7 +104,7 @@ typedef struct mimo_image_desc {
     int32_t dst_h, dst_w;
     int32_t grid_t, grid_h, grid_w;
     int32_t status;
-    int32_t reserved;
+    int32_t frames;
 } mimo_image_desc;
 
 /*
@@ -127,6 +134,46 @@ int mimo_smart_resize(int64_t h, int64_t w, const mimo_params *params, int64_t *
  */
 int mimo_plan_geometry(int32_t n, const int32_t *hwc, const mimo_params *params,
                        mimo_image_desc *out, int64_t *total_rows, int64_t *total_src_bytes);
+
+/*
+ * Plans a batch of still images and videos (host only, no allocation).
+ *   fhwc       host int32 [n][4]: frames, height, width, channels.  frames = 1
+ *              is a still image; a video's frames share one size.
+ *   max_pixels host int64 [n], nullable: a per-item ceiling on the resized
+ *              area used instead of params->max_pixels (prepare_video_frames:
+ *              the per-frame budget from mimo_video_max_pixels); entries <= 0
+ *              mean params->max_pixels.
+ * One smart_resize per item serves all its frames (cortiq
+ * prepare_video_frames).  Otherwise as mimo_plan_geometry.
+ */
+int mimo_plan_frames(int32_t n, const int32_t *fhwc, const int64_t *max_pixels,
+                     const mimo_params *params, mimo_image_desc *out, int64_t *total_rows,
+                     int64_t *total_src_bytes);
+
+/*
+ * cortiq video_max_pixels: per-frame pixel ceiling for n_sampled frames,
+ * max(min_pixels, min(total_max * temporal_patch_size // n_sampled,
+ * max_pixels)).  total_max is the video's total pixel budget (the pages do
+ * not print a default).  Returns the ceiling, or MIMO_E_INVALID.
+ */
+int64_t mimo_video_max_pixels(int64_t n_sampled, int64_t total_max, const mimo_params *params);
+
+/*
+ * cortiq smart_nframes: frame count for `total` source frames at fps_src
+ * sampled at fps: total / fps_src * fps, clamped to [min_frames,
+ * max_frames], then to at most total, floored to an even count.  Returns the
+ * count, or MIMO_E_INVALID.
+ */
+int64_t mimo_smart_nframes(int64_t total, double fps_src, double fps, int64_t min_frames,
+                           int64_t max_frames);
+
+/*
+ * cortiq sample_frames: indices unique(int64(linspace(0, total - 1, n))) and
+ * timestamps float32(index) / fps_src.  idx (int64) and ts (float) are host
+ * arrays of at least n entries.  Returns the number of indices written, or
+ * MIMO_E_INVALID.
+ */
+int64_t mimo_sample_frames(int64_t total, int64_t n, double fps_src, int64_t *idx, float *ts);
 
 /* Bytes of device workspace mimo_preprocess_batch / mimo_column_permute need
  * for n images (descriptor tables copied from the host on each call). */

@@ -120,7 +120,7 @@ def test_plan_reports_per_image_status():
     assert total_rows == desc["rows"].sum()
     with pytest.raises(V.MimoError):
         V.plan_geometry(shapes)
-    assert "image 1" in V.last_error()
+    assert "item 1" in V.last_error()
 
 
 def test_column_permutation_matches_oracle():
@@ -156,3 +156,61 @@ def test_preprocess_argument_validation_without_gpu():
     assert lib.mimo_column_permute(1, desc.ctypes.data, dummy, dummy, 0, 16, dummy, 4096,
                                    None) == V.MIMO_E_INVALID
     assert V.status_string(V.MIMO_E_DEGENERATE).startswith("degenerate")
+
+
+def test_video_helpers_match_oracle():
+    rng = np.random.default_rng(29)
+    for _ in range(3000):
+        total = int(rng.integers(1, 20000))
+        fps_src = float(rng.uniform(5, 120))
+        fps = float(rng.uniform(0.1, 8))
+        n = V.smart_nframes(total, fps_src, fps, 4, 768)
+        assert n == oracle.smart_nframes(total, fps_src, fps, 4, 768), (total, fps_src, fps)
+        k = max(n, 1)
+        idx, ts = V.sample_frames(total, k, fps_src)
+        ridx, rts = oracle.sample_frames(total, k, fps_src)
+        assert np.array_equal(idx, ridx) and np.array_equal(ts, rts), (total, k, fps_src)
+        total_max = int(rng.integers(1, 1 << 26))
+        assert V.video_max_pixels(k, total_max) == oracle.video_max_pixels(k, total_max)
+
+
+def test_plan_frames_matches_oracle():
+    """Per-item ceilings, grid_t = ceil(frames / 2), rows and offsets for a
+    mix of stills and videos; one-frame items plan exactly like images."""
+    rng = np.random.default_rng(31)
+    items, ceilings = [], []
+    for i in range(200):
+        f = int(rng.integers(1, 40)) if i % 3 else 1
+        h = int(rng.integers(8, 2200))
+        w = int(rng.integers(8, 2200))
+        c = 3 if rng.random() < 0.7 else 4
+        items.append((f, h, w, c))
+        ceilings.append(oracle.video_max_pixels(f, 1 << 24) if f > 1 else 0)
+    desc, total_rows, total_src, code = V.plan_frames(items, ceilings, check=False)
+    rows = src = 0
+    for i, (f, h, w, c) in enumerate(items):
+        mx = ceilings[i] if ceilings[i] > 0 else oracle.MAX_PIXELS
+        st, oh, ow = oracle.smart_resize_status(h, w, 32, oracle.MIN_PIXELS, mx)
+        d = desc[i]
+        assert d["status"] == st, (i, items[i])
+        if st:
+            assert d["rows"] == 0
+            continue
+        gt = (f + 1) // 2
+        assert (d["dst_h"], d["dst_w"], d["frames"]) == (oh, ow, f)
+        assert (d["grid_t"], d["grid_h"], d["grid_w"]) == (gt, oh // 16, ow // 16)
+        assert d["rows"] == gt * (oh // 16) * (ow // 16)
+        assert d["row_offset"] == rows and d["src_offset"] == src
+        rows += int(d["rows"])
+        src += f * h * w * c
+    assert (total_rows, total_src) == (rows, src)
+    stills = [it for it in items if it[0] == 1]
+    gdesc, _, _, _ = V.plan_geometry([it[1:] for it in stills], check=False)
+    fdesc, _, _, _ = V.plan_frames(stills, check=False)
+    assert np.array_equal(gdesc, fdesc)
+
+
+def test_plan_frames_rejects_bad_frame_counts():
+    desc, _, _, code = V.plan_frames([(0, 64, 64, 3), (2, 64, 64, 3), (-3, 64, 64, 3)], check=False)
+    assert list(desc["status"]) == [V.MIMO_E_INVALID, 0, V.MIMO_E_INVALID]
+    assert code == V.MIMO_E_INVALID

@@ -35,7 +35,7 @@ IMAGE_DESC_DTYPE = np.dtype([
     ("src_h", "<i4"), ("src_w", "<i4"), ("channels", "<i4"),
     ("dst_h", "<i4"), ("dst_w", "<i4"),
     ("grid_t", "<i4"), ("grid_h", "<i4"), ("grid_w", "<i4"),
-    ("status", "<i4"), ("reserved", "<i4"),
+    ("status", "<i4"), ("frames", "<i4"),
 ])
 assert IMAGE_DESC_DTYPE.itemsize == 64
 
@@ -70,6 +70,10 @@ SIGNATURES = {
     "mimo_default_params": ([_P], None),
     "mimo_smart_resize": ([_I64, _I64, _P, _P, _P], ctypes.c_int),
     "mimo_plan_geometry": ([_I32, _P, _P, _P, _P, _P], ctypes.c_int),
+    "mimo_plan_frames": ([_I32, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "mimo_video_max_pixels": ([_I64, _I64, _P], _I64),
+    "mimo_smart_nframes": ([_I64, ctypes.c_double, ctypes.c_double, _I64, _I64], _I64),
+    "mimo_sample_frames": ([_I64, _I64, ctypes.c_double, _P, _P], _I64),
     "mimo_workspace_bytes": ([_I32], _SZ),
     "mimo_preprocess_batch": ([_I32, _P, _P, _I64, _P, _P, _I32, _P, _P, _I64, _P, _SZ, _P],
                               ctypes.c_int),
@@ -178,6 +182,55 @@ def plan_geometry(hwc, params: MimoParams | None = None, check: bool = True):
     if check:
         _check(code, "plan_geometry")
     return desc, total_rows.value, total_src.value, code
+
+
+def plan_frames(fhwc, max_pixels=None, params: MimoParams | None = None, check: bool = True):
+    """mimo_plan_frames over an [n, 4] (frames, height, width, channels)
+    table; max_pixels: optional per-item resized-area ceilings ([n] int64,
+    <= 0 for the default).  Returns (desc, total_rows, total_src_bytes,
+    status) like plan_geometry."""
+    fhwc = np.ascontiguousarray(np.asarray(fhwc, dtype=np.int32).reshape(-1, 4))
+    n = fhwc.shape[0]
+    mp = None
+    if max_pixels is not None:
+        mp = np.ascontiguousarray(np.asarray(max_pixels, dtype=np.int64).reshape(n))
+    desc = np.zeros(n, dtype=IMAGE_DESC_DTYPE)
+    total_rows, total_src = ctypes.c_int64(), ctypes.c_int64()
+    code = load().mimo_plan_frames(n, fhwc.ctypes.data, mp.ctypes.data if mp is not None else None,
+                                   ctypes.byref(params) if params is not None else None,
+                                   desc.ctypes.data, ctypes.byref(total_rows),
+                                   ctypes.byref(total_src))
+    if check:
+        _check(code, "plan_frames")
+    return desc, total_rows.value, total_src.value, code
+
+
+def video_max_pixels(n_sampled: int, total_max: int, params: MimoParams | None = None) -> int:
+    """mimo_video_max_pixels: per-frame pixel ceiling for n sampled frames."""
+    v = load().mimo_video_max_pixels(int(n_sampled), int(total_max),
+                                     ctypes.byref(params) if params is not None else None)
+    if v < 0:
+        _check(int(v), "video_max_pixels")
+    return int(v)
+
+
+def smart_nframes(total: int, fps_src: float, fps: float, min_frames: int, max_frames: int) -> int:
+    """mimo_smart_nframes: even frame count for a video of `total` frames."""
+    v = load().mimo_smart_nframes(int(total), float(fps_src), float(fps), int(min_frames),
+                                  int(max_frames))
+    if v < 0:
+        _check(int(v), "smart_nframes")
+    return int(v)
+
+
+def sample_frames(total: int, n: int, fps_src: float):
+    """mimo_sample_frames: (indices int64, timestamps float32)."""
+    idx = np.empty(max(int(n), 1), dtype=np.int64)
+    ts = np.empty(max(int(n), 1), dtype=np.float32)
+    k = load().mimo_sample_frames(int(total), int(n), float(fps_src), idx.ctypes.data, ts.ctypes.data)
+    if k < 0:
+        _check(int(k), "sample_frames")
+    return idx[:k].copy(), ts[:k].copy()
 
 
 def workspace_bytes(n: int) -> int:

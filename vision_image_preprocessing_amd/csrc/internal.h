@@ -41,7 +41,7 @@ struct DevImage {
     float scale_y;          // float32(src_h) / float32(dst_h)
     float scale_x;          // float32(src_w) / float32(dst_w)
     float inv_blocks_h;     // 1 / blocks_h
-    int32_t reserved;
+    int32_t frames;         // source frames (1 for a still image)
 };
 static_assert(sizeof(DevImage) == 64, "DevImage must stay 64 bytes");
 

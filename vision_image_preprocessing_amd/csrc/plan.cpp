@@ -125,52 +125,56 @@ int mimo_smart_resize(int64_t h, int64_t w, const mimo_params *params, int64_t *
     return MIMO_OK;
 }
 
-int mimo_plan_geometry(int32_t n, const int32_t *hwc, const mimo_params *params,
-                       mimo_image_desc *out, int64_t *total_rows, int64_t *total_src_bytes) {
-    clear_error();
-    if (n < 0 || (n > 0 && (!hwc || !out)))
-        return set_error(MIMO_E_INVALID, "plan_geometry: bad n or null pointer");
-    mimo_params def;
-    mimo_default_params(&def);
-    const mimo_params &p = params ? *params : def;
-    if (!params_ok(p)) return set_error(MIMO_E_INVALID, "plan_geometry: invalid parameters");
+}  // extern "C"
+
+namespace mimo {
+namespace {
+
+// Plans n items (still images or videos).  item(i) gives frames, h, w, c;
+// ceiling(i) the resized-area ceiling for item i.
+template <typename Item, typename Ceiling>
+int plan_items(int32_t n, Item item, Ceiling ceiling, const mimo_params &p, mimo_image_desc *out,
+               int64_t *total_rows, int64_t *total_src_bytes) {
     const int64_t patch = p.patch_size;
     const int64_t merge = p.merge_size;
-
+    const int64_t temporal = p.temporal_patch_size;
     int first_error = MIMO_OK;
     std::string first_msg;
     int64_t src_off = 0, row_off = 0;
     for (int32_t i = 0; i < n; ++i) {
+        int32_t f, h, w, c;
+        item(i, f, h, w, c);
         mimo_image_desc d;
         std::memset(&d, 0, sizeof(d));
-        const int32_t h = hwc[3 * i], w = hwc[3 * i + 1], c = hwc[3 * i + 2];
         d.src_h = h;
         d.src_w = w;
         d.channels = c;
+        d.frames = f;
         d.src_offset = src_off;
         d.row_offset = row_off;
+        const int64_t max_px = ceiling(i);
         int st = MIMO_OK;
         std::string msg;
-        if (h < 1 || w < 1 || (c != 3 && c != 4)) {
+        if (f < 1 || h < 1 || w < 1 || (c != 3 && c != 4) || max_px < p.min_pixels) {
             st = MIMO_E_INVALID;
-            msg = "image " + std::to_string(i) + ": bad shape";
+            msg = "item " + std::to_string(i) + ": bad shape or pixel ceiling";
         } else if (h > kMaxSide || w > kMaxSide) {
             st = MIMO_E_TOO_LARGE;
-            msg = "image " + std::to_string(i) + ": side above 2^23 - 1";
+            msg = "item " + std::to_string(i) + ": side above 2^23 - 1";
         } else {
             int64_t oh = 0, ow = 0;
-            st = smart_resize_impl(h, w, patch * merge, p.min_pixels, p.max_pixels, p.max_aspect,
-                                   &oh, &ow);
+            st = smart_resize_impl(h, w, patch * merge, p.min_pixels, max_px, p.max_aspect, &oh, &ow);
+            const int64_t grid_t = (f + temporal - 1) / temporal;
             if (st == MIMO_OK && (oh > kMaxSide || ow > kMaxSide ||
-                                  (oh / patch) * (ow / patch) > kMaxRowsPerImage)) {
+                                  grid_t * (oh / patch) * (ow / patch) > kMaxRowsPerImage)) {
                 st = MIMO_E_TOO_LARGE;
-                msg = "image " + std::to_string(i) + ": resized side above 2^23 - 1 or more than 2^24 rows";
+                msg = "item " + std::to_string(i) + ": resized side above 2^23 - 1 or more than 2^24 rows";
             } else if (st != MIMO_OK) {
-                msg = "image " + std::to_string(i) + ": " + mimo_status_string(st);
+                msg = "item " + std::to_string(i) + ": " + mimo_status_string(st);
             } else {
                 d.dst_h = int32_t(oh);
                 d.dst_w = int32_t(ow);
-                d.grid_t = 1;
+                d.grid_t = int32_t(grid_t);
                 d.grid_h = int32_t(oh / patch);
                 d.grid_w = int32_t(ow / patch);
                 d.rows = int64_t(d.grid_t) * d.grid_h * d.grid_w;
@@ -181,14 +185,104 @@ int mimo_plan_geometry(int32_t n, const int32_t *hwc, const mimo_params *params,
             first_error = st;
             first_msg = msg;
         }
-        if (h > 0 && w > 0 && c > 0) src_off += int64_t(h) * w * c;
+        if (f > 0 && h > 0 && w > 0 && c > 0) src_off += int64_t(f) * h * w * c;
         row_off += d.rows;
         out[i] = d;
     }
     if (total_rows) *total_rows = row_off;
     if (total_src_bytes) *total_src_bytes = src_off;
-    if (first_error != MIMO_OK) return set_error(first_error, "plan_geometry: " + first_msg);
+    if (first_error != MIMO_OK) return set_error(first_error, "plan: " + first_msg);
     return MIMO_OK;
+}
+
+}  // namespace
+}  // namespace mimo
+
+extern "C" {
+
+int mimo_plan_geometry(int32_t n, const int32_t *hwc, const mimo_params *params,
+                       mimo_image_desc *out, int64_t *total_rows, int64_t *total_src_bytes) {
+    clear_error();
+    if (n < 0 || (n > 0 && (!hwc || !out)))
+        return set_error(MIMO_E_INVALID, "plan_geometry: bad n or null pointer");
+    mimo_params def;
+    mimo_default_params(&def);
+    const mimo_params &p = params ? *params : def;
+    if (!params_ok(p)) return set_error(MIMO_E_INVALID, "plan_geometry: invalid parameters");
+    return plan_items(
+        n,
+        [&](int32_t i, int32_t &f, int32_t &h, int32_t &w, int32_t &c) {
+            f = 1;
+            h = hwc[3 * i];
+            w = hwc[3 * i + 1];
+            c = hwc[3 * i + 2];
+        },
+        [&](int32_t) { return p.max_pixels; }, p, out, total_rows, total_src_bytes);
+}
+
+int mimo_plan_frames(int32_t n, const int32_t *fhwc, const int64_t *max_pixels,
+                     const mimo_params *params, mimo_image_desc *out, int64_t *total_rows,
+                     int64_t *total_src_bytes) {
+    clear_error();
+    if (n < 0 || (n > 0 && (!fhwc || !out)))
+        return set_error(MIMO_E_INVALID, "plan_frames: bad n or null pointer");
+    mimo_params def;
+    mimo_default_params(&def);
+    const mimo_params &p = params ? *params : def;
+    if (!params_ok(p)) return set_error(MIMO_E_INVALID, "plan_frames: invalid parameters");
+    return plan_items(
+        n,
+        [&](int32_t i, int32_t &f, int32_t &h, int32_t &w, int32_t &c) {
+            f = fhwc[4 * i];
+            h = fhwc[4 * i + 1];
+            w = fhwc[4 * i + 2];
+            c = fhwc[4 * i + 3];
+        },
+        [&](int32_t i) {
+            return (max_pixels && max_pixels[i] > 0) ? max_pixels[i] : p.max_pixels;
+        },
+        p, out, total_rows, total_src_bytes);
+}
+
+int64_t mimo_video_max_pixels(int64_t n_sampled, int64_t total_max, const mimo_params *params) {
+    clear_error();
+    mimo_params def;
+    mimo_default_params(&def);
+    const mimo_params &p = params ? *params : def;
+    if (n_sampled < 1 || total_max < 0 || !params_ok(p))
+        return set_error(MIMO_E_INVALID, "video_max_pixels: n_sampled >= 1, total_max >= 0");
+    // floor division of non-negative values
+    const int64_t share = total_max * p.temporal_patch_size / n_sampled;
+    return std::max(p.min_pixels, std::min(share, p.max_pixels));
+}
+
+int64_t mimo_smart_nframes(int64_t total, double fps_src, double fps, int64_t min_frames,
+                           int64_t max_frames) {
+    clear_error();
+    if (total < 1 || !(fps_src > 0.0) || !(fps > 0.0) || min_frames > max_frames)
+        return set_error(MIMO_E_INVALID, "smart_nframes: bad arguments");
+    const double want = double(total) / fps_src * fps;
+    const double clamped = std::min(std::min(std::max(want, double(min_frames)), double(max_frames)),
+                                    double(total));
+    return int64_t(std::floor(clamped / 2.0)) * 2;
+}
+
+int64_t mimo_sample_frames(int64_t total, int64_t n, double fps_src, int64_t *idx, float *ts) {
+    clear_error();
+    if (total < 1 || n < 1 || !(fps_src > 0.0) || !idx || !ts)
+        return set_error(MIMO_E_INVALID, "sample_frames: bad arguments");
+    // linspace(0, total - 1, n) as numpy evaluates it: i * step + 0, last = stop
+    const double stop = double(total - 1);
+    const double step = n > 1 ? stop / double(n - 1) : 0.0;
+    int64_t k = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        const double v = (n > 1 && i == n - 1) ? stop : double(i) * step;
+        const int64_t j = int64_t(v);
+        if (k == 0 || idx[k - 1] != j) idx[k++] = j;
+    }
+    const float rate = float(fps_src);
+    for (int64_t i = 0; i < k; ++i) ts[i] = float(idx[i]) / rate;
+    return k;
 }
 
 size_t mimo_workspace_bytes(int32_t n) { return n < 0 ? 0 : ws_total_bytes(n); }

@@ -162,26 +162,27 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// Stores one lane's 4 consecutive values of channel c into both frames of a
-// row.  row_ptr points at the row's element (py*16 + 4q).
+// Stores one lane's 4 consecutive values of channel c into temporal slot tt
+// of a row, or into both slots when tt < 0 (two identical frames).  row_ptr
+// points at the row's element (py*16 + 4q).
 template <typename OutT>
-__device__ __forceinline__ void store_both_frames(OutT *row_ptr, int c, const float (&v)[4]);
+__device__ __forceinline__ void store_frames(OutT *row_ptr, int c, int tt, const float (&v)[4]);
 
 template <>
-__device__ __forceinline__ void store_both_frames<float>(float *row_ptr, int c, const float (&v)[4]) {
+__device__ __forceinline__ void store_frames<float>(float *row_ptr, int c, int tt, const float (&v)[4]) {
     const f32x4 q = {v[0], v[1], v[2], v[3]};
     float *p = row_ptr + c * (kTemporal * kPlane);
-    __builtin_nontemporal_store(q, reinterpret_cast<f32x4 *>(p));
-    __builtin_nontemporal_store(q, reinterpret_cast<f32x4 *>(p + kPlane));
+    if (tt <= 0) __builtin_nontemporal_store(q, reinterpret_cast<f32x4 *>(p));
+    if (tt != 0) __builtin_nontemporal_store(q, reinterpret_cast<f32x4 *>(p + kPlane));
 }
 
 template <>
-__device__ __forceinline__ void store_both_frames<uint16_t>(uint16_t *row_ptr, int c,
-                                                            const float (&v)[4]) {
+__device__ __forceinline__ void store_frames<uint16_t>(uint16_t *row_ptr, int c, int tt,
+                                                       const float (&v)[4]) {
     const u32x2 q = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
     uint16_t *p = row_ptr + c * (kTemporal * kPlane);
-    __builtin_nontemporal_store(q, reinterpret_cast<u32x2 *>(p));
-    __builtin_nontemporal_store(q, reinterpret_cast<u32x2 *>(p + kPlane));
+    if (tt <= 0) __builtin_nontemporal_store(q, reinterpret_cast<u32x2 *>(p));
+    if (tt != 0) __builtin_nontemporal_store(q, reinterpret_cast<u32x2 *>(p + kPlane));
 }
 
 // A raw buffer resource over [first & ~3, src_end): `lead` is first's offset
@@ -241,24 +242,28 @@ __device__ __forceinline__ void load_4px(const SourceWindow &w, uint32_t off, in
     }
 }
 
-// Destination of output row (br, bc, mh, mw): its merge-block position, or
-// its column-order position when `column`.
+// Destination of output row (t, br, bc, mh, mw): its merge-block position,
+// or its column-order position when `column` (units of temporal patch t
+// listed by (block col, block row)).
 template <typename OutT>
-__device__ __forceinline__ OutT *row_dest(OutT *out, const DevImage &d, int br, int bc, int mh,
-                                          int mw, bool column) {
-    const int64_t unit = column ? int64_t(bc) * d.blocks_h + br : int64_t(br) * d.blocks_w + bc;
+__device__ __forceinline__ OutT *row_dest(OutT *out, const DevImage &d, int t, int br, int bc,
+                                          int mh, int mw, bool column) {
+    const int64_t units = int64_t(d.blocks_h) * d.blocks_w;
+    const int64_t unit = t * units +
+                         (column ? int64_t(bc) * d.blocks_h + br : int64_t(br) * d.blocks_w + bc);
     const int64_t row = d.row_offset + unit * kRowsPerUnit + mh * kMerge + mw;
     const int lane = threadIdx.x & 63;
     return out + row * kRowLen + (lane >> 2) * kPatch + 4 * (lane & 3);
 }
 
 // Identity resize (dst == src): output pixel (y, x) is source pixel (y, x).
-// Each lane reads its 4 pixels straight from HBM; no LDS.
+// Each lane reads its 4 pixels straight from HBM; no LDS.  The values go to
+// temporal slot tt of row (t, br, bc, mh, mw), or to both slots if tt < 0.
 template <typename OutT>
 __device__ __forceinline__ void identity_patch(const PreArgs &a, const DevImage &d,
                                                const SourceWindow &w, int64_t row_bytes, int oy0,
-                                               int ox0, int br, int bc, int mh, int mw, OutT *out,
-                                               bool column) {
+                                               int ox0, int t, int tt, int br, int bc, int mh,
+                                               int mw, OutT *out, bool column) {
     const int lane = threadIdx.x & 63;
     const int py = lane >> 2, q = lane & 3;
     const int oy = (br * kMerge + mh) * kPatch + py;
@@ -271,9 +276,9 @@ __device__ __forceinline__ void identity_patch(const PreArgs &a, const DevImage 
     for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int c = 0; c < 3; ++c) v[c][j] = (chan(p[j], c) - a.mean[c]) * a.inv_std[c];
-    OutT *dst = row_dest(out, d, br, bc, mh, mw, column);
+    OutT *dst = row_dest(out, d, t, br, bc, mh, mw, column);
 #pragma unroll
-    for (int c = 0; c < 3; ++c) store_both_frames<OutT>(dst, c, v[c]);
+    for (int c = 0; c < 3; ++c) store_frames<OutT>(dst, c, tt, v[c]);
 }
 
 // Source pixels for the bilinear taps.  Both give the pixel at (y, x) for
@@ -304,8 +309,8 @@ struct GlobalPixels {  // straight from memory, clamped
 // frames.  W taps on the two source rows, then the H tap.
 template <typename OutT, typename Pixels>
 __device__ __forceinline__ void bilinear_patch(const Pixels &px, const DevImage &d, const PreArgs &a,
-                                               int br, int bc, int mh, int mw, OutT *out,
-                                               bool column) {
+                                               int t, int tt, int br, int bc, int mh, int mw,
+                                               OutT *out, bool column) {
     const int lane = threadIdx.x & 63;
     const int py = lane >> 2, q = lane & 3;
     const int oy = (br * kMerge + mh) * kPatch + py;
@@ -327,19 +332,20 @@ __device__ __forceinline__ void bilinear_patch(const Pixels &px, const DevImage 
             v[c][j] = (val - a.mean[c]) * a.inv_std[c];
         }
     }
-    OutT *dst = row_dest(out, d, br, bc, mh, mw, column);
+    OutT *dst = row_dest(out, d, t, br, bc, mh, mw, column);
 #pragma unroll
-    for (int c = 0; c < 3; ++c) store_both_frames<OutT>(dst, c, v[c]);
+    for (int c = 0; c < 3; ++c) store_frames<OutT>(dst, c, tt, v[c]);
 }
 
 // Stages source rows [r_lo, r_lo + rows) x columns [c_lo, c_lo + 4*groups)
 // into LDS, one dword per pixel.  Rows past the last image row repeat it;
 // a column past the last image column is patched afterwards.
 __device__ __forceinline__ void stage_band(uint32_t *band, const PreArgs &a, const DevImage &d,
-                                           int r_lo, int c_lo, int rows, int groups, int pitch) {
+                                           int64_t frame_offset, int r_lo, int c_lo, int rows,
+                                           int groups, int pitch) {
     const int C = d.channels;
     const int64_t row_bytes = int64_t(d.src_w) * C;
-    const uint64_t first = reinterpret_cast<uint64_t>(a.src) + uint64_t(d.src_offset) +
+    const uint64_t first = reinterpret_cast<uint64_t>(a.src) + uint64_t(frame_offset) +
                            uint64_t(int64_t(r_lo) * row_bytes + int64_t(c_lo) * C);
     const SourceWindow w = source_window(a, first);
     const int last_row = d.src_h - 1 - r_lo;  // band row of the image's last row
@@ -391,7 +397,14 @@ __global__ __launch_bounds__(kThreads) void preprocess_kernel(PreArgs a) {
     OutT *const out = static_cast<OutT *>(column ? a.rows_col : a.rows);
     const int img = find_segment(a.tile_begin, a.n, tile);
     const DevImage d = a.images[img];
-    const int local = int(tile - a.tile_begin[img]);
+    int local = int(tile - a.tile_begin[img]);
+    // temporal patch t of a video: tiles are listed slice by slice
+    int t = 0;
+    if (d.frames > kTemporal) {
+        const int per_slice = d.blocks_h * d.tiles_per_brow;
+        t = div_small(local, per_slice, 1.0f / float(per_slice));
+        local -= t * per_slice;
+    }
     const int R = a.rows_per_tile;
     int br, first, count;
     if (!column) {
@@ -428,15 +441,29 @@ __global__ __launch_bounds__(kThreads) void preprocess_kernel(PreArgs a) {
     const int wave = threadIdx.x >> 6;
     const int waves = blockDim.x >> 6;
 
+    // Temporal slot tt of patch t shows frame min(2t + tt, frames - 1): an
+    // odd frame count repeats its last frame, a still image is two copies of
+    // its one frame.  Identical frames are computed once and stored to both
+    // slots (tt = -1); distinct frames take one pass per slot.
+    const int64_t frame_bytes = int64_t(d.src_h) * d.src_w * d.channels;
+    const int f0 = min(kTemporal * t, d.frames - 1);
+    const int f1 = min(kTemporal * t + 1, d.frames - 1);
+    const int passes = f0 == f1 ? 1 : 2;
+
     if (d.flags & kFlagIdentity) {
         const int64_t row_bytes = int64_t(d.src_w) * d.channels;
-        const uint64_t first_byte = reinterpret_cast<uint64_t>(a.src) + uint64_t(d.src_offset) +
-                                    uint64_t(int64_t(oy_first) * row_bytes + int64_t(ox_first) * d.channels);
-        const SourceWindow w = source_window(a, first_byte);
-        for (int p = wave; p < count; p += waves) {
-            const int qr = first + p;  // row within the block row: (block col, mh, mw)
-            identity_patch<OutT>(a, d, w, row_bytes, oy_first, ox_first, br, qr >> 2, (qr >> 1) & 1,
-                                 qr & 1, out, column);
+        for (int fp = 0; fp < passes; ++fp) {
+            const int64_t frame_offset = d.src_offset + int64_t(fp == 0 ? f0 : f1) * frame_bytes;
+            const uint64_t first_byte = reinterpret_cast<uint64_t>(a.src) + uint64_t(frame_offset) +
+                                        uint64_t(int64_t(oy_first) * row_bytes +
+                                                 int64_t(ox_first) * d.channels);
+            const SourceWindow w = source_window(a, first_byte);
+            const int tt = passes == 1 ? -1 : fp;
+            for (int p = wave; p < count; p += waves) {
+                const int qr = first + p;  // row within the block row: (block col, mh, mw)
+                identity_patch<OutT>(a, d, w, row_bytes, oy_first, ox_first, t, tt, br, qr >> 2,
+                                     (qr >> 1) & 1, qr & 1, out, column);
+            }
         }
         return;
     }
@@ -455,25 +482,31 @@ __global__ __launch_bounds__(kThreads) void preprocess_kernel(PreArgs a) {
     const int64_t band_bytes = int64_t(rows) * d.src_w * d.channels;
     const bool fits = int64_t(rows) * pitch <= a.band_capacity && band_bytes < 0x7FFF0000ll;
 
-    if (fits) {
-        stage_band(band, a, d, r_lo, c_lo, rows, groups, pitch);
-        __syncthreads();
-        if (c_end == d.src_w) {  // second tap at the right edge: repeat the last column
-            const int xl = d.src_w - 1 - c_lo;
-            for (int r = threadIdx.x; r < rows; r += blockDim.x) band[r * pitch + xl + 1] = band[r * pitch + xl];
+    for (int fp = 0; fp < passes; ++fp) {
+        const int64_t frame_offset = d.src_offset + int64_t(fp == 0 ? f0 : f1) * frame_bytes;
+        const int tt = passes == 1 ? -1 : fp;
+        if (fits) {
+            if (fp > 0) __syncthreads();  // the previous frame's band is no longer read
+            stage_band(band, a, d, frame_offset, r_lo, c_lo, rows, groups, pitch);
             __syncthreads();
-        }
-        const BandPixels px{band, pitch, r_lo, c_lo};
-        for (int p = wave; p < count; p += waves) {
-            const int qr = first + p;
-            bilinear_patch<OutT>(px, d, a, br, qr >> 2, (qr >> 1) & 1, qr & 1, out, column);
-        }
-    } else {
-        const GlobalPixels px{a.src + d.src_offset, int64_t(d.src_w) * d.channels, d.channels,
-                              d.src_h, d.src_w};
-        for (int p = wave; p < count; p += waves) {
-            const int qr = first + p;
-            bilinear_patch<OutT>(px, d, a, br, qr >> 2, (qr >> 1) & 1, qr & 1, out, column);
+            if (c_end == d.src_w) {  // second tap at the right edge: repeat the last column
+                const int xl = d.src_w - 1 - c_lo;
+                for (int r = threadIdx.x; r < rows; r += blockDim.x)
+                    band[r * pitch + xl + 1] = band[r * pitch + xl];
+                __syncthreads();
+            }
+            const BandPixels px{band, pitch, r_lo, c_lo};
+            for (int p = wave; p < count; p += waves) {
+                const int qr = first + p;
+                bilinear_patch<OutT>(px, d, a, t, tt, br, qr >> 2, (qr >> 1) & 1, qr & 1, out, column);
+            }
+        } else {
+            const GlobalPixels px{a.src + frame_offset, int64_t(d.src_w) * d.channels, d.channels,
+                                  d.src_h, d.src_w};
+            for (int p = wave; p < count; p += waves) {
+                const int qr = first + p;
+                bilinear_patch<OutT>(px, d, a, t, tt, br, qr >> 2, (qr >> 1) & 1, qr & 1, out, column);
+            }
         }
     }
 }
@@ -489,10 +522,14 @@ __global__ __launch_bounds__(kThreads) void column_permute_kernel(PermArgs a) {
     const int64_t drow = unit * kRowsPerUnit;
     const int img = find_segment(a.row_begin, a.n, drow);
     const DevImage d = a.images[img];
-    const int j = int((drow - d.row_offset) / kRowsPerUnit);  // column-order unit index
+    const int units = d.blocks_h * d.blocks_w;  // per temporal patch
+    const int ju = int((drow - d.row_offset) / kRowsPerUnit);  // column-order unit index
+    const int t = ju / units;
+    const int j = ju - t * units;
     const int bc = div_small(j, d.blocks_h, d.inv_blocks_h);
     const int br = j - bc * d.blocks_h;
-    const int64_t src_row = d.row_offset + (int64_t(br) * d.blocks_w + bc) * kRowsPerUnit;
+    const int64_t src_row =
+        d.row_offset + (int64_t(t) * units + int64_t(br) * d.blocks_w + bc) * kRowsPerUnit;
     constexpr int kVecs = kRowsPerUnit * kRowLen * int(sizeof(OutT)) / 16;  // 16-byte vectors per unit
     const u32x4 *in = reinterpret_cast<const u32x4 *>(static_cast<const OutT *>(a.in) + src_row * kRowLen);
     u32x4 *out = reinterpret_cast<u32x4 *>(static_cast<OutT *>(a.out) + drow * kRowLen);
@@ -658,10 +695,12 @@ int build_tables(int32_t n, const mimo_image_desc *desc, const Tiling &tiling, B
             img[i] = d;
             continue;
         }
-        if (s.src_h < 1 || s.src_w < 1 || (s.channels != 3 && s.channels != 4) ||
+        if (s.src_h < 1 || s.src_w < 1 || (s.channels != 3 && s.channels != 4) || s.frames < 1 ||
             s.dst_h < kUnitPx || s.dst_w < kUnitPx || s.dst_h % kUnitPx || s.dst_w % kUnitPx ||
-            s.grid_t != 1 || s.grid_h * kPatch != s.dst_h || s.grid_w * kPatch != s.dst_w ||
-            s.rows != int64_t(s.grid_h) * s.grid_w || s.row_offset != rows || s.src_offset < 0)
+            s.grid_t != (s.frames + kTemporal - 1) / kTemporal || s.grid_h * kPatch != s.dst_h ||
+            s.grid_w * kPatch != s.dst_w ||
+            s.rows != int64_t(s.grid_t) * s.grid_h * s.grid_w || s.rows > kMaxRowsPerImage ||
+            s.row_offset != rows || s.src_offset < 0)
             return set_error(MIMO_E_INVALID, "descriptor " + std::to_string(i) +
                                                  " is not a plan of the 16/2/2 kernels");
         if (s.src_h > kMaxSide || s.src_w > kMaxSide || s.dst_h > kMaxSide || s.dst_w > kMaxSide)
@@ -669,6 +708,7 @@ int build_tables(int32_t n, const mimo_image_desc *desc, const Tiling &tiling, B
         d.src_h = s.src_h;
         d.src_w = s.src_w;
         d.channels = s.channels;
+        d.frames = s.frames;
         d.blocks_h = s.dst_h / kUnitPx;
         d.blocks_w = s.dst_w / kUnitPx;
         d.scale_y = float(s.src_h) / float(s.dst_h);
@@ -681,7 +721,7 @@ int build_tables(int32_t n, const mimo_image_desc *desc, const Tiling &tiling, B
         d.inv_tiles_per_brow = 1.0f / float(d.tiles_per_brow);
         d.inv_blocks_h = 1.0f / float(d.blocks_h);
         img[i] = d;
-        tiles += int64_t(d.blocks_h) * d.tiles_per_brow;
+        tiles += int64_t(s.grid_t) * d.blocks_h * d.tiles_per_brow;
         rows += s.rows;
     }
     tile_begin[n] = tiles;
@@ -748,8 +788,9 @@ int mimo_preprocess_batch(int32_t n, const mimo_image_desc *desc, const uint8_t 
     int64_t src_needed = 0;
     for (int32_t i = 0; i < n; ++i)
         if (desc[i].status == MIMO_OK && desc[i].rows > 0)
-            src_needed = std::max<int64_t>(src_needed, desc[i].src_offset + int64_t(desc[i].src_h) *
-                                                                             desc[i].src_w * desc[i].channels);
+            src_needed = std::max<int64_t>(src_needed, desc[i].src_offset +
+                                                           int64_t(desc[i].frames) * desc[i].src_h *
+                                                               desc[i].src_w * desc[i].channels);
     if (src_capacity < ((src_needed + 15) & ~int64_t(15)))
         return set_error(MIMO_E_CAPACITY, "preprocess_batch: src_capacity below the packed size rounded up to 16");
     if (t.total_rows > capacity_rows)

@@ -39,6 +39,11 @@ class BatchPlan:
         return max(16, (self.total_src_bytes + 15) // 16 * 16)
 
     @property
+    def grid_thw(self) -> np.ndarray:
+        """(grid_t, grid_h, grid_w) per item: image_grid_thw / video_grid_thw."""
+        return self.image_grid_thw
+
+    @property
     def image_grid_thw(self) -> np.ndarray:
         return np.stack([self.desc["grid_t"], self.desc["grid_h"], self.desc["grid_w"]],
                         axis=1).astype(np.int64)
@@ -52,6 +57,32 @@ def plan_batch(shapes, min_pixels=None, max_pixels=None, check: bool = True) -> 
     params = _abi.make_params(min_pixels, max_pixels)
     desc, rows, src, _ = _abi.plan_geometry(np.asarray(shapes, dtype=np.int32).reshape(-1, 3),
                                             params, check=check)
+    return BatchPlan(desc=desc, total_rows=rows, total_src_bytes=src)
+
+
+def plan_media(items, max_pixels=None, min_pixels=None, video_budget=None,
+               check: bool = True) -> BatchPlan:
+    """Plans still images and already-sampled clips given as (frames, height,
+    width, channels) tuples (prepare_video_frames, inference page).
+
+    max_pixels: one resized-area ceiling for every item, or one per item.
+    video_budget: a clip's total pixel budget (one value or one per item; 0
+    for none); where it is set, the item's ceiling is the per-frame share
+    mimo_video_max_pixels gives for its sampled frame count.
+    """
+    params = _abi.make_params(min_pixels, None)
+    items = np.asarray(items, dtype=np.int32).reshape(-1, 4)
+    n = items.shape[0]
+    ceilings = np.zeros(n, dtype=np.int64)
+    if max_pixels is not None:
+        ceilings[:] = np.broadcast_to(np.asarray(max_pixels, dtype=np.int64), (n,))
+    if video_budget is not None:
+        budget = np.broadcast_to(np.asarray(video_budget, dtype=np.int64), (n,))
+        vparams = _abi.make_params(min_pixels, max_pixels if np.isscalar(max_pixels) else None)
+        for i in range(n):
+            if budget[i] > 0 and items[i, 0] > 0:
+                ceilings[i] = _abi.video_max_pixels(int(items[i, 0]), int(budget[i]), vparams)
+    desc, rows, src, _ = _abi.plan_frames(items, ceilings, params, check=check)
     return BatchPlan(desc=desc, total_rows=rows, total_src_bytes=src)
 
 

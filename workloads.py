@@ -24,6 +24,11 @@ Workloads:
   (lattices 512/256/128/64 px, amplitudes 1/2^k, smoothstep-interpolated),
   scaled to [0, 255].
 * ``throughput_512_1024`` -- 512 RGB 1024x1024 images, uniform pixels.
+* ``video_8x64_1280x720`` -- 8 already-sampled RGB clips of 64 frames,
+  1280x720: each clip pans across one 4-octave value-noise field (8 px to
+  the right per frame) with N(0, 4^2) per-frame sensor noise, rounded and
+  clipped; a 2^24-pixel budget per clip (per-frame ceiling from the sampled
+  count), bf16 rows.
 """
 from __future__ import annotations
 
@@ -45,34 +50,57 @@ CLIP_STD = (0.26862954, 0.26130258, 0.27577711)
 
 @dataclass
 class Batch:
-    """Images packed back to back (each uint8 [h, w, c], row-major) in one
-    flat buffer, in batch order."""
+    """Items packed back to back in one flat buffer, in batch order: a still
+    image is uint8 [h, w, c] (row-major), a clip is its frames [f, h, w, c]
+    one after another."""
 
     name: str
     shapes: list  # [(h, w, c)]
     packed: np.ndarray  # uint8, flat
-    offsets: np.ndarray  # int64 [n], byte offset of each image
+    offsets: np.ndarray  # int64 [n], byte offset of each item
     mean: tuple
     std: tuple
     out_dtype: str  # "f32" or "bf16"
     column_order: bool = False
     notes: dict = field(default_factory=dict)
+    frames: list | None = None  # frames per item (None: all stills)
+    video_budget: list | None = None  # per-item total pixel budget of a clip (0: none)
 
     def __len__(self):
         return len(self.shapes)
+
+    @property
+    def frame_counts(self) -> list:
+        return list(self.frames) if self.frames is not None else [1] * len(self.shapes)
+
+    @property
+    def items(self) -> list:
+        """(frames, h, w, c) per item."""
+        return [(f, h, w, c) for f, (h, w, c) in zip(self.frame_counts, self.shapes)]
+
+    @property
+    def is_media(self) -> bool:
+        return self.frames is not None
 
     def image(self, i: int) -> np.ndarray:
         h, w, c = self.shapes[i]
         o = int(self.offsets[i])
         return self.packed[o:o + h * w * c].reshape(h, w, c)
 
+    def clip(self, i: int) -> np.ndarray:
+        f = self.frame_counts[i]
+        h, w, c = self.shapes[i]
+        o = int(self.offsets[i])
+        return self.packed[o:o + f * h * w * c].reshape(f, h, w, c)
+
     @property
     def src_bytes(self) -> int:
         return int(self.packed.size)
 
 
-def _pack(shapes):
-    sizes = np.array([h * w * c for (h, w, c) in shapes], dtype=np.int64)
+def _pack(shapes, frames=None):
+    frames = frames if frames is not None else [1] * len(shapes)
+    sizes = np.array([f * h * w * c for f, (h, w, c) in zip(frames, shapes)], dtype=np.int64)
     offsets = np.zeros(len(shapes), dtype=np.int64)
     if len(shapes) > 1:
         offsets[1:] = np.cumsum(sizes)[:-1]
@@ -220,12 +248,67 @@ def throughput_512_1024(seed: int = 5, n: int = 512, side: int = 1024) -> Batch:
                           column_order=True)
 
 
+def _panning_clip(rng, frames, h, w, step=8, sigma=4.0):
+    """One clip: a window sliding `step` px right per frame over a wider
+    3-channel value-noise field, plus per-frame Gaussian noise."""
+    fw = w + step * (frames - 1)
+    field_ = np.stack([_value_noise(rng, h, fw) for _ in range(3)], axis=-1) * 255.0
+    out = np.empty((frames, h, w, 3), dtype=np.uint8)
+    for f in range(frames):
+        x0 = f * step
+        v = field_[:, x0:x0 + w] + rng.normal(0.0, sigma, size=(h, w, 3)).astype(np.float32)
+        out[f] = np.clip(np.rint(v), 0, 255)
+    return out
+
+
+def video_clips(name, clips, frames, h, w, seed, total_max=1 << 24,
+                out_dtype="bf16") -> Batch:
+    """`clips` RGB clips of `frames` already-sampled frames each, with a
+    total pixel budget of `total_max` per clip (the caller's video budget; the
+    per-frame ceiling derived from it belongs to the method)."""
+    shapes = [(h, w, 3)] * clips
+    counts = [frames] * clips
+    offsets, total = _pack(shapes, counts)
+    packed = np.empty(total, dtype=np.uint8)
+    rngs = _image_rngs(seed, clips)
+    size = frames * h * w * 3
+
+    def one(i):
+        packed[offsets[i]:offsets[i] + size] = _panning_clip(rngs[i], frames, h, w).reshape(-1)
+
+    _pool_map(one, list(range(clips)))
+    return Batch(name=name, shapes=shapes, packed=packed, offsets=offsets, mean=IMAGENET_MEAN,
+                 std=IMAGENET_STD, out_dtype=out_dtype, frames=counts,
+                 video_budget=[total_max] * clips)
+
+
+def video_8x64_1280x720(seed: int = 6) -> Batch:
+    return video_clips("video_8x64_1280x720", 8, 64, 720, 1280, seed)
+
+
+def media_batch(items, seed: int, video_budget=None, name="custom_media") -> Batch:
+    """Uniform pixels for (frames, h, w, c) items (tests); video_budget: the
+    total pixel budget per item (0: none), one value or one per item."""
+    items = [tuple(int(v) for v in it) for it in items]
+    shapes = [it[1:] for it in items]
+    counts = [it[0] for it in items]
+    rng = np.random.default_rng(seed)
+    offsets, total = _pack(shapes, counts)
+    packed = rng.integers(0, 256, size=total, dtype=np.uint8)
+    vb = None
+    if video_budget is not None:
+        vb = [int(v) for v in np.broadcast_to(video_budget, (len(items),))]
+    return Batch(name=name, shapes=shapes, packed=packed, offsets=offsets, mean=IMAGENET_MEAN,
+                 std=IMAGENET_STD, out_dtype="f32", frames=counts, video_budget=vb)
+
+
 WORKLOADS = {
     "single_rgb_300x200": single_rgb_300x200,
     "rgba_64_mixed": rgba_64_mixed,
     "subfactor_256": subfactor_256,
     "large_16_6000x4000": large_16_6000x4000,
     "throughput_512_1024": throughput_512_1024,
+    "video_8x64_1280x720": video_8x64_1280x720,
 }
 
 
