@@ -238,7 +238,8 @@ def main():
             "traffic": traffic,
         },
         "algorithmic_bytes_per_step": alg,
-        "kernel": "preprocess_kernel<float>" if out_dtype == "f32" else "preprocess_kernel<bf16>",
+        "kernel": "preprocess_kernel<{}, {}>".format("float" if out_dtype == "f32" else "bf16",
+                                                     "clips" if batch.is_media else "stills"),
         "launch_ms_mean": mean_launch_ms,
         "launch_ms_min": float(np.min(per_launch_ms)),
         "launch_ms_median": float(np.median(per_launch_ms)),

@@ -162,27 +162,23 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// Stores one lane's 4 consecutive values of channel c into temporal slot tt
-// of a row, or into both slots when tt < 0 (two identical frames).  row_ptr
+// Stores one lane's 4 consecutive values of channel c into temporal slot TT
+// of a row, or into both slots when TT < 0 (two identical frames).  row_ptr
 // points at the row's element (py*16 + 4q).
-template <typename OutT>
-__device__ __forceinline__ void store_frames(OutT *row_ptr, int c, int tt, const float (&v)[4]);
-
-template <>
-__device__ __forceinline__ void store_frames<float>(float *row_ptr, int c, int tt, const float (&v)[4]) {
+template <int TT>
+__device__ __forceinline__ void store_frames(float *row_ptr, int c, const float (&v)[4]) {
     const f32x4 q = {v[0], v[1], v[2], v[3]};
     float *p = row_ptr + c * (kTemporal * kPlane);
-    if (tt <= 0) __builtin_nontemporal_store(q, reinterpret_cast<f32x4 *>(p));
-    if (tt != 0) __builtin_nontemporal_store(q, reinterpret_cast<f32x4 *>(p + kPlane));
+    if (TT <= 0) __builtin_nontemporal_store(q, reinterpret_cast<f32x4 *>(p));
+    if (TT != 0) __builtin_nontemporal_store(q, reinterpret_cast<f32x4 *>(p + kPlane));
 }
 
-template <>
-__device__ __forceinline__ void store_frames<uint16_t>(uint16_t *row_ptr, int c, int tt,
-                                                       const float (&v)[4]) {
+template <int TT>
+__device__ __forceinline__ void store_frames(uint16_t *row_ptr, int c, const float (&v)[4]) {
     const u32x2 q = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
     uint16_t *p = row_ptr + c * (kTemporal * kPlane);
-    if (tt <= 0) __builtin_nontemporal_store(q, reinterpret_cast<u32x2 *>(p));
-    if (tt != 0) __builtin_nontemporal_store(q, reinterpret_cast<u32x2 *>(p + kPlane));
+    if (TT <= 0) __builtin_nontemporal_store(q, reinterpret_cast<u32x2 *>(p));
+    if (TT != 0) __builtin_nontemporal_store(q, reinterpret_cast<u32x2 *>(p + kPlane));
 }
 
 // A raw buffer resource over [first & ~3, src_end): `lead` is first's offset
@@ -258,12 +254,12 @@ __device__ __forceinline__ OutT *row_dest(OutT *out, const DevImage &d, int t, i
 
 // Identity resize (dst == src): output pixel (y, x) is source pixel (y, x).
 // Each lane reads its 4 pixels straight from HBM; no LDS.  The values go to
-// temporal slot tt of row (t, br, bc, mh, mw), or to both slots if tt < 0.
-template <typename OutT>
+// temporal slot TT of row (t, br, bc, mh, mw), or to both slots if TT < 0.
+template <typename OutT, int TT>
 __device__ __forceinline__ void identity_patch(const PreArgs &a, const DevImage &d,
                                                const SourceWindow &w, int64_t row_bytes, int oy0,
-                                               int ox0, int t, int tt, int br, int bc, int mh,
-                                               int mw, OutT *out, bool column) {
+                                               int ox0, int t, int br, int bc, int mh, int mw,
+                                               OutT *out, bool column) {
     const int lane = threadIdx.x & 63;
     const int py = lane >> 2, q = lane & 3;
     const int oy = (br * kMerge + mh) * kPatch + py;
@@ -278,7 +274,7 @@ __device__ __forceinline__ void identity_patch(const PreArgs &a, const DevImage 
         for (int c = 0; c < 3; ++c) v[c][j] = (chan(p[j], c) - a.mean[c]) * a.inv_std[c];
     OutT *dst = row_dest(out, d, t, br, bc, mh, mw, column);
 #pragma unroll
-    for (int c = 0; c < 3; ++c) store_frames<OutT>(dst, c, tt, v[c]);
+    for (int c = 0; c < 3; ++c) store_frames<TT>(dst, c, v[c]);
 }
 
 // Source pixels for the bilinear taps.  Both give the pixel at (y, x) for
@@ -305,12 +301,13 @@ struct GlobalPixels {  // straight from memory, clamped
     }
 };
 
-// Bilinear output row (br, bc, mh, mw): a 16x16 patch, 3 channels, both
-// frames.  W taps on the two source rows, then the H tap.
-template <typename OutT, typename Pixels>
+// Bilinear output row (t, br, bc, mh, mw): a 16x16 patch, 3 channels, into
+// temporal slot TT (both slots if TT < 0).  W taps on the two source rows,
+// then the H tap.
+template <typename OutT, int TT, typename Pixels>
 __device__ __forceinline__ void bilinear_patch(const Pixels &px, const DevImage &d, const PreArgs &a,
-                                               int t, int tt, int br, int bc, int mh, int mw,
-                                               OutT *out, bool column) {
+                                               int t, int br, int bc, int mh, int mw, OutT *out,
+                                               bool column) {
     const int lane = threadIdx.x & 63;
     const int py = lane >> 2, q = lane & 3;
     const int oy = (br * kMerge + mh) * kPatch + py;
@@ -334,7 +331,7 @@ __device__ __forceinline__ void bilinear_patch(const Pixels &px, const DevImage 
     }
     OutT *dst = row_dest(out, d, t, br, bc, mh, mw, column);
 #pragma unroll
-    for (int c = 0; c < 3; ++c) store_frames<OutT>(dst, c, tt, v[c]);
+    for (int c = 0; c < 3; ++c) store_frames<TT>(dst, c, v[c]);
 }
 
 // Stages source rows [r_lo, r_lo + rows) x columns [c_lo, c_lo + 4*groups)
@@ -385,7 +382,93 @@ __device__ __forceinline__ int64_t xcd_contiguous_tile(int64_t b, int64_t grid) 
     return b < per * kXcds ? (b % kXcds) * per + b / kXcds : b;
 }
 
-template <typename OutT>
+// What one workgroup's tile covers: temporal patch t, block row br, rows
+// [first, first + count) of that block row (merge order) or of its column-
+// order unit, and the output pixel rectangle those rows cover.
+struct TileGeom {
+    int t, br, first, count;
+    int oy_first, oy_last, ox_first, ox_last;
+};
+
+// Source band touched by a tile: taps are monotone in the output index, so
+// the first and last output rows/columns bound it.  The band runs one past
+// the last first-tap so that the second tap is always i0 + 1; at the image
+// edge that row/column repeats the last one.
+struct Band {
+    int r_lo, c_lo, c_end, rows, groups, pitch;
+    bool fits;  // the band fits the LDS
+};
+
+__device__ __forceinline__ Band tile_band(const PreArgs &a, const DevImage &d, const TileGeom &g) {
+    Band b;
+    b.r_lo = make_tap(d.scale_y, g.oy_first, d.src_h).i0;
+    const int r_end = make_tap(d.scale_y, g.oy_last, d.src_h).i0 + 1;
+    b.c_lo = make_tap(d.scale_x, g.ox_first, d.src_w).i0;
+    b.c_end = make_tap(d.scale_x, g.ox_last, d.src_w).i0 + 1;
+    b.rows = r_end - b.r_lo + 1;
+    b.groups = (b.c_end - b.c_lo + 4) >> 2;
+    b.pitch = 4 * b.groups;
+    b.fits = int64_t(b.rows) * b.pitch <= a.band_capacity &&
+             int64_t(b.rows) * d.src_w * d.channels < 0x7FFF0000ll;
+    return b;
+}
+
+// At the right image edge the band's last column is the second tap of the
+// last first-tap: repeat the image's last column there.
+__device__ __forceinline__ void replicate_right_edge(uint32_t *band, const DevImage &d, const Band &b) {
+    const int xl = d.src_w - 1 - b.c_lo;
+    for (int r = threadIdx.x; r < b.rows; r += blockDim.x)
+        band[r * b.pitch + xl + 1] = band[r * b.pitch + xl];
+}
+
+// Resamples one source frame (at frame_offset) of the tile into temporal
+// slot TT of its rows (both slots when TT < 0).
+template <typename OutT, int TT>
+__device__ __forceinline__ void tile_pass(const PreArgs &a, const DevImage &d, const TileGeom &g,
+                                          int64_t frame_offset, OutT *out, bool column,
+                                          uint32_t *band) {
+    const int wave = threadIdx.x >> 6;
+    const int waves = blockDim.x >> 6;
+    if (d.flags & kFlagIdentity) {
+        const int64_t row_bytes = int64_t(d.src_w) * d.channels;
+        const uint64_t first_byte = reinterpret_cast<uint64_t>(a.src) + uint64_t(frame_offset) +
+                                    uint64_t(int64_t(g.oy_first) * row_bytes +
+                                             int64_t(g.ox_first) * d.channels);
+        const SourceWindow w = source_window(a, first_byte);
+        for (int p = wave; p < g.count; p += waves) {
+            const int qr = g.first + p;  // row within the block row: (block col, mh, mw)
+            identity_patch<OutT, TT>(a, d, w, row_bytes, g.oy_first, g.ox_first, g.t, g.br, qr >> 2,
+                                     (qr >> 1) & 1, qr & 1, out, column);
+        }
+        return;
+    }
+
+    const Band b = tile_band(a, d, g);
+    if (b.fits) {
+        stage_band(band, a, d, frame_offset, b.r_lo, b.c_lo, b.rows, b.groups, b.pitch);
+        __syncthreads();
+        if (b.c_end == d.src_w) {
+            replicate_right_edge(band, d, b);
+            __syncthreads();
+        }
+        const BandPixels px{band, b.pitch, b.r_lo, b.c_lo};
+        for (int p = wave; p < g.count; p += waves) {
+            const int qr = g.first + p;
+            bilinear_patch<OutT, TT>(px, d, a, g.t, g.br, qr >> 2, (qr >> 1) & 1, qr & 1, out, column);
+        }
+    } else {
+        const GlobalPixels px{a.src + frame_offset, int64_t(d.src_w) * d.channels, d.channels,
+                              d.src_h, d.src_w};
+        for (int p = wave; p < g.count; p += waves) {
+            const int qr = g.first + p;
+            bilinear_patch<OutT, TT>(px, d, a, g.t, g.br, qr >> 2, (qr >> 1) & 1, qr & 1, out, column);
+        }
+    }
+}
+
+// kClips: the batch holds at least one clip (an item with two or more
+// frames); batches of still images compile without the temporal decode.
+template <typename OutT, bool kClips>
 __global__ __launch_bounds__(kThreads) void preprocess_kernel(PreArgs a) {
     extern __shared__ uint32_t band[];
     int64_t tile = a.xcd_order ? xcd_contiguous_tile(blockIdx.x, gridDim.x) : int64_t(blockIdx.x);
@@ -398,116 +481,64 @@ __global__ __launch_bounds__(kThreads) void preprocess_kernel(PreArgs a) {
     const int img = find_segment(a.tile_begin, a.n, tile);
     const DevImage d = a.images[img];
     int local = int(tile - a.tile_begin[img]);
-    // temporal patch t of a video: tiles are listed slice by slice
-    int t = 0;
-    if (d.frames > kTemporal) {
+    TileGeom g;
+    // temporal patch t of a clip: tiles are listed slice by slice
+    g.t = 0;
+    if (kClips && d.frames > kTemporal) {
         const int per_slice = d.blocks_h * d.tiles_per_brow;
-        t = div_small(local, per_slice, 1.0f / float(per_slice));
-        local -= t * per_slice;
+        g.t = div_small(local, per_slice, 1.0f / float(per_slice));
+        local -= g.t * per_slice;
     }
     const int R = a.rows_per_tile;
-    int br, first, count;
     if (!column) {
-        br = div_small(local, d.tiles_per_brow, d.inv_tiles_per_brow);
-        first = (local - br * d.tiles_per_brow) * R;  // first row within the block row
-        count = min(R, d.blocks_w * kRowsPerUnit - first);
+        g.br = div_small(local, d.tiles_per_brow, d.inv_tiles_per_brow);
+        g.first = (local - g.br * d.tiles_per_brow) * R;  // first row within the block row
+        g.count = min(R, d.blocks_w * kRowsPerUnit - g.first);
     } else {
         // column order lists units by (block col, block row); R <= 4 divides
         // a unit, so a tile is part of one unit
         const int rc = local * R;
         const int unit = rc >> 2;
         const int bc = div_small(unit, d.blocks_h, d.inv_blocks_h);
-        br = unit - bc * d.blocks_h;
-        first = bc * kRowsPerUnit + (rc & 3);
-        count = R;
+        g.br = unit - bc * d.blocks_h;
+        g.first = bc * kRowsPerUnit + (rc & 3);
+        g.count = R;
     }
 
     // Output rectangle of the tile: whole merge units when R >= 4, else one
     // patch row (mh fixed) of one unit, one or both of its patches.
-    int oy_first, oy_last, ox_first, ox_last;
     if (R >= kRowsPerUnit) {
-        oy_first = br * kUnitPx;
-        oy_last = oy_first + kUnitPx - 1;
-        ox_first = (first >> 2) * kUnitPx;
-        ox_last = ((first + count - 1) >> 2) * kUnitPx + kUnitPx - 1;
+        g.oy_first = g.br * kUnitPx;
+        g.oy_last = g.oy_first + kUnitPx - 1;
+        g.ox_first = (g.first >> 2) * kUnitPx;
+        g.ox_last = ((g.first + g.count - 1) >> 2) * kUnitPx + kUnitPx - 1;
     } else {
-        const int mh = (first >> 1) & 1;
-        oy_first = (br * kMerge + mh) * kPatch;
-        oy_last = oy_first + kPatch - 1;
-        const int bc = first >> 2;
-        ox_first = (bc * kMerge + (first & 1)) * kPatch;
-        ox_last = (bc * kMerge + ((first + count - 1) & 1)) * kPatch + kPatch - 1;
+        const int mh = (g.first >> 1) & 1;
+        g.oy_first = (g.br * kMerge + mh) * kPatch;
+        g.oy_last = g.oy_first + kPatch - 1;
+        const int bc = g.first >> 2;
+        g.ox_first = (bc * kMerge + (g.first & 1)) * kPatch;
+        g.ox_last = (bc * kMerge + ((g.first + g.count - 1) & 1)) * kPatch + kPatch - 1;
     }
-    const int wave = threadIdx.x >> 6;
-    const int waves = blockDim.x >> 6;
 
     // Temporal slot tt of patch t shows frame min(2t + tt, frames - 1): an
     // odd frame count repeats its last frame, a still image is two copies of
     // its one frame.  Identical frames are computed once and stored to both
-    // slots (tt = -1); distinct frames take one pass per slot.
-    const int64_t frame_bytes = int64_t(d.src_h) * d.src_w * d.channels;
-    const int f0 = min(kTemporal * t, d.frames - 1);
-    const int f1 = min(kTemporal * t + 1, d.frames - 1);
-    const int passes = f0 == f1 ? 1 : 2;
-
-    if (d.flags & kFlagIdentity) {
-        const int64_t row_bytes = int64_t(d.src_w) * d.channels;
-        for (int fp = 0; fp < passes; ++fp) {
-            const int64_t frame_offset = d.src_offset + int64_t(fp == 0 ? f0 : f1) * frame_bytes;
-            const uint64_t first_byte = reinterpret_cast<uint64_t>(a.src) + uint64_t(frame_offset) +
-                                        uint64_t(int64_t(oy_first) * row_bytes +
-                                                 int64_t(ox_first) * d.channels);
-            const SourceWindow w = source_window(a, first_byte);
-            const int tt = passes == 1 ? -1 : fp;
-            for (int p = wave; p < count; p += waves) {
-                const int qr = first + p;  // row within the block row: (block col, mh, mw)
-                identity_patch<OutT>(a, d, w, row_bytes, oy_first, ox_first, t, tt, br, qr >> 2,
-                                     (qr >> 1) & 1, qr & 1, out, column);
-            }
-        }
+    // slots; distinct frames take one pass per slot.
+    if (!kClips) {
+        tile_pass<OutT, -1>(a, d, g, d.src_offset, out, column, band);
         return;
     }
-
-    // Source band touched by the tile: taps are monotone in the output
-    // index, so the first and last output rows/columns bound it.  The band
-    // runs one past the last first-tap so that the second tap is always
-    // i0 + 1; at the image edge that row/column repeats the last one.
-    const int r_lo = make_tap(d.scale_y, oy_first, d.src_h).i0;
-    const int r_end = make_tap(d.scale_y, oy_last, d.src_h).i0 + 1;
-    const int c_lo = make_tap(d.scale_x, ox_first, d.src_w).i0;
-    const int c_end = make_tap(d.scale_x, ox_last, d.src_w).i0 + 1;
-    const int rows = r_end - r_lo + 1;
-    const int groups = (c_end - c_lo + 4) >> 2;
-    const int pitch = 4 * groups;
-    const int64_t band_bytes = int64_t(rows) * d.src_w * d.channels;
-    const bool fits = int64_t(rows) * pitch <= a.band_capacity && band_bytes < 0x7FFF0000ll;
-
-    for (int fp = 0; fp < passes; ++fp) {
-        const int64_t frame_offset = d.src_offset + int64_t(fp == 0 ? f0 : f1) * frame_bytes;
-        const int tt = passes == 1 ? -1 : fp;
-        if (fits) {
-            if (fp > 0) __syncthreads();  // the previous frame's band is no longer read
-            stage_band(band, a, d, frame_offset, r_lo, c_lo, rows, groups, pitch);
-            __syncthreads();
-            if (c_end == d.src_w) {  // second tap at the right edge: repeat the last column
-                const int xl = d.src_w - 1 - c_lo;
-                for (int r = threadIdx.x; r < rows; r += blockDim.x)
-                    band[r * pitch + xl + 1] = band[r * pitch + xl];
-                __syncthreads();
-            }
-            const BandPixels px{band, pitch, r_lo, c_lo};
-            for (int p = wave; p < count; p += waves) {
-                const int qr = first + p;
-                bilinear_patch<OutT>(px, d, a, t, tt, br, qr >> 2, (qr >> 1) & 1, qr & 1, out, column);
-            }
-        } else {
-            const GlobalPixels px{a.src + frame_offset, int64_t(d.src_w) * d.channels, d.channels,
-                                  d.src_h, d.src_w};
-            for (int p = wave; p < count; p += waves) {
-                const int qr = first + p;
-                bilinear_patch<OutT>(px, d, a, t, tt, br, qr >> 2, (qr >> 1) & 1, qr & 1, out, column);
-            }
-        }
+    const int64_t frame_bytes = int64_t(d.src_h) * d.src_w * d.channels;
+    const int f0 = min(kTemporal * g.t, d.frames - 1);
+    const int f1 = min(kTemporal * g.t + 1, d.frames - 1);
+    const int64_t off0 = d.src_offset + int64_t(f0) * frame_bytes;
+    if (f0 == f1) {
+        tile_pass<OutT, -1>(a, d, g, off0, out, column, band);
+    } else {
+        tile_pass<OutT, 0>(a, d, g, off0, out, column, band);
+        __syncthreads();  // the first frame's band is no longer read
+        tile_pass<OutT, 1>(a, d, g, d.src_offset + int64_t(f1) * frame_bytes, out, column, band);
     }
 }
 
@@ -636,6 +667,9 @@ int hip_error(hipError_t e, const char *what) {
 #ifndef MIMO_ROWS_PER_TILE_DUAL
 #define MIMO_ROWS_PER_TILE_DUAL 1
 #endif
+#ifndef MIMO_ROWS_PER_TILE_CLIPS
+#define MIMO_ROWS_PER_TILE_CLIPS 12
+#endif
 #ifndef MIMO_XCD_ORDER
 #define MIMO_XCD_ORDER 1
 #endif
@@ -643,8 +677,13 @@ struct Tiling {
     int rows_per_tile = MIMO_ROWS_PER_TILE;
     int xcd_order = MIMO_XCD_ORDER;
     int passes = 1;
-    static Tiling choose(bool merge, bool column) {
+    // clips: the batch holds an item with two or more frames.  A clip tile
+    // stages and resamples its two frames one after the other; three merge
+    // units per tile amortise the two band loads and barriers better than
+    // one (measured on 64-frame 1280x720 clips, bf16: 0.62 vs 0.70 ms).
+    static Tiling choose(bool merge, bool column, bool clips) {
         Tiling t;
+        if (clips) t.rows_per_tile = MIMO_ROWS_PER_TILE_CLIPS;
         if (merge && column) {
             t.passes = 2;
             t.rows_per_tile = std::min(MIMO_ROWS_PER_TILE_DUAL, kRowsPerUnit);
@@ -671,6 +710,7 @@ struct BuiltTables {
     int64_t total_tiles = 0;
     int64_t total_rows = 0;
     int32_t band_capacity = 0;  // dwords
+    bool clips = false;         // some item has two or more frames
 };
 
 // Builds the workspace image: DevImage records, tile prefix, row prefix.
@@ -709,6 +749,7 @@ int build_tables(int32_t n, const mimo_image_desc *desc, const Tiling &tiling, B
         d.src_w = s.src_w;
         d.channels = s.channels;
         d.frames = s.frames;
+        out.clips = out.clips || s.frames > 1;
         d.blocks_h = s.dst_h / kUnitPx;
         d.blocks_w = s.dst_w / kUnitPx;
         d.scale_y = float(s.src_h) / float(s.dst_h);
@@ -781,7 +822,9 @@ int mimo_preprocess_batch(int32_t n, const mimo_image_desc *desc, const uint8_t 
         a.inv_std[c] = float(1.0 / double(std255[c]));
         a.mean[c] = mean255[c];
     }
-    const Tiling tiling = Tiling::choose(rows != nullptr, rows_col != nullptr);
+    bool clips = false;
+    for (int32_t i = 0; i < n; ++i) clips = clips || (desc[i].status == MIMO_OK && desc[i].frames > 1);
+    const Tiling tiling = Tiling::choose(rows != nullptr, rows_col != nullptr, clips);
     BuiltTables t;
     int st = build_tables(n, desc, tiling, t);
     if (st != MIMO_OK) return st;
@@ -820,10 +863,17 @@ int mimo_preprocess_batch(int32_t n, const mimo_image_desc *desc, const uint8_t 
     const dim3 grid{unsigned(t.total_tiles * tiling.passes), 1, 1},
         block{unsigned(tiling.threads()), 1, 1};
     e = timed_launch(s, [&] {
-        if (out_dtype == MIMO_F32)
-            hipLaunchKernelGGL(preprocess_kernel<float>, grid, block, lds, s, a);
-        else
-            hipLaunchKernelGGL(preprocess_kernel<uint16_t>, grid, block, lds, s, a);
+        if (out_dtype == MIMO_F32) {
+            if (t.clips)
+                hipLaunchKernelGGL((preprocess_kernel<float, true>), grid, block, lds, s, a);
+            else
+                hipLaunchKernelGGL((preprocess_kernel<float, false>), grid, block, lds, s, a);
+        } else {
+            if (t.clips)
+                hipLaunchKernelGGL((preprocess_kernel<uint16_t, true>), grid, block, lds, s, a);
+            else
+                hipLaunchKernelGGL((preprocess_kernel<uint16_t, false>), grid, block, lds, s, a);
+        }
     });
     if (e != hipSuccess) return hip_error(e, "preprocess_batch: kernel launch");
     g_dispatches.fetch_add(1);
