@@ -103,6 +103,16 @@ def _load():
         lib.oracle_preprocess_video.argtypes = [p, i64, i64, i64, i64, i64, i64, i64, i64, i64,
                                                 p, p, p]
         lib.oracle_preprocess_video.restype = ctypes.c_int
+        lib.oracle_rotary_positions.argtypes = [i64, i64, i64, i64, ctypes.c_int, p]
+        lib.oracle_rotary_positions.restype = ctypes.c_int
+        lib.oracle_rope_inv_freq.argtypes = [i64, ctypes.c_double, p]
+        lib.oracle_rope_inv_freq.restype = ctypes.c_int
+        lib.oracle_rope_tables.argtypes = [p, i64, i64, p, p, p, p]
+        lib.oracle_rope_tables.restype = ctypes.c_int
+        lib.oracle_window_index.argtypes = [i64, p, i64, ctypes.c_int, p]
+        lib.oracle_window_index.restype = ctypes.c_int
+        lib.oracle_chunk_seqlens.argtypes = [i64, p, p]
+        lib.oracle_chunk_seqlens.restype = i64
         _lib = lib
         return lib
 
@@ -292,3 +302,69 @@ def preprocess_video(frames: np.ndarray, out_h: int, out_w: int, mean255, std255
     if st != OK:
         raise OracleError(st, "preprocess_video")
     return out
+
+
+# ------------------------------------------------------- ViT index tables
+ROPE_THETA = 10000.0
+
+
+def rotary_positions(grid_t: int, grid_h: int, grid_w: int, column: bool = False,
+                     merge: int = MERGE) -> np.ndarray:
+    """vision page, MiMoVisionTransformer._rotary_positions: int32 [rows, 2]
+    (h, w) patch coordinates of every row, in merge-block order or, with
+    column=True, in column order."""
+    rows = grid_t * grid_h * grid_w
+    pos = np.empty((rows, 2), dtype=np.int32)
+    st = _load().oracle_rotary_positions(grid_t, grid_h, grid_w, merge, int(bool(column)), _ptr(pos))
+    if st != OK:
+        raise OracleError(st, "rotary_positions")
+    return pos
+
+
+def rope_inv_freq(dim: int, theta: float = ROPE_THETA) -> np.ndarray:
+    """vision page, MiMoVisionRotaryEmbedding(dim, theta) inv_freq: float32 [dim/2]."""
+    inv = np.empty(dim // 2, dtype=np.float32)
+    st = _load().oracle_rope_inv_freq(dim, float(theta), _ptr(inv))
+    if st != OK:
+        raise OracleError(st, "rope_inv_freq")
+    return inv
+
+
+def rope_tables(pos: np.ndarray, dim: int, theta: float = ROPE_THETA):
+    """Rotary angles (float32 [rows, dim]: h half, then w half) and their
+    cosine and sine in float64, for int32 [rows, 2] positions."""
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    rows = pos.shape[0]
+    inv = rope_inv_freq(dim, theta)
+    angle = np.empty((rows, dim), dtype=np.float32)
+    c = np.empty((rows, dim), dtype=np.float64)
+    s = np.empty((rows, dim), dtype=np.float64)
+    st = _load().oracle_rope_tables(_ptr(pos), rows, dim, _ptr(inv), _ptr(angle), _ptr(c), _ptr(s))
+    if st != OK:
+        raise OracleError(st, "rope_tables")
+    return angle, c, s
+
+
+def window_index(grid_thw, column_major: bool, merge: int = MERGE) -> np.ndarray:
+    """vision page, MiMoVisionTransformer._get_window_index(grid_thw,
+    column_major): int64 [units], index[dst] = src over the batch's merge
+    units."""
+    thw = np.ascontiguousarray(np.asarray(grid_thw, dtype=np.int64).reshape(-1, 3))
+    units = int(sum(t * (h // merge) * (w // merge) for t, h, w in thw))
+    index = np.empty(max(units, 1), dtype=np.int64)
+    st = _load().oracle_window_index(thw.shape[0], _ptr(thw), merge, int(bool(column_major)),
+                                      _ptr(index))
+    if st != OK:
+        raise OracleError(st, "window_index")
+    return index[:units]
+
+
+def chunk_seqlens(grid_thw) -> np.ndarray:
+    """Cumulative rows per attention chunk (one chunk per temporal slice of
+    every item): int64 [chunks + 1]."""
+    thw = np.ascontiguousarray(np.asarray(grid_thw, dtype=np.int64).reshape(-1, 3))
+    cu = np.empty(int(thw[:, 0].sum()) + 1 if thw.size else 1, dtype=np.int64)
+    k = _load().oracle_chunk_seqlens(thw.shape[0], _ptr(thw), _ptr(cu))
+    if k < 0:
+        raise OracleError(int(k), "chunk_seqlens")
+    return cu[:k + 1]

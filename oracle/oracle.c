@@ -13,7 +13,11 @@
  *     (module docstring; MimoV2ImageProcessor class docstring and defaults;
  *      smart_resize; _to_rgb; get_number_of_image_patches),
  *   - docs.rs "cortiq_engine::mimo_vision" (module conventions list;
- *      resize_bilinear; column_permutation; smart_resize).
+ *      resize_bilinear; column_permutation; smart_resize; the video helpers
+ *      prepare_video_frames, smart_nframes, sample_frames, video_max_pixels),
+ *   - NeMo Automodel "nemo_automodel.components.models.mimo_v2_flash.vision"
+ *     (MiMoVisionRotaryEmbedding; MiMoVisionTransformer._rotary_positions,
+ *      _get_window_index, _apply_merge_index) for the ViT index tables.
  *
  * Precision: the pages fix the resize as torch F.interpolate(bilinear,
  * align_corners=False) on a float32 tensor of 0-255 values, so the resize and
@@ -28,7 +32,10 @@
  * 65,536 (value, alpha) pairs; resize against torch CPU F.interpolate and
  * against a float64 evaluation within a derived bound; layout against a
  * coded image and a tensor reshape formulation; permutation against brute
- * force; bf16 rounding against torch.  No function here is "parity unpinned".
+ * force; bf16 rounding against torch; video helpers against numpy linspace
+ * and hand-derived cases, frames against a torch composition; ViT tables
+ * against reshapes, brute-force sorts, a coded image and torch's float32
+ * inv_freq / outer product.  No function here is "parity unpinned".
  */
 #include <math.h>
 #include <stdint.h>
@@ -584,4 +591,165 @@ int oracle_preprocess_video(const uint8_t *frames, int64_t n_frames, int64_t H, 
     free(planar);
     free(resized);
     return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* ViT index tables (NeMo Automodel "...mimo_v2_flash.vision":               */
+/* MiMoVisionTransformer._rotary_positions, _get_window_index,               */
+/* _apply_merge_index, MiMoVisionRotaryEmbedding; docs.rs                    */
+/* "cortiq_engine::mimo_vision" module conventions on window blocks).        */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Rotary patch coordinates of every row of one item.  Rows are listed in
+ * merge-block order (t, block row, block col, mh, mw), and the row's patch
+ * sits at grid row h = block row * merge + mh and grid column
+ * w = block col * merge + mw, whatever t.  In column order (column != 0)
+ * the same coordinates follow the rows: pos_col[dst] = pos[perm[dst]] with
+ * perm the column permutation.  pos[2r] = h, pos[2r + 1] = w.
+ */
+int oracle_rotary_positions(int64_t grid_t, int64_t grid_h, int64_t grid_w, int64_t merge,
+                            int column, int32_t *pos)
+{
+    if (grid_t < 1 || grid_h < 1 || grid_w < 1 || merge < 1 ||
+        grid_h % merge != 0 || grid_w % merge != 0)
+        return ORC_E_INVALID;
+    int64_t rows = grid_t * grid_h * grid_w;
+    int32_t *merge_order = malloc((size_t)rows * 2 * sizeof(int32_t));
+    if (!merge_order)
+        return ORC_E_NOMEM;
+    int64_t bh = grid_h / merge, bw = grid_w / merge, r = 0;
+    for (int64_t t = 0; t < grid_t; ++t)
+        for (int64_t br = 0; br < bh; ++br)
+            for (int64_t bc = 0; bc < bw; ++bc)
+                for (int64_t mh = 0; mh < merge; ++mh)
+                    for (int64_t mw = 0; mw < merge; ++mw) {
+                        merge_order[2 * r] = (int32_t)(br * merge + mh);
+                        merge_order[2 * r + 1] = (int32_t)(bc * merge + mw);
+                        ++r;
+                    }
+    if (!column) {
+        memcpy(pos, merge_order, (size_t)rows * 2 * sizeof(int32_t));
+        free(merge_order);
+        return ORC_OK;
+    }
+    int64_t *perm = malloc((size_t)rows * sizeof(int64_t));
+    if (!perm) {
+        free(merge_order);
+        return ORC_E_NOMEM;
+    }
+    int st = oracle_column_permutation(grid_t, grid_h, grid_w, merge, perm);
+    if (st == ORC_OK)
+        for (int64_t dst = 0; dst < rows; ++dst) {
+            pos[2 * dst] = merge_order[2 * perm[dst]];
+            pos[2 * dst + 1] = merge_order[2 * perm[dst] + 1];
+        }
+    free(perm);
+    free(merge_order);
+    return st;
+}
+
+/*
+ * inv_freq of MiMoVisionRotaryEmbedding(dim, theta): dim / 2 entries
+ * theta^-(2i / dim), as a float32 module evaluates them: the exponent
+ * 2i / dim in float32, the power rounded to float32, then its reciprocal
+ * rounded to float32.  The power is evaluated in float64, whose error is far
+ * below half a float32 ulp, so it is the correctly rounded float32 power.
+ */
+int oracle_rope_inv_freq(int64_t dim, double theta, float *inv)
+{
+    if (dim < 2 || dim % 2 != 0 || !(theta > 1.0))
+        return ORC_E_INVALID;
+    for (int64_t i = 0; i < dim / 2; ++i) {
+        float e = (float)(2 * i) / (float)dim;
+        float p = (float)pow(theta, (double)e);
+        inv[i] = 1.0f / p;
+    }
+    return ORC_OK;
+}
+
+/*
+ * Rotary angles of every row and their cosine and sine: a row whose patch
+ * sits at (h, w) gets, for k < dim / 2, the angle float32(h * inv[k]) in
+ * column k and float32(w * inv[k]) in column dim / 2 + k (h half first,
+ * then w half), the float32 outer product of positions and inv_freq.
+ * cos and sin are taken in float64 of that float32 angle.
+ */
+int oracle_rope_tables(const int32_t *pos, int64_t rows, int64_t dim, const float *inv,
+                       float *angle, double *cos_out, double *sin_out)
+{
+    if (rows < 0 || dim < 2 || dim % 2 != 0)
+        return ORC_E_INVALID;
+    int64_t half = dim / 2;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t axis = 0; axis < 2; ++axis) {
+            float p = (float)pos[2 * r + axis];
+            for (int64_t k = 0; k < half; ++k) {
+                float a = p * inv[k];
+                int64_t col = r * dim + axis * half + k;
+                angle[col] = a;
+                cos_out[col] = cos((double)a);
+                sin_out[col] = sin((double)a);
+            }
+        }
+    return ORC_OK;
+}
+
+/*
+ * Merge-unit index of a batch for the windowed blocks: index[dst] = src over
+ * the batch's merge units, numbered globally with the items back to back in
+ * batch order and each item's units in merge-block order.  column_major = 0
+ * keeps that order (the identity); column_major = 1 lists, within each item
+ * and each temporal slice, the units by (block col, block row).  thw holds
+ * (grid_t, grid_h, grid_w) per item.
+ */
+int oracle_window_index(int64_t n, const int64_t *thw, int64_t merge, int column_major,
+                        int64_t *index)
+{
+    if (n < 0 || merge < 1)
+        return ORC_E_INVALID;
+    int64_t base = 0, dst = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t gt = thw[3 * i], gh = thw[3 * i + 1], gw = thw[3 * i + 2];
+        if (gt < 1 || gh < 1 || gw < 1 || gh % merge != 0 || gw % merge != 0)
+            return ORC_E_INVALID;
+        int64_t bh = gh / merge, bw = gw / merge;
+        for (int64_t t = 0; t < gt; ++t) {
+            if (column_major) {
+                for (int64_t bc = 0; bc < bw; ++bc)
+                    for (int64_t br = 0; br < bh; ++br)
+                        index[dst++] = base + (t * bh + br) * bw + bc;
+            } else {
+                for (int64_t br = 0; br < bh; ++br)
+                    for (int64_t bc = 0; bc < bw; ++bc)
+                        index[dst++] = base + (t * bh + br) * bw + bc;
+            }
+        }
+        base += gt * bh * bw;
+    }
+    return ORC_OK;
+}
+
+/*
+ * Attention chunks of a batch: every temporal slice of every item is its
+ * own chunk of grid_h * grid_w rows (frames are independent chunks).
+ * cu[0] = 0 and cu[k + 1] = cu[k] + rows of chunk k.  Returns the number of
+ * chunks; cu must hold sum(grid_t) + 1 entries.
+ */
+int64_t oracle_chunk_seqlens(int64_t n, const int64_t *thw, int64_t *cu)
+{
+    if (n < 0)
+        return ORC_E_INVALID;
+    int64_t k = 0;
+    cu[0] = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t gt = thw[3 * i], gh = thw[3 * i + 1], gw = thw[3 * i + 2];
+        if (gt < 1 || gh < 1 || gw < 1)
+            return ORC_E_INVALID;
+        for (int64_t t = 0; t < gt; ++t) {
+            cu[k + 1] = cu[k] + gh * gw;
+            ++k;
+        }
+    }
+    return k;
 }
