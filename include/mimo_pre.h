@@ -232,14 +232,92 @@ int mimo_column_permute(int32_t n, const mimo_image_desc *desc, const void *rows
                         void *rows_out, int32_t out_dtype, int64_t capacity_rows,
                         void *workspace, size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * ViT index tables.  NeMo Automodel "mimo_v2_flash.vision":
+ * MiMoVisionRotaryEmbedding(dim, theta = 10000) with dim = head_dim / 2,
+ * MiMoVisionTransformer._rotary_positions, _get_window_index(grid_thw,
+ * column_major) and _apply_merge_index; docs.rs "cortiq_engine::mimo_vision"
+ * module conventions: type-1 window blocks run in column order, the RoPE
+ * tables are permuted the same way as the rows, and frames are independent
+ * chunks.  They describe the rows mimo_preprocess_batch emits, in either
+ * order, so a consumer can run rotary attention on them directly.
+ * ------------------------------------------------------------------------ */
+
+#define MIMO_ORDER_MERGE 0   /* rows in merge-block order (t, block row, block col, mh, mw) */
+#define MIMO_ORDER_COLUMN 1  /* rows in column order (t, block col, block row, mh, mw) */
+#define MIMO_ROPE_DIM_MAX 256
+
+/*
+ * inv_freq of MiMoVisionRotaryEmbedding(rope_dim, theta): rope_dim / 2
+ * floats theta^-(2i / rope_dim), evaluated as a float32 module does (float32
+ * exponent, power rounded to float32, reciprocal rounded to float32).
+ *   inv  host [rope_dim / 2].
+ * Returns MIMO_OK, or MIMO_E_INVALID unless rope_dim is even, in [2,
+ * MIMO_ROPE_DIM_MAX], and theta > 1.
+ */
+int mimo_rope_inv_freq(int32_t rope_dim, double theta, float *inv);
+
+/*
+ * Rotary tables of every row of a planned batch, in the order the rows are
+ * emitted (one kernel launch, after one table upload).  Row r of item i
+ * (global index row_offset_i + r) covers the patch at grid position (h, w):
+ * h = 2 * block row + mh, w = 2 * block col + mw of that row, whatever t.
+ *   n, desc    host plan (mimo_plan_geometry / mimo_plan_frames); items with
+ *              a non-zero status are skipped.
+ *   order      MIMO_ORDER_MERGE or MIMO_ORDER_COLUMN.
+ *   rope_dim   table width: a multiple of 8 in [8, MIMO_ROPE_DIM_MAX]
+ *              (head_dim / 2 of the tower; 32 for head_dim 64).
+ *   theta      rotary base (10000 in the tower).
+ *   pos_hw     device int32 [rows][2] (h, w), or NULL.
+ *   rope_cos, rope_sin  device float32 [rows][rope_dim], or NULL: column k <
+ *              rope_dim / 2 holds cos / sin of float32(h * inv_freq[k]),
+ *              column rope_dim / 2 + k the same for w (the h half, then the w
+ *              half, as the positions index the frequency table).  16-byte
+ *              aligned.
+ *   capacity_rows  rows the outputs hold (>= the plan's total).
+ *   workspace  device, >= mimo_workspace_bytes(n), 16-byte aligned.
+ * At least one output must be given.  Returns MIMO_OK, MIMO_E_INVALID,
+ * MIMO_E_CAPACITY or MIMO_E_HIP.
+ */
+int mimo_rotary_tables(int32_t n, const mimo_image_desc *desc, int32_t order, int32_t rope_dim,
+                       double theta, int32_t *pos_hw, float *rope_cos, float *rope_sin,
+                       int64_t capacity_rows, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/*
+ * Merge-unit index of a planned batch for the windowed blocks
+ * (_get_window_index): units are the 4-row groups of the merge-order rows,
+ * numbered globally (unit u = rows 4u .. 4u + 3).  index[dst] = src: with
+ * column_major = 0 the identity; with column_major = 1, within each item and
+ * temporal slice, units listed by (block col, block row) -- the unit-level
+ * form of mimo_column_permutation.  inverse[src] = dst undoes it.
+ * Applying it (_apply_merge_index) is a gather of whole units.
+ *   index, inverse  device int64 [units], either may be NULL (not both).
+ *   capacity_units  entries the outputs hold (>= total rows / 4).
+ *   workspace  device, >= mimo_workspace_bytes(n), 16-byte aligned.
+ * Returns MIMO_OK, MIMO_E_INVALID, MIMO_E_CAPACITY or MIMO_E_HIP.
+ */
+int mimo_window_index(int32_t n, const mimo_image_desc *desc, int32_t column_major,
+                      int64_t *index, int64_t *inverse, int64_t capacity_units, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/*
+ * Attention chunk boundaries (host): every temporal slice of every item is
+ * its own chunk of grid_h * grid_w rows.  cu[0] = 0, cu[k + 1] = cu[k] +
+ * rows of chunk k, over the items with status MIMO_OK in batch order.
+ *   cu  host int32 [capacity]; needs sum(grid_t) + 1 entries.
+ * Returns the number of chunks, MIMO_E_INVALID, MIMO_E_CAPACITY, or
+ * MIMO_E_TOO_LARGE if a boundary exceeds 2^31 - 1.
+ */
+int64_t mimo_chunk_seqlens(int32_t n, const mimo_image_desc *desc, int32_t *cu, int64_t capacity);
+
 /*
  * Instrumentation.  When start and stop are non-null hipEvent_t handles
- * (passed as void*), every later kernel launch that mimo_preprocess_batch or
- * mimo_column_permute makes on the calling thread records `start` on the
- * launch stream immediately before the kernel and `stop` immediately after
- * it, so the pair times the kernel alone (the descriptor upload falls
- * outside).  NULL, NULL switches it off.  Thread-local; the caller owns the
- * events.  Returns MIMO_OK, or MIMO_E_INVALID if only one is null.
+ * (passed as void*), every later kernel launch that the library makes on the
+ * calling thread records `start` on the launch stream immediately before
+ * the kernel and `stop` immediately after it, so the pair times the kernel
+ * alone (the descriptor upload falls outside).  NULL, NULL switches it off.
+ * Thread-local; the caller owns the events.  Returns MIMO_OK, or MIMO_E_INVALID if only one is null.
  */
 int mimo_set_launch_events(void *start, void *stop);
 

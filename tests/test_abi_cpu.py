@@ -214,3 +214,49 @@ def test_plan_frames_rejects_bad_frame_counts():
     desc, _, _, code = V.plan_frames([(0, 64, 64, 3), (2, 64, 64, 3), (-3, 64, 64, 3)], check=False)
     assert list(desc["status"]) == [V.MIMO_E_INVALID, 0, V.MIMO_E_INVALID]
     assert code == V.MIMO_E_INVALID
+
+
+@pytest.mark.parametrize("dim", [8, 16, 32, 40, 64, 128, 256])
+def test_rope_inv_freq_matches_oracle(dim):
+    for theta in (10000.0, 500.0, 1e6):
+        assert np.array_equal(V.rope_inv_freq(dim, theta), oracle.rope_inv_freq(dim, theta)), (dim, theta)
+    with pytest.raises(V.MimoError):
+        V.rope_inv_freq(7)
+
+
+def test_chunk_seqlens_match_oracle():
+    items = [(1, 200, 300, 3), (5, 64, 96, 3), (1, 1, 8193, 3), (4, 1080, 1920, 3), (3, 37, 29, 4)]
+    desc, _, _, _ = V.plan_frames(items, check=False)
+    ok = desc["status"] == 0
+    thw = np.stack([desc["grid_t"], desc["grid_h"], desc["grid_w"]], axis=1)[ok]
+    assert np.array_equal(V.chunk_seqlens(desc), oracle.chunk_seqlens(thw))
+    lib = V.load()
+    cu = np.empty(2, dtype=np.int32)
+    assert lib.mimo_chunk_seqlens(len(desc), desc.ctypes.data, cu.ctypes.data, 2) == V.MIMO_E_CAPACITY
+
+
+def test_vit_tables_argument_validation_without_gpu():
+    lib = V.load()
+    desc, _, _, _ = V.plan_geometry([(64, 64, 3)])
+    dummy = ctypes.c_void_p(0x1000)
+    # bad order, bad rope_dim, no outputs, misaligned table: all rejected before any GPU work
+    assert lib.mimo_rotary_tables(1, desc.ctypes.data, 2, 32, 1e4, dummy, None, None, 16, dummy,
+                                  4096, None) == V.MIMO_E_INVALID
+    assert lib.mimo_rotary_tables(1, desc.ctypes.data, 0, 12, 1e4, dummy, None, None, 16, dummy,
+                                  4096, None) == V.MIMO_E_INVALID
+    assert lib.mimo_rotary_tables(1, desc.ctypes.data, 0, 32, 1e4, None, None, None, 16, dummy,
+                                  4096, None) == V.MIMO_E_INVALID
+    assert lib.mimo_rotary_tables(1, desc.ctypes.data, 0, 32, 1e4, None, ctypes.c_void_p(0x1004),
+                                  None, 16, dummy, 4096, None) == V.MIMO_E_INVALID
+    # capacity below the plan's rows (16 rows for 64x64 -> 128x128... use a tiny capacity)
+    assert lib.mimo_rotary_tables(1, desc.ctypes.data, 0, 32, 1e4, dummy, None, None, 1, dummy,
+                                  4096, None) == V.MIMO_E_CAPACITY
+    assert lib.mimo_window_index(1, desc.ctypes.data, 1, None, None, 16, dummy, 4096,
+                                 None) == V.MIMO_E_INVALID
+    assert lib.mimo_window_index(1, desc.ctypes.data, 1, dummy, None, 1, dummy, 4096,
+                                 None) == V.MIMO_E_CAPACITY
+    assert lib.mimo_window_index(1, desc.ctypes.data, 1, dummy, None, 1 << 20, dummy, 8,
+                                 None) == V.MIMO_E_CAPACITY
+    # an empty batch is a no-op
+    assert lib.mimo_rotary_tables(0, None, 0, 32, 1e4, dummy, None, None, 0, None, 0,
+                                  None) == V.MIMO_OK

@@ -28,6 +28,10 @@ MIMO_F32 = 0
 MIMO_BF16 = 1
 
 ROW_LEN = 1536  # 3 channels x 2 frames x 16 x 16
+MIMO_ORDER_MERGE = 0
+MIMO_ORDER_COLUMN = 1
+MIMO_ROPE_DIM_MAX = 256
+ROPE_THETA = 10000.0
 
 # mimo_image_desc, 64 bytes (include/mimo_pre.h)
 IMAGE_DESC_DTYPE = np.dtype([
@@ -83,6 +87,11 @@ SIGNATURES = {
     "mimo_last_error": ([], ctypes.c_char_p),
     "mimo_dispatch_count": ([], _I64),
     "mimo_set_launch_events": ([_P, _P], ctypes.c_int),
+    "mimo_rope_inv_freq": ([_I32, ctypes.c_double, _P], ctypes.c_int),
+    "mimo_rotary_tables": ([_I32, _P, _I32, _I32, ctypes.c_double, _P, _P, _P, _I64, _P, _SZ, _P],
+                           ctypes.c_int),
+    "mimo_window_index": ([_I32, _P, _I32, _P, _P, _I64, _P, _SZ, _P], ctypes.c_int),
+    "mimo_chunk_seqlens": ([_I32, _P, _P, _I64], _I64),
 }
 
 _lock = threading.Lock()
@@ -306,3 +315,56 @@ def column_permute(desc: np.ndarray, rows_in, rows_out, workspace, stream=None):
                                       code_dtype, cap, workspace.data_ptr(), workspace.numel(),
                                       _stream_handle(stream, rows_in.device))
     _check(code, "column_permute")
+
+
+def rope_inv_freq(rope_dim: int, theta: float = ROPE_THETA) -> np.ndarray:
+    """mimo_rope_inv_freq: float32 [rope_dim / 2]."""
+    inv = np.empty(max(int(rope_dim) // 2, 1), dtype=np.float32)
+    _check(load().mimo_rope_inv_freq(int(rope_dim), float(theta), inv.ctypes.data), "rope_inv_freq")
+    return inv[:int(rope_dim) // 2]
+
+
+def rotary_tables(desc: np.ndarray, workspace, pos=None, cos=None, sin=None, column=False,
+                  rope_dim: int = 32, theta: float = ROPE_THETA, stream=None):
+    """mimo_rotary_tables: fills the given device tensors (pos int32 [rows, 2],
+    cos / sin float32 [rows, rope_dim]) for the rows in merge-block order, or
+    column order with column=True."""
+    desc = np.ascontiguousarray(desc, dtype=IMAGE_DESC_DTYPE)
+    outs = [t for t in (pos, cos, sin) if t is not None]
+    cap = min(t.shape[0] for t in outs) if outs else 0
+    dev = outs[0].device if outs else workspace.device
+    code = load().mimo_rotary_tables(
+        desc.shape[0], desc.ctypes.data, MIMO_ORDER_COLUMN if column else MIMO_ORDER_MERGE,
+        int(rope_dim), float(theta),
+        pos.data_ptr() if pos is not None else None,
+        cos.data_ptr() if cos is not None else None,
+        sin.data_ptr() if sin is not None else None,
+        cap, workspace.data_ptr(), workspace.numel(), _stream_handle(stream, dev))
+    _check(code, "rotary_tables")
+
+
+def window_index(desc: np.ndarray, workspace, index=None, inverse=None, column_major=True,
+                 stream=None):
+    """mimo_window_index: fills int64 device tensors [units] (index[dst] = src,
+    inverse[src] = dst)."""
+    desc = np.ascontiguousarray(desc, dtype=IMAGE_DESC_DTYPE)
+    outs = [t for t in (index, inverse) if t is not None]
+    cap = min(t.shape[0] for t in outs) if outs else 0
+    dev = outs[0].device if outs else workspace.device
+    code = load().mimo_window_index(
+        desc.shape[0], desc.ctypes.data, int(bool(column_major)),
+        index.data_ptr() if index is not None else None,
+        inverse.data_ptr() if inverse is not None else None,
+        cap, workspace.data_ptr(), workspace.numel(), _stream_handle(stream, dev))
+    _check(code, "window_index")
+
+
+def chunk_seqlens(desc: np.ndarray) -> np.ndarray:
+    """mimo_chunk_seqlens: int32 [chunks + 1] cumulative rows per chunk."""
+    desc = np.ascontiguousarray(desc, dtype=IMAGE_DESC_DTYPE)
+    ok = desc["status"] == MIMO_OK
+    cu = np.empty(int(desc["grid_t"][ok].sum()) + 1, dtype=np.int32)
+    k = load().mimo_chunk_seqlens(desc.shape[0], desc.ctypes.data, cu.ctypes.data, cu.shape[0])
+    if k < 0:
+        _check(int(k), "chunk_seqlens")
+    return cu[:k + 1]

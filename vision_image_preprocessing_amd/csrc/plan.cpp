@@ -308,6 +308,43 @@ int mimo_column_permutation(int64_t grid_t, int64_t grid_h, int64_t grid_w, int6
     return MIMO_OK;
 }
 
+int mimo_rope_inv_freq(int32_t rope_dim, double theta, float *inv) {
+    clear_error();
+    if (rope_dim < 2 || rope_dim > MIMO_ROPE_DIM_MAX || rope_dim % 2 || !(theta > 1.0) || !inv)
+        return set_error(MIMO_E_INVALID, "rope_inv_freq: rope_dim must be even in [2, 256], theta > 1");
+    // theta ** (arange(0, dim, 2) / dim) and its reciprocal, each rounded to
+    // float32; the float64 power is within a tiny fraction of a float32 ulp.
+    for (int32_t i = 0; i < rope_dim / 2; ++i) {
+        const float exponent = float(2 * i) / float(rope_dim);
+        const float power = float(std::pow(theta, double(exponent)));
+        inv[i] = 1.0f / power;
+    }
+    return MIMO_OK;
+}
+
+int64_t mimo_chunk_seqlens(int32_t n, const mimo_image_desc *desc, int32_t *cu, int64_t capacity) {
+    clear_error();
+    if (n < 0 || (n > 0 && !desc) || !cu || capacity < 1)
+        return set_error(MIMO_E_INVALID, "chunk_seqlens: bad n or null pointer");
+    int64_t k = 0, acc = 0;
+    cu[0] = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        const mimo_image_desc &d = desc[i];
+        if (d.status != MIMO_OK || d.rows == 0) continue;
+        if (d.grid_t < 1 || d.grid_h < 1 || d.grid_w < 1)
+            return set_error(MIMO_E_INVALID, "chunk_seqlens: item " + std::to_string(i) + " has a bad grid");
+        for (int32_t t = 0; t < d.grid_t; ++t) {
+            if (k + 2 > capacity)
+                return set_error(MIMO_E_CAPACITY, "chunk_seqlens: cu holds fewer than sum(grid_t) + 1 entries");
+            acc += int64_t(d.grid_h) * d.grid_w;
+            if (acc > 0x7FFFFFFFll)
+                return set_error(MIMO_E_TOO_LARGE, "chunk_seqlens: a boundary exceeds 2^31 - 1");
+            cu[++k] = int32_t(acc);
+        }
+    }
+    return k;
+}
+
 const char *mimo_status_string(int status) {
     switch (status) {
         case MIMO_OK: return "ok";

@@ -46,13 +46,14 @@
 #include <string>
 #include <vector>
 
+#include "device_util.h"
 #include "internal.h"
+#include "runtime.h"
 
 namespace mimo {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
 // LDS budget for one tile's source band, in dwords (one dword per pixel).
 constexpr int kBandBudgetDwords = 12288;  // 48 KB
 // Buffer resource word 3 for raw (untyped) buffer loads on gfx9-family parts.
@@ -84,38 +85,6 @@ struct PermArgs {
 };
 
 // ---------------------------------------------------------------- helpers
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// Largest i in [0, n) with begin[i] <= key (begin non-decreasing,
-// begin[0] = 0 <= key).  Each round one wavefront compares 64 evenly spaced
-// entries and keeps the bracket that holds the key.  Result is wave-uniform.
-__device__ __forceinline__ int find_segment(const int64_t *__restrict__ begin, int n, int64_t key) {
-    const int lane = threadIdx.x & 63;
-    int lo = 0, hi = n;
-    while (hi - lo > 1) {
-        const int step = (hi - lo + 63) >> 6;
-        const int idx = lo + lane * step;
-        const bool le = idx < hi && begin[idx] <= key;
-        const uint64_t mask = __ballot(le);
-        const int k = __popcll(mask) - 1;
-        lo = lo + k * step;
-        hi = min(lo + step, hi);
-    }
-    return __builtin_amdgcn_readfirstlane(lo);
-}
-
-// n / d for 0 <= n < 2^24 and d >= 1, given inv = float(1 / d): the float
-// estimate is within one of the quotient and is corrected exactly.
-__device__ __forceinline__ int div_small(int n, int d, float inv) {
-    int q = int(float(n) * inv);
-    const int r = n - q * d;
-    q += (r >= d) - (r < 0);
-    return q;
-}
 
 struct Tap {
     int i0;
@@ -374,14 +343,6 @@ __device__ __forceinline__ void stage_band(uint32_t *band, const PreArgs &a, con
     }
 }
 
-// Tile order: workgroup b is dispatched to XCD b % 8; tile t = (b % 8) * per
-// + b / 8 gives each XCD one contiguous run of tiles (and so of output
-// rows), which keeps each XCD's write stream and its source reads local.
-__device__ __forceinline__ int64_t xcd_contiguous_tile(int64_t b, int64_t grid) {
-    const int64_t per = grid / kXcds;
-    return b < per * kXcds ? (b % kXcds) * per + b / kXcds : b;
-}
-
 // What one workgroup's tile covers: temporal patch t, block row br, rows
 // [first, first + count) of that block row (merge order) or of its column-
 // order unit, and the output pixel rectangle those rows cover.
@@ -573,89 +534,6 @@ __global__ __launch_bounds__(kThreads) void column_permute_kernel(PermArgs a) {
 
 // ------------------------------------------------------------- host side
 
-std::atomic<int64_t> g_dispatches{0};
-thread_local hipEvent_t g_launch_start = nullptr;
-thread_local hipEvent_t g_launch_stop = nullptr;
-
-// Records the caller's timing events around one kernel launch.
-template <typename Launch>
-hipError_t timed_launch(hipStream_t s, Launch &&launch) {
-    hipError_t e = hipSuccess;
-    if (g_launch_start && (e = hipEventRecord(g_launch_start, s)) != hipSuccess) return e;
-    launch();
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (g_launch_stop && (e = hipEventRecord(g_launch_stop, s)) != hipSuccess) return e;
-    return hipSuccess;
-}
-
-// Pinned host staging for the per-call descriptor tables: a small ring per
-// device, each slot fenced by an event so a slot is rewritten only after
-// its previous copy has executed.
-class TableStaging {
-  public:
-    struct Slot {
-        void *host = nullptr;
-        size_t cap = 0;
-        hipEvent_t done = nullptr;
-        bool pending = false;
-    };
-    static constexpr int kSlots = 8;
-
-    // Copies bytes from `table` to device `dst` on `stream`, asynchronously.
-    hipError_t upload(const void *table, size_t bytes, void *dst, hipStream_t stream) {
-        int dev = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e != hipSuccess) return e;
-        std::lock_guard<std::mutex> lock(mu_);
-        if (int(rings_.size()) <= dev) rings_.resize(dev + 1);
-        Ring &ring = rings_[dev];
-        Slot &s = ring.slots[ring.next];
-        ring.next = (ring.next + 1) % kSlots;
-        if (s.pending) {
-            e = hipEventSynchronize(s.done);
-            if (e != hipSuccess) return e;
-            s.pending = false;
-        }
-        if (!s.done) {
-            e = hipEventCreateWithFlags(&s.done, hipEventDisableTiming);
-            if (e != hipSuccess) return e;
-        }
-        if (s.cap < bytes) {
-            if (s.host) (void)hipHostFree(s.host);
-            s.host = nullptr;
-            s.cap = 0;
-            e = hipHostMalloc(&s.host, bytes, hipHostMallocDefault);
-            if (e != hipSuccess) return e;
-            s.cap = bytes;
-        }
-        std::memcpy(s.host, table, bytes);
-        e = hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, stream);
-        if (e != hipSuccess) return e;
-        e = hipEventRecord(s.done, stream);
-        if (e != hipSuccess) return e;
-        s.pending = true;
-        return hipSuccess;
-    }
-
-  private:
-    struct Ring {
-        Slot slots[kSlots];
-        int next = 0;
-    };
-    std::mutex mu_;
-    std::vector<Ring> rings_;
-};
-
-TableStaging &staging() {
-    static TableStaging *s = new TableStaging();  // lives until process exit
-    return *s;
-}
-
-int hip_error(hipError_t e, const char *what) {
-    return set_error(MIMO_E_HIP, std::string(what) + ": " + hipGetErrorName(e) + " (" +
-                                     hipGetErrorString(e) + ")");
-}
-
 // Tiling policy: rows per tile (1, 2 or a multiple of 4) and whether
 // workgroups are mapped to XCD-contiguous runs of tiles.  Small tiles keep
 // the output each workgroup writes small, which the HBM write path favours.
@@ -773,26 +651,11 @@ int build_tables(int32_t n, const mimo_image_desc *desc, const Tiling &tiling, B
     return MIMO_OK;
 }
 
-int check_ptr_align(const void *p, uintptr_t align) {
-    return (reinterpret_cast<uintptr_t>(p) & (align - 1)) == 0;
-}
-
 }  // namespace mimo
 
 using namespace mimo;
 
 extern "C" {
-
-int64_t mimo_dispatch_count(void) { return g_dispatches.load(); }
-
-int mimo_set_launch_events(void *start, void *stop) {
-    clear_error();
-    if ((start == nullptr) != (stop == nullptr))
-        return set_error(MIMO_E_INVALID, "set_launch_events: give both events or neither");
-    g_launch_start = static_cast<hipEvent_t>(start);
-    g_launch_stop = static_cast<hipEvent_t>(stop);
-    return MIMO_OK;
-}
 
 int mimo_preprocess_batch(int32_t n, const mimo_image_desc *desc, const uint8_t *src,
                           int64_t src_capacity, const float *mean255, const float *std255,
@@ -844,7 +707,7 @@ int mimo_preprocess_batch(int32_t n, const mimo_image_desc *desc, const uint8_t 
         return set_error(MIMO_E_TOO_LARGE, "preprocess_batch: more than 2^31-1 tiles");
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = staging().upload(t.bytes.data(), t.bytes.size(), workspace, s);
+    hipError_t e = upload_table(t.bytes.data(), t.bytes.size(), workspace, s);
     if (e != hipSuccess) return hip_error(e, "preprocess_batch: table upload");
 
     uint8_t *ws = static_cast<uint8_t *>(workspace);
@@ -908,7 +771,7 @@ int mimo_column_permute(int32_t n, const mimo_image_desc *desc, const void *rows
         return set_error(MIMO_E_TOO_LARGE, "column_permute: too many merge units");
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = staging().upload(t.bytes.data(), t.bytes.size(), workspace, s);
+    hipError_t e = upload_table(t.bytes.data(), t.bytes.size(), workspace, s);
     if (e != hipSuccess) return hip_error(e, "column_permute: table upload");
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     PermArgs a;

@@ -127,3 +127,38 @@ def preprocess(src_dev, plan: BatchPlan, mean=IMAGENET_MEAN, std=IMAGENET_STD,
         "pixel_values_col": rows_col if column_order else None,
         "image_grid_thw": torch.from_numpy(plan.image_grid_thw),
     }
+
+
+def vit_tables(plan: BatchPlan, device="cuda", column: bool = False, rope_dim: int = 32,
+               theta: float = _abi.ROPE_THETA, stream=None, workspace=None):
+    """The ViT index tables of a planned batch (vision page,
+    MiMoVisionTransformer._rotary_positions / _get_window_index; cortiq
+    module conventions), for rows in merge-block order or, with column=True,
+    column order:
+
+    ``rotary_pos`` int32 [rows, 2] (h, w); ``rope_cos`` / ``rope_sin``
+    float32 [rows, rope_dim] (h half, then w half); ``window_index`` /
+    ``window_inverse`` int64 [rows / 4] (the identity for merge-block order);
+    ``cu_seqlens`` int32 [chunks + 1] (one chunk per temporal slice).
+    """
+    import torch
+    n_rows = max(plan.total_rows, 1)
+    units = max(plan.total_rows // 4, 1)
+    if workspace is None:
+        workspace = torch.empty(max(_abi.workspace_bytes(len(plan)), 16), dtype=torch.uint8,
+                                device=device)
+    pos = torch.empty((n_rows, 2), dtype=torch.int32, device=device)
+    cos = torch.empty((n_rows, rope_dim), dtype=torch.float32, device=device)
+    sin = torch.empty((n_rows, rope_dim), dtype=torch.float32, device=device)
+    index = torch.empty(units, dtype=torch.int64, device=device)
+    inverse = torch.empty(units, dtype=torch.int64, device=device)
+    _abi.rotary_tables(plan.desc, workspace, pos=pos, cos=cos, sin=sin, column=column,
+                       rope_dim=rope_dim, theta=theta, stream=stream)
+    _abi.window_index(plan.desc, workspace, index=index, inverse=inverse, column_major=column,
+                      stream=stream)
+    rows = plan.total_rows
+    return {
+        "rotary_pos": pos[:rows], "rope_cos": cos[:rows], "rope_sin": sin[:rows],
+        "window_index": index[:rows // 4], "window_inverse": inverse[:rows // 4],
+        "cu_seqlens": torch.from_numpy(_abi.chunk_seqlens(plan.desc)),
+    }
