@@ -94,6 +94,55 @@ def cpu_baseline(batch, plan, sample: int, threads: int) -> dict:
             "seconds": dt, "cpu_model": platform.processor() or platform.machine()}
 
 
+def time_launches(V, fn, reps: int, stream):
+    """Mean kernel time (ms) of `reps` calls of fn, each launch bracketed by
+    the library's launch events."""
+    import numpy as np
+    import torch
+
+    fn()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    for ev in starts + ends:
+        ev.record(stream)
+    torch.cuda.synchronize()
+    for i in range(reps):
+        V.set_launch_events(starts[i], ends[i])
+        fn()
+    V.set_launch_events(None, None)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)]))
+
+
+def vit_tables_rates(V, plan, ws, reps: int, rope_dim: int = 32) -> dict:
+    """The ViT index-table kernels on the same batch, rows in column order:
+    algorithmic bytes are what they write (int32 (h, w) + float32 cos and sin
+    per row; int64 index and inverse per merge unit)."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    rows, units = plan.total_rows, plan.total_rows // 4
+    pos = torch.empty((rows, 2), dtype=torch.int32, device="cuda")
+    cos = torch.empty((rows, rope_dim), dtype=torch.float32, device="cuda")
+    sin = torch.empty_like(cos)
+    idx = torch.empty(units, dtype=torch.int64, device="cuda")
+    inv = torch.empty_like(idx)
+    out = {}
+    ms = time_launches(V, lambda: V.rotary_tables(plan.desc, ws, pos=pos, cos=cos, sin=sin,
+                                                   column=True, rope_dim=rope_dim), reps, stream)
+    b = rows * (8 + 2 * 4 * rope_dim)
+    out["rotary_tables_kernel"] = {"rows": rows, "rope_dim": rope_dim, "bytes": b, "ms": ms,
+                                   "GB/s": b / (ms * 1e-3) / 1e9,
+                                   "frac": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+    ms = time_launches(V, lambda: V.window_index(plan.desc, ws, index=idx, inverse=inv,
+                                                  column_major=True), reps, stream)
+    b = units * 16
+    out["window_index_kernel"] = {"units": units, "bytes": b, "ms": ms,
+                                  "GB/s": b / (ms * 1e-3) / 1e9,
+                                  "frac": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+    return out
+
+
 def calibrate_copy(gib: float, reps: int):
     """A plain elementwise copy kernel of known size (read N bytes, write N
     bytes) for scaling the HBM byte counters."""
@@ -126,6 +175,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=512)
     ap.add_argument("--gather", action="store_true",
                     help="also time the standalone column_permute gather kernel")
+    ap.add_argument("--no-vit-tables", action="store_true",
+                    help="skip timing the ViT index-table kernels on the same batch")
     ap.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GIB",
                     help="only run a plain copy kernel of this size (counter calibration)")
     args = ap.parse_args()
@@ -262,6 +313,10 @@ def main():
         gb = 2 * plan.total_rows * 1536 * bpv / (ms * 1e-3) / 1e9
         result["column_permute_gather"] = {"ms": ms, "GB/s": gb, "frac": gb / HBM_PEAK_GBPS}
         del gathered
+
+    if not args.no_vit_tables:
+        log("vit tables")
+        result["vit_tables"] = vit_tables_rates(V, plan, ws, reps=10)
 
     if not args.no_cpu_baseline:
         threads = max(1, min(16, os.cpu_count() or 1))
