@@ -160,8 +160,8 @@ int64_t mimo_video_max_pixels(int64_t n_sampled, int64_t total_max, const mimo_p
 
 /*
  * cortiq smart_nframes: frame count for `total` source frames at fps_src
- * sampled at fps: total / fps_src * fps, clamped to [min_frames,
- * max_frames], then to at most total, floored to an even count.  Returns the
+ * sampled at fps: total / fps_src * fps, held inside [min_frames,
+ * max_frames], then capped at total, then rounded down to an even count.  Returns the
  * count, or MIMO_E_INVALID.
  */
 int64_t mimo_smart_nframes(int64_t total, double fps_src, double fps, int64_t min_frames,
@@ -238,8 +238,8 @@ int mimo_column_permute(int32_t n, const mimo_image_desc *desc, const void *rows
  * MiMoVisionTransformer._rotary_positions, _get_window_index(grid_thw,
  * column_major) and _apply_merge_index; docs.rs "cortiq_engine::mimo_vision"
  * module conventions: type-1 window blocks run in column order, the RoPE
- * tables are permuted the same way as the rows, and frames are independent
- * chunks.  They describe the rows mimo_preprocess_batch emits, in either
+ * tables follow the same permutation as the rows, and no two frames share a
+ * chunk.  They describe the rows mimo_preprocess_batch emits, in either
  * order, so a consumer can run rotary attention on them directly.
  * ------------------------------------------------------------------------ */
 

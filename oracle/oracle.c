@@ -471,7 +471,7 @@ int64_t oracle_video_max_pixels(int64_t n_sampled, int64_t total_max, int64_t te
 
 /*
  * Frame count for `total` source frames at `fps_src` sampled at `fps`:
- * total / fps_src * fps, clamped to [min_frames, max_frames], then to at
+ * total / fps_src * fps, held inside [min_frames, max_frames], then to at
  * most total, then floored to an even count.
  */
 int64_t oracle_smart_nframes(int64_t total, double fps_src, double fps, int64_t min_frames,
@@ -732,7 +732,7 @@ int oracle_window_index(int64_t n, const int64_t *thw, int64_t merge, int column
 
 /*
  * Attention chunks of a batch: every temporal slice of every item is its
- * own chunk of grid_h * grid_w rows (frames are independent chunks).
+ * own chunk of grid_h * grid_w rows (frames never share a chunk).
  * cu[0] = 0 and cu[k + 1] = cu[k] + rows of chunk k.  Returns the number of
  * chunks; cu must hold sum(grid_t) + 1 entries.
  */
