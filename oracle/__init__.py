@@ -113,6 +113,8 @@ def _load():
         lib.oracle_window_index.restype = ctypes.c_int
         lib.oracle_chunk_seqlens.argtypes = [i64, p, p]
         lib.oracle_chunk_seqlens.restype = i64
+        lib.oracle_patch_embed.argtypes = [p, i64, i64, p, i64, p, p]
+        lib.oracle_patch_embed.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -368,3 +370,22 @@ def chunk_seqlens(grid_thw) -> np.ndarray:
     if k < 0:
         raise OracleError(int(k), "chunk_seqlens")
     return cu[:k + 1]
+
+
+# ------------------------------------------------------------ patch embedding
+def patch_embed(rows: np.ndarray, w: np.ndarray, bias=None) -> np.ndarray:
+    """vision page, MiMoVisionPatchEmbed: the Conv3d (kernel = stride =
+    (T, P, P)) on rows [n, C*T*P*P] with weight [E, C, T, P, P] given
+    flattened [E, C*T*P*P]; float64 [n, E]."""
+    rows = np.ascontiguousarray(rows, dtype=np.float32)
+    w = np.ascontiguousarray(w, dtype=np.float32).reshape(w.shape[0], -1)
+    n, k = rows.shape
+    e = w.shape[0]
+    assert w.shape[1] == k
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    out = np.empty((n, e), dtype=np.float64)
+    st = _load().oracle_patch_embed(_ptr(rows), n, k, _ptr(w), e, _ptr(b) if b is not None else None,
+                                    _ptr(out))
+    if st != OK:
+        raise OracleError(st, "patch_embed")
+    return out

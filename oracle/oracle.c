@@ -753,3 +753,31 @@ int64_t oracle_chunk_seqlens(int64_t n, const int64_t *thw, int64_t *cu)
     }
     return k;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Patch embedding (NeMo Automodel "...mimo_v2_flash.vision":                */
+/* MiMoVisionPatchEmbed): a Conv3d whose kernel and stride are both          */
+/* (T, P, P), applied to rows that are exactly one kernel window each.       */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * out[r][e] = bias[e] + sum over k of rows[r][k] * w[e][k], where w is the
+ * Conv3d weight [embed_dim][C][T][P][P] flattened in the rows' own
+ * (c, tt, py, px) order, so the convolution at the one window position is
+ * this dot product.  Accumulated in float64 (the float inputs convert
+ * exactly).  bias may be NULL.
+ */
+int oracle_patch_embed(const float *rows, int64_t n_rows, int64_t row_len, const float *w,
+                       int64_t embed_dim, const float *bias, double *out)
+{
+    if (n_rows < 0 || row_len < 1 || embed_dim < 1)
+        return ORC_E_INVALID;
+    for (int64_t r = 0; r < n_rows; ++r)
+        for (int64_t e = 0; e < embed_dim; ++e) {
+            double acc = bias ? (double)bias[e] : 0.0;
+            for (int64_t k = 0; k < row_len; ++k)
+                acc += (double)rows[r * row_len + k] * (double)w[e * row_len + k];
+            out[r * embed_dim + e] = acc;
+        }
+    return ORC_OK;
+}
