@@ -311,6 +311,44 @@ int mimo_window_index(int32_t n, const mimo_image_desc *desc, int32_t column_maj
  */
 int64_t mimo_chunk_seqlens(int32_t n, const mimo_image_desc *desc, int32_t *cu, int64_t capacity);
 
+/* ------------------------------------------------------------------------
+ * Patch embedding.  NeMo Automodel "mimo_v2_flash.vision",
+ * MiMoVisionPatchEmbed: the rows' consumer, a Conv3d whose kernel and stride
+ * are both (T, P, P) = (2, 16, 16), so each row is one window and the
+ * convolution is out[r][e] = bias[e] + sum_k rows[r][k] * W[e][k] with the
+ * weight [E][3][2][16][16] flattened in the rows' (c, tt, py, px) order.
+ * Runs on the matrix cores in bf16 with float32 accumulation.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Folded weight for rows whose two temporal slots are equal (still images):
+ * w_folded[e][c][p] = bf16(W[e][c][0][p] + W[e][c][1][p]) (sum in float32,
+ * one rounding to nearest even), so the embedding needs K = 768 instead of
+ * 1536 (mimo_patch_embed with folded = 1).
+ *   w         device bf16 [embed_dim][1536], 16-byte aligned.
+ *   w_folded  device bf16 [embed_dim][768], 16-byte aligned, not w.
+ * One kernel launch.  Returns MIMO_OK, MIMO_E_INVALID or MIMO_E_HIP.
+ */
+int mimo_fold_patch_weights(int32_t embed_dim, const void *w, void *w_folded, void *stream);
+
+/*
+ * out = rows * W^T (+ bias) for n_rows rows, one kernel launch.
+ *   rows       device bf16 [n_rows][1536] (mimo_preprocess_batch output with
+ *              MIMO_BF16, either row order), 16-byte aligned.
+ *   embed_dim  E: a multiple of 128 in [128, 65536].
+ *   w          device bf16 [E][1536] (folded = 0), or the folded weight
+ *              [E][768] (folded = 1: only the tt = 0 half of every row is
+ *              read, which is exact only for rows whose two frames are
+ *              equal), 16-byte aligned.
+ *   bias       device float32 [E], or NULL.
+ *   out        device [n_rows][E] of out_dtype (MIMO_F32 or MIMO_BF16,
+ *              rounded to nearest even), 16-byte aligned.
+ * Returns MIMO_OK, MIMO_E_INVALID, MIMO_E_TOO_LARGE or MIMO_E_HIP.
+ */
+int mimo_patch_embed(int64_t n_rows, const void *rows, int32_t embed_dim, const void *w,
+                     int32_t folded, const float *bias, int32_t out_dtype, void *out,
+                     void *stream);
+
 /*
  * Instrumentation.  When start and stop are non-null hipEvent_t handles
  * (passed as void*), every later kernel launch that the library makes on the

@@ -92,6 +92,8 @@ SIGNATURES = {
                            ctypes.c_int),
     "mimo_window_index": ([_I32, _P, _I32, _P, _P, _I64, _P, _SZ, _P], ctypes.c_int),
     "mimo_chunk_seqlens": ([_I32, _P, _P, _I64], _I64),
+    "mimo_fold_patch_weights": ([_I32, _P, _P, _P], ctypes.c_int),
+    "mimo_patch_embed": ([_I64, _P, _I32, _P, _I32, _P, _I32, _P, _P], ctypes.c_int),
 }
 
 _lock = threading.Lock()
@@ -368,3 +370,31 @@ def chunk_seqlens(desc: np.ndarray) -> np.ndarray:
     if k < 0:
         _check(int(k), "chunk_seqlens")
     return cu[:k + 1]
+
+
+def fold_patch_weights(w, w_folded=None, stream=None):
+    """mimo_fold_patch_weights: bf16 [E, 1536] -> bf16 [E, 768] (device tensors)."""
+    import torch
+    e = w.shape[0]
+    if w_folded is None:
+        w_folded = torch.empty((e, ROW_LEN // 2), dtype=torch.bfloat16, device=w.device)
+    _check(load().mimo_fold_patch_weights(e, w.data_ptr(), w_folded.data_ptr(),
+                                          _stream_handle(stream, w.device)), "fold_patch_weights")
+    return w_folded
+
+
+def patch_embed(rows, w, bias=None, out=None, out_dtype: str = "bf16", stream=None):
+    """mimo_patch_embed: rows bf16 [n, 1536] x w bf16 [E, 1536] (or folded
+    [E, 768]) -> out [n, E] (+ bias float32 [E])."""
+    import torch
+    n, e = rows.shape[0], w.shape[0]
+    folded = int(w.shape[1] == ROW_LEN // 2)
+    tdtype = {"f32": torch.float32, "bf16": torch.bfloat16}[out_dtype]
+    if out is None:
+        out = torch.empty((n, e), dtype=tdtype, device=rows.device)
+    code = load().mimo_patch_embed(n, rows.data_ptr(), e, w.data_ptr(), folded,
+                                   bias.data_ptr() if bias is not None else None,
+                                   _dtype_code(out), out.data_ptr(),
+                                   _stream_handle(stream, rows.device))
+    _check(code, "patch_embed")
+    return out
