@@ -143,6 +143,48 @@ def vit_tables_rates(V, plan, ws, reps: int, rope_dim: int = 32) -> dict:
     return out
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+
+
+def patch_embed_rates(V, batch, plan, src, ws, reps: int, embed_dim: int = 1280) -> dict:
+    """The patch embedding (the rows' Conv3d consumer) on the same batch's
+    rows emitted in bf16: the full weight (K = 1536) and, for a batch of
+    stills, the folded weight (K = 768).  Synthetic N(0, 0.02) weights."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    rows = torch.empty((plan.total_rows, 1536), dtype=torch.bfloat16, device="cuda")
+    V.preprocess(src, plan, mean=batch.mean, std=batch.std, out_dtype="bf16", rows=rows,
+                 workspace=ws)
+    g = torch.Generator(device="cuda").manual_seed(0)
+    w = (torch.randn((embed_dim, 1536), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    bias = torch.zeros(embed_dim, dtype=torch.float32, device="cuda")
+    out = torch.empty((plan.total_rows, embed_dim), dtype=torch.bfloat16, device="cuda")
+    res = {"rows": plan.total_rows, "embed_dim": embed_dim, "out": "bf16",
+           "weights": "synthetic N(0, 0.02^2) bf16"}
+    forms = [("full", w, 1536)]
+    if not batch.is_media:
+        forms.append(("folded", V.fold_patch_weights(w), 768))
+    for name, wt, k in forms:
+        ms = time_launches(V, lambda: V.patch_embed(rows, wt, bias, out=out), reps, stream)
+        tflops = 2.0 * plan.total_rows * embed_dim * k / (ms * 1e-3) / 1e12
+        res[name] = {"k": k, "ms": ms, "TFLOP/s": tflops, "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+                     "conv_equivalent_TFLOP/s": 2.0 * plan.total_rows * embed_dim * 1536 / (ms * 1e-3) / 1e12}
+    # the same product through torch's bf16 matmul (vendor GEMM), for context
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.matmul(rows, w.t(), out=out)
+    e0.record(stream)
+    for _ in range(reps):
+        torch.matmul(rows, w.t(), out=out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    res["torch_matmul_full"] = {"ms": ms, "TFLOP/s": 2.0 * plan.total_rows * embed_dim * 1536 / (ms * 1e-3) / 1e12}
+    del rows, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def calibrate_copy(gib: float, reps: int):
     """A plain elementwise copy kernel of known size (read N bytes, write N
     bytes) for scaling the HBM byte counters."""
@@ -177,6 +219,8 @@ def main():
                     help="also time the standalone column_permute gather kernel")
     ap.add_argument("--no-vit-tables", action="store_true",
                     help="skip timing the ViT index-table kernels on the same batch")
+    ap.add_argument("--no-embed", action="store_true",
+                    help="skip timing the patch embedding on the same batch's rows")
     ap.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GIB",
                     help="only run a plain copy kernel of this size (counter calibration)")
     args = ap.parse_args()
@@ -317,6 +361,10 @@ def main():
     if not args.no_vit_tables:
         log("vit tables")
         result["vit_tables"] = vit_tables_rates(V, plan, ws, reps=10)
+
+    if not args.no_embed:
+        log("patch embed")
+        result["patch_embed"] = patch_embed_rates(V, batch, plan, src, ws, reps=5)
 
     if not args.no_cpu_baseline:
         threads = max(1, min(16, os.cpu_count() or 1))

@@ -335,7 +335,7 @@ int mimo_fold_patch_weights(int32_t embed_dim, const void *w, void *w_folded, vo
  * out = rows * W^T (+ bias) for n_rows rows, one kernel launch.
  *   rows       device bf16 [n_rows][1536] (mimo_preprocess_batch output with
  *              MIMO_BF16, either row order), 16-byte aligned.
- *   embed_dim  E: a multiple of 128 in [128, 65536].
+ *   embed_dim  E: a multiple of 256 in [256, 65536].
  *   w          device bf16 [E][1536] (folded = 0), or the folded weight
  *              [E][768] (folded = 1: only the tt = 0 half of every row is
  *              read, which is exact only for rows whose two frames are

@@ -74,11 +74,11 @@ MIXED = STILLS + [(5, 64, 96, 3), (2, 120, 200, 4)]
 
 
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("e", [128, 1280])
+@pytest.mark.parametrize("e", [256, 1280])
 def test_full_k_ragged(V, out_dtype, e):
     _say("full K, E =", e, out_dtype)
     plan, rows = _bf16_rows(V, MIXED, seed=71)
-    assert rows.shape[0] % 128 != 0  # a ragged last tile
+    assert rows.shape[0] % 256 != 0  # a ragged last tile
     w, bias = _weights(e, seed=72)
     wd, bd = w.cuda(), bias.cuda()
     out = V.patch_embed(rows, wd, bd, out_dtype=out_dtype)
@@ -114,19 +114,19 @@ def test_folded_stills_match_full_conv(V, out_dtype):
 
 def test_empty_and_argument_errors(V):
     _say("empty and errors")
-    w, _ = _weights(128, seed=76, bias=False)
+    w, _ = _weights(256, seed=76, bias=False)
     wd = w.cuda()
     rows = torch.zeros((0, 1536), dtype=torch.bfloat16, device="cuda")
     out = V.patch_embed(rows, wd)
-    assert out.shape == (0, 128)
+    assert out.shape == (0, 256)
     lib = V.load()
     r1 = torch.zeros((4, 1536), dtype=torch.bfloat16, device="cuda")
     o1 = torch.zeros((4, 100), dtype=torch.float32, device="cuda")
     assert lib.mimo_patch_embed(4, r1.data_ptr(), 100, wd.data_ptr(), 0, None, V.MIMO_F32,
-                                o1.data_ptr(), None) == V.MIMO_E_INVALID  # E not a multiple of 128
-    assert lib.mimo_patch_embed(4, r1.data_ptr() + 2, 128, wd.data_ptr(), 0, None, V.MIMO_F32,
+                                o1.data_ptr(), None) == V.MIMO_E_INVALID  # E not a multiple of 256
+    assert lib.mimo_patch_embed(4, r1.data_ptr() + 2, 256, wd.data_ptr(), 0, None, V.MIMO_F32,
                                 o1.data_ptr(), None) == V.MIMO_E_INVALID  # misaligned rows
-    assert lib.mimo_patch_embed(4, r1.data_ptr(), 128, wd.data_ptr(), 2, None, V.MIMO_F32,
+    assert lib.mimo_patch_embed(4, r1.data_ptr(), 256, wd.data_ptr(), 2, None, V.MIMO_F32,
                                 o1.data_ptr(), None) == V.MIMO_E_INVALID
 
 

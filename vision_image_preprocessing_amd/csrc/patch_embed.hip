@@ -14,13 +14,20 @@
 // to that one bf16 rounding of W'.
 //
 // Kernel.  C = A * W^T with both operands K-contiguous (bf16), fp32
-// accumulation on v_mfma_f32_32x32x16_bf16.  A workgroup (4 wave64s) owns a
-// 128 x 128 tile of C; each wave a 64 x 64 quarter as 2 x 2 MFMA blocks.  K
-// advances 64 at a time through double-buffered LDS (rows padded by 16 bytes
-// against bank conflicts): while the waves multiply one stage, the next
-// stage's global loads are in flight in registers.  Tiles are ordered N
-// fastest and assigned to XCDs in contiguous runs, so one XCD's L2 serves an
-// A tile to all of its N tiles, and W (<= 4 MB) stays L2-resident.
+// accumulation on v_mfma_f32_32x32x16_bf16.  A workgroup (4 wave64s, one
+// per SIMD) owns a 256 x 256 tile of C; each wave a 128 x 128 quarter as
+// 4 x 4 MFMA blocks (256 accumulators per lane), which keeps the LDS bytes
+// per matrix-core flop at (128 + 128) / (128 * 128) of a 16-wide k step.  K
+// advances 64 at a time through double-buffered LDS; rows are 128 bytes and
+// their eight 16-byte chunks are XOR-swizzled by the row index, so the
+// fragment reads of eight consecutive rows hit distinct banks.  Operand
+// tiles go from global memory straight into LDS (global_load_lds_dwordx4,
+// no register staging): while the waves multiply one stage, the next
+// stage's loads fill the other buffer.  W is the MFMA's first operand, so
+// each lane ends with four consecutive output columns of one row, stored as
+// one 16-byte (float32) or 8-byte (bf16) write.  Tiles are ordered N fastest
+// and assigned to XCDs in contiguous runs, so one XCD's L2 serves an A tile
+// to all of its N tiles, and W (<= 4 MB) stays L2-resident.
 #include <hip/hip_runtime.h>
 
 #include <cstring>
@@ -33,13 +40,17 @@
 namespace mimo {
 namespace {
 
-constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kBM = 256, kBN = 256, kBK = 64;
 constexpr int kEmbedThreads = 256;
-constexpr int kPitch = kBK + 8;     // LDS row pitch in bf16 (144 bytes)
+constexpr int kWaveM = 128, kWaveN = 128;       // one wave's quarter of the tile
+constexpr int kBlocksM = kWaveM / 32, kBlocksN = kWaveN / 32;
+constexpr int kChunks = kBK / 8;                // 16-byte chunks per LDS row
+constexpr int kGroups = kBM / 8 / (kEmbedThreads / 64);  // 1 KB LDS groups per wave per operand
 constexpr int kFoldSeg = 256;       // contiguous K run of one channel in the folded form
 constexpr int kFoldStride = 512;    // its stride in the row (the tt = 1 plane is skipped)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void *lds_void_ptr;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 struct EmbedArgs {
@@ -48,10 +59,10 @@ struct EmbedArgs {
     const float *bias;     // [E] or null
     void *out;             // OutT [n_rows][E]
     int64_t n_rows;
-    int32_t embed_dim;     // E, a multiple of 128
+    int32_t embed_dim;     // E, a multiple of 256
     int32_t k;             // 1536, or 768 folded
     int32_t folded;
-    int32_t n_tiles;       // E / 128
+    int32_t n_tiles;       // E / 256
 };
 
 // Row column of reduction index k0 (a multiple of kBK): the folded form
@@ -60,15 +71,27 @@ __device__ __forceinline__ int a_column(int k0, bool folded) {
     return folded ? (k0 / kFoldSeg) * kFoldStride + k0 % kFoldSeg : k0;
 }
 
-__device__ __forceinline__ void store_out(float *p, float v) { *p = v; }
-__device__ __forceinline__ void store_out(uint16_t *p, float v) {
-    *reinterpret_cast<__bf16 *>(p) = __bf16(v);  // round to nearest even
+// Four consecutive outputs of one row.
+__device__ __forceinline__ void store_out4(float *p, const f32x4 &v) {
+    *reinterpret_cast<f32x4 *>(p) = v;
 }
+__device__ __forceinline__ void store_out4(uint16_t *p, const f32x4 &v) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    const bf16x4 h = {__bf16(v.x), __bf16(v.y), __bf16(v.z), __bf16(v.w)};  // nearest even
+    *reinterpret_cast<bf16x4 *>(p) = h;
+}
+
+// LDS offset (in bf16) of 16-byte chunk v of row r: chunks are swizzled by
+// the row so that eight consecutive rows use eight distinct bank groups.
+__device__ __forceinline__ int lds_at(int r, int v) { return r * kBK + ((v ^ (r & 7)) << 3); }
 
 template <typename OutT>
 __global__ __launch_bounds__(kEmbedThreads) void patch_embed_kernel(EmbedArgs a) {
-    __shared__ uint16_t sa[2][kBM * kPitch];
-    __shared__ uint16_t sb[2][kBN * kPitch];
+    // Two LDS stages as four distinct arrays: the compiler then sees that the
+    // loads filling one stage never alias the reads of the other, and does
+    // not make those reads wait for the loads in flight.
+    __shared__ uint16_t sa0[kBM * kBK], sa1[kBM * kBK];
+    __shared__ uint16_t sb0[kBN * kBK], sb1[kBN * kBK];
     const int64_t tile = xcd_contiguous_tile(blockIdx.x, gridDim.x);
     const int64_t mt = tile / a.n_tiles;
     const int nt = int(tile - mt * a.n_tiles);
@@ -76,86 +99,109 @@ __global__ __launch_bounds__(kEmbedThreads) void patch_embed_kernel(EmbedArgs a)
     const int n0 = nt * kBN;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;  // the wave's 64 x 64 quarter
+    const int wm = wave >> 1, wn = wave & 1;  // the wave's quarter
     const bool folded = a.folded != 0;
 
-    // Global -> register loads of one stage: 128 rows x 64 k of A and of W,
-    // 16 bytes per load, 4 + 4 per thread.  Rows past n_rows load zeros.
-    u32x4 ra[4], rb[4];
-    auto load_stage = [&](int k0) {
+    // Global -> LDS loads of one stage: 256 rows x 64 k of A and of W.  Wave
+    // w fills LDS row groups [8 kGroups w, 8 kGroups (w + 1)); within a 1 KB
+    // group lane l lands at row l / 8, physical chunk l % 8, so it fetches
+    // the logical chunk (l % 8) ^ (l / 8) of its row (the swizzle).  Rows
+    // past n_rows read the last row instead; their results are never stored.
+    const uint16_t *a_src[kGroups];
+    const uint16_t *w_src[kGroups];
+#pragma unroll
+    for (int i = 0; i < kGroups; ++i) {
+        const int r = (wave * kGroups + i) * 8 + (lane >> 3);
+        const int v = (lane & 7) ^ (lane >> 3);
+        const int64_t row = m0 + r < a.n_rows ? m0 + r : a.n_rows - 1;
+        a_src[i] = a.rows + row * kRowLen + v * 8;
+        w_src[i] = a.w + int64_t(n0 + r) * a.k + v * 8;
+    }
+    auto load_stage = [&](int k0, uint16_t *da, uint16_t *db) {
         const int acol = a_column(k0, folded);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int idx = tid + i * kEmbedThreads;
-            const int r = idx >> 3, v = idx & 7;
-            const int64_t row = m0 + r;
-            if (row < a.n_rows)
-                ra[i] = *reinterpret_cast<const u32x4 *>(a.rows + row * kRowLen + acol + v * 8);
-            else
-                ra[i] = u32x4{0, 0, 0, 0};
-            rb[i] = *reinterpret_cast<const u32x4 *>(a.w + int64_t(n0 + r) * a.k + k0 + v * 8);
+        for (int i = 0; i < kGroups; ++i) {
+            const int g = wave * kGroups + i;
+            __builtin_amdgcn_global_load_lds(a_src[i] + acol, (lds_void_ptr)(da + g * 8 * kBK), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(w_src[i] + k0, (lds_void_ptr)(db + g * 8 * kBK), 16, 0, 0);
         }
     };
-    auto store_stage = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int idx = tid + i * kEmbedThreads;
-            const int r = idx >> 3, v = idx & 7;
-            *reinterpret_cast<u32x4 *>(&sa[buf][r * kPitch + v * 8]) = ra[i];
-            *reinterpret_cast<u32x4 *>(&sb[buf][r * kPitch + v * 8]) = rb[i];
-        }
-    };
+    // every direct load of this thread has landed in LDS
+    auto wait_loads = [] { __builtin_amdgcn_s_waitcnt(0); };
 
-    f32x16 acc[2][2];
+    f32x16 acc[kBlocksM][kBlocksN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kBlocksM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+        for (int j = 0; j < kBlocksN; ++j) acc[i][j] = f32x16{};
 
     const int stages = a.k / kBK;
-    load_stage(0);
-    store_stage(0);
+    load_stage(0, sa0, sb0);
+    wait_loads();
     __syncthreads();
-    // MFMA operand rows of this lane: A block i covers C rows wm*64 + i*32 +
-    // (lane % 32); B block j covers C columns wn*64 + j*32 + (lane % 32); the
-    // lane supplies k = 8 * (lane / 32) .. + 7 of each 16-wide k step.
-    const int frag_k = 8 * (lane >> 5);
-    for (int s = 0; s < stages; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < stages) load_stage((s + 1) * kBK);
+    // MFMA operand rows of this lane: A block i covers C rows wm*128 + i*32 +
+    // (lane % 32); B block j covers C columns wn*128 + j*32 + (lane % 32);
+    // the lane supplies k = 8 * (lane / 32) .. + 7 of each 16-wide k step.
+    const int frag_chunk = lane >> 5;
+    const int frag_row = lane & 31;
+    // Fragments of k step ks from one LDS stage.
+    auto read_frags = [&](const uint16_t *ta, const uint16_t *tb, int ks, bf16x8 (&fa)[kBlocksM],
+                          bf16x8 (&fb)[kBlocksN]) {
 #pragma unroll
-        for (int ks = 0; ks < kBK; ks += 16) {
-            bf16x8 fa[2], fb[2];
+        for (int i = 0; i < kBlocksM; ++i)
+            fa[i] = *reinterpret_cast<const bf16x8 *>(
+                &ta[lds_at(wm * kWaveM + i * 32 + frag_row, 2 * ks + frag_chunk)]);
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int ar = wm * 64 + i * 32 + (lane & 31);
-                fa[i] = *reinterpret_cast<const bf16x8 *>(&sa[buf][ar * kPitch + ks + frag_k]);
-                const int br = wn * 64 + i * 32 + (lane & 31);
-                fb[i] = *reinterpret_cast<const bf16x8 *>(&sb[buf][br * kPitch + ks + frag_k]);
-            }
+        for (int j = 0; j < kBlocksN; ++j)
+            fb[j] = *reinterpret_cast<const bf16x8 *>(
+                &tb[lds_at(wn * kWaveN + j * 32 + frag_row, 2 * ks + frag_chunk)]);
+    };
+    constexpr int kSteps = kBK / 16;
+    // One stage: start filling the other LDS stage with stage s + 1, multiply
+    // this one (the next k step's fragments are read while this step's
+    // MFMAs run), then wait for the loads and for every wave.
+    auto stage = [&](int s, const uint16_t *ta, const uint16_t *tb, uint16_t *na, uint16_t *nb) {
+        if (s + 1 < stages) load_stage((s + 1) * kBK, na, nb);
+        bf16x8 fa[2][kBlocksM], fb[2][kBlocksN];
+        read_frags(ta, tb, 0, fa[0], fb[0]);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+        for (int ks = 0; ks < kSteps; ++ks) {
+            if (ks + 1 < kSteps) read_frags(ta, tb, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+            for (int i = 0; i < kBlocksM; ++i)
+#pragma unroll
+                for (int j = 0; j < kBlocksN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks & 1][j], fa[ks & 1][i],
+                                                                        acc[i][j], 0, 0, 0);
         }
-        if (s + 1 < stages) store_stage(buf ^ 1);
+        wait_loads();
         __syncthreads();
+    };
+    // stages is even (1536 / 64 or 768 / 64), so stages alternate in pairs
+    for (int s = 0; s < stages; s += 2) {
+        stage(s, sa0, sb0, sa1, sb1);
+        stage(s + 1, sa1, sb1, sa0, sb0);
     }
 
-    // Epilogue: value q of block (i, j) is C row 8 * (q / 4) + 4 * (lane / 32)
-    // + q % 4 of the block, column lane % 32.
+    // Epilogue.  With W as the first operand, value q of block (i, j) is
+    // output row (lane % 32) of A block i and column 8 * (q / 4) +
+    // 4 * (lane / 32) + q % 4 of W block j: four consecutive columns per
+    // group q / 4.
     OutT *out = static_cast<OutT *>(a.out);
+    const bool full_tile = m0 + kBM <= a.n_rows;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int col = n0 + wn * 64 + j * 32 + (lane & 31);
-        const float b = a.bias ? a.bias[col] : 0.0f;
+    for (int i = 0; i < kBlocksM; ++i) {
+        const int64_t row = m0 + wm * kWaveM + i * 32 + (lane & 31);
+        if (!full_tile && row >= a.n_rows) continue;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < kBlocksN; ++j)
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int64_t row = m0 + wm * 64 + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-                if (row < a.n_rows) store_out(out + row * a.embed_dim + col, acc[i][j][q] + b);
+            for (int g = 0; g < 4; ++g) {
+                const int col = n0 + wn * kWaveN + j * 32 + 8 * g + 4 * (lane >> 5);
+                f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                           acc[i][j][4 * g + 3]};
+                if (a.bias) v += *reinterpret_cast<const f32x4 *>(a.bias + col);
+                store_out4(out + row * a.embed_dim + col, v);
             }
     }
 }
@@ -204,15 +250,15 @@ int mimo_patch_embed(int64_t n_rows, const void *rows, int32_t embed_dim, const 
                      void *stream) {
     clear_error();
     if (n_rows < 0 || embed_dim < kBN || embed_dim % kBN || embed_dim > 65536)
-        return set_error(MIMO_E_INVALID, "patch_embed: embed_dim must be a multiple of 128 in [128, 65536]");
+        return set_error(MIMO_E_INVALID, "patch_embed: embed_dim must be a multiple of 256 in [256, 65536]");
     if (folded != 0 && folded != 1)
         return set_error(MIMO_E_INVALID, "patch_embed: folded must be 0 or 1");
     if (out_dtype != MIMO_F32 && out_dtype != MIMO_BF16)
         return set_error(MIMO_E_INVALID, "patch_embed: out_dtype must be MIMO_F32 or MIMO_BF16");
     if (n_rows == 0) return MIMO_OK;
     if (!rows || !w || !out || !check_ptr_align(rows, 16) || !check_ptr_align(w, 16) ||
-        !check_ptr_align(out, 16) || (bias && !check_ptr_align(bias, 4)))
-        return set_error(MIMO_E_INVALID, "patch_embed: null or misaligned pointer (rows, w, out: 16 bytes)");
+        !check_ptr_align(out, 16) || (bias && !check_ptr_align(bias, 16)))
+        return set_error(MIMO_E_INVALID, "patch_embed: null or misaligned pointer (rows, w, out, bias: 16 bytes)");
     const int64_t m_tiles = (n_rows + kBM - 1) / kBM;
     const int32_t n_tiles = embed_dim / kBN;
     if (m_tiles * n_tiles > 0x7FFFFFFFll)
