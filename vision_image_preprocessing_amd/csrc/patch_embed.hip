@@ -20,7 +20,7 @@
 // per matrix-core flop at (128 + 128) / (128 * 128) of a 16-wide k step.  K
 // advances 64 at a time through double-buffered LDS; rows are 128 bytes and
 // their eight 16-byte chunks are XOR-swizzled by the row index, so the
-// fragment reads of eight consecutive rows hit distinct banks.  Operand
+// fragment reads of 16 consecutive rows hit distinct banks.  Operand
 // tiles go from global memory straight into LDS (global_load_lds_dwordx4,
 // no register staging): while the waves multiply one stage, the next
 // stage's loads fill the other buffer.  W is the MFMA's first operand, so
@@ -81,9 +81,13 @@ __device__ __forceinline__ void store_out4(uint16_t *p, const f32x4 &v) {
     *reinterpret_cast<bf16x4 *>(p) = h;
 }
 
-// LDS offset (in bf16) of 16-byte chunk v of row r: chunks are swizzled by
-// the row so that eight consecutive rows use eight distinct bank groups.
-__device__ __forceinline__ int lds_at(int r, int v) { return r * kBK + ((v ^ (r & 7)) << 3); }
+// Swizzle key of LDS row r: the same logical chunk of rows r .. r + 7 lands
+// in 8 distinct 16-byte positions, and that of rows r .. r + 15 in 16
+// distinct (row parity, position) pairs, so a 16-byte read by 8 or by 16
+// lanes of consecutive rows touches every bank at most once.
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+// LDS offset (in bf16) of logical 16-byte chunk v of row r.
+__device__ __forceinline__ int lds_at(int r, int v) { return r * kBK + ((v ^ swz(r)) << 3); }
 
 template <typename OutT>
 __global__ __launch_bounds__(kEmbedThreads) void patch_embed_kernel(EmbedArgs a) {
@@ -105,14 +109,14 @@ __global__ __launch_bounds__(kEmbedThreads) void patch_embed_kernel(EmbedArgs a)
     // Global -> LDS loads of one stage: 256 rows x 64 k of A and of W.  Wave
     // w fills LDS row groups [8 kGroups w, 8 kGroups (w + 1)); within a 1 KB
     // group lane l lands at row l / 8, physical chunk l % 8, so it fetches
-    // the logical chunk (l % 8) ^ (l / 8) of its row (the swizzle).  Rows
+    // the logical chunk (l % 8) ^ swz(row) of its row.  Rows
     // past n_rows read the last row instead; their results are never stored.
     const uint16_t *a_src[kGroups];
     const uint16_t *w_src[kGroups];
 #pragma unroll
     for (int i = 0; i < kGroups; ++i) {
         const int r = (wave * kGroups + i) * 8 + (lane >> 3);
-        const int v = (lane & 7) ^ (lane >> 3);
+        const int v = (lane & 7) ^ swz(r);
         const int64_t row = m0 + r < a.n_rows ? m0 + r : a.n_rows - 1;
         a_src[i] = a.rows + row * kRowLen + v * 8;
         w_src[i] = a.w + int64_t(n0 + r) * a.k + v * 8;
@@ -167,6 +171,9 @@ __global__ __launch_bounds__(kEmbedThreads) void patch_embed_kernel(EmbedArgs a)
 #pragma unroll
         for (int ks = 0; ks < kSteps; ++ks) {
             if (ks + 1 < kSteps) read_frags(ta, tb, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+            // keep those reads ahead of this step's MFMAs (the scheduler would
+            // otherwise sink each read to its first use and expose its latency)
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < kBlocksM; ++i)
 #pragma unroll
