@@ -115,6 +115,14 @@ def _load():
         lib.oracle_chunk_seqlens.restype = i64
         lib.oracle_patch_embed.argtypes = [p, i64, i64, p, i64, p, p]
         lib.oracle_patch_embed.restype = ctypes.c_int
+        lib.oracle_hf_smart_resize.argtypes = [i64, i64, i64, i64, i64, ctypes.c_double,
+                                               ctypes.POINTER(i64), ctypes.POINTER(i64)]
+        lib.oracle_hf_smart_resize.restype = ctypes.c_int
+        lib.oracle_pil_resize_bicubic.argtypes = [p, i64, i64, i64, i64, i64, p]
+        lib.oracle_pil_resize_bicubic.restype = ctypes.c_int
+        lib.oracle_hf_preprocess_image.argtypes = [p, i64, i64, i64, i64, i64, i64, i64, i64,
+                                                   p, p, p]
+        lib.oracle_hf_preprocess_image.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -389,3 +397,50 @@ def patch_embed(rows: np.ndarray, w: np.ndarray, bias=None) -> np.ndarray:
     if st != OK:
         raise OracleError(st, "patch_embed")
     return out
+
+
+# ------------------------------------------------- stock-HF contrast path
+def hf_smart_resize_status(height: int, width: int, factor: int = PATCH * MERGE,
+                           min_pixels: int = MIN_PIXELS, max_pixels: int = MAX_PIXELS,
+                           max_aspect: float = MAX_ASPECT):
+    """processing page, module docstring: the stock Qwen2-VL smart_resize
+    (each side clamped on its own, no short-side upscale): (status, h, w)."""
+    oh, ow = ctypes.c_int64(0), ctypes.c_int64(0)
+    st = _load().oracle_hf_smart_resize(height, width, factor, min_pixels, max_pixels,
+                                        float(max_aspect), ctypes.byref(oh), ctypes.byref(ow))
+    return st, oh.value, ow.value
+
+
+def hf_smart_resize(height: int, width: int, **kw):
+    st, oh, ow = hf_smart_resize_status(height, width, **kw)
+    if st != OK:
+        raise OracleError(st, f"hf_smart_resize({height}, {width})")
+    return oh, ow
+
+
+def pil_resize_bicubic(img: np.ndarray, out_h: int, out_w: int) -> np.ndarray:
+    """PIL's 8-bit antialiased bicubic resize of uint8 [h, w, c]."""
+    img = np.ascontiguousarray(img, dtype=np.uint8)
+    h, w, c = img.shape
+    out = np.empty((out_h, out_w, c), dtype=np.uint8)
+    st = _load().oracle_pil_resize_bicubic(_ptr(img), h, w, c, out_h, out_w, _ptr(out))
+    if st != OK:
+        raise OracleError(st, "pil_resize_bicubic")
+    return out
+
+
+def hf_preprocess_image(hwc: np.ndarray, out_h: int, out_w: int, mean01, std01,
+                        patch: int = PATCH, merge: int = MERGE, temporal: int = TEMPORAL) -> np.ndarray:
+    """The stock processor's pixel path for one image (alpha dropped, PIL
+    bicubic to uint8, 0-1 rescale, float32 normalise): float32 rows in
+    merge-block order."""
+    hwc = np.ascontiguousarray(hwc, dtype=np.uint8)
+    h, w, c = hwc.shape
+    m = np.ascontiguousarray(np.asarray(mean01, dtype=np.float32))
+    s = np.ascontiguousarray(np.asarray(std01, dtype=np.float32))
+    rows = np.empty(((out_h // patch) * (out_w // patch), 3 * temporal * patch * patch), dtype=np.float32)
+    st = _load().oracle_hf_preprocess_image(_ptr(hwc), h, w, c, out_h, out_w, patch, merge, temporal,
+                                            _ptr(m), _ptr(s), _ptr(rows))
+    if st != OK:
+        raise OracleError(st, "hf_preprocess_image")
+    return rows

@@ -15,6 +15,8 @@
  *   - docs.rs "cortiq_engine::mimo_vision" (module conventions list;
  *      resize_bilinear; column_permutation; smart_resize; the video helpers
  *      prepare_video_frames, smart_nframes, sample_frames, video_max_pixels),
+ *   - the processing page's module docstring for the stock-HF contrast path
+ *     (PIL bicubic with antialias, uint8 round trip, 0-1 normalisation),
  *   - NeMo Automodel "nemo_automodel.components.models.mimo_v2_flash.vision"
  *     (MiMoVisionRotaryEmbedding; MiMoVisionTransformer._rotary_positions,
  *      _get_window_index, _apply_merge_index) for the ViT index tables.
@@ -32,7 +34,9 @@
  * 65,536 (value, alpha) pairs; resize against torch CPU F.interpolate and
  * against a float64 evaluation within a derived bound; layout against a
  * coded image and a tensor reshape formulation; permutation against brute
- * force; bf16 rounding against torch; video helpers against numpy linspace
+ * force; bf16 rounding against torch; the stock-HF contrast path against
+ * PIL's bicubic resize and transformers' Qwen2-VL processor and smart_resize,
+ * bitwise; video helpers against numpy linspace
  * and hand-derived cases, frames against a torch composition; ViT tables
  * against reshapes, brute-force sorts, a coded image and torch's float32
  * inv_freq / outer product.  No function here is "parity unpinned".
@@ -780,4 +784,241 @@ int oracle_patch_embed(const float *rows, int64_t n_rows, int64_t row_len, const
             out[r * embed_dim + e] = acc;
         }
     return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Stock-HF contrast path (NeMo Automodel "mimo_v2_flash.processing", module */
+/* docstring): the stock Qwen2-VL processor resizes with PIL bicubic         */
+/* (antialiased, back to uint8), normalises in 0-1 units, drops alpha, and   */
+/* its smart_resize clamps each side on its own instead of upscaling a short */
+/* side first.                                                               */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Stock smart_resize: round each side to the factor (ties to even); if the
+ * area is above max_pixels shrink by beta = sqrt(h*w/max) with floor, each
+ * side clamped to at least factor; else if below min_pixels grow by
+ * beta = sqrt(min/(h*w)) with ceil.  Aspect above max_aspect is an error.
+ */
+int oracle_hf_smart_resize(int64_t h, int64_t w, int64_t factor, int64_t min_pixels,
+                           int64_t max_pixels, double max_aspect, int64_t *out_h, int64_t *out_w)
+{
+    if (h < 1 || w < 1 || factor < 1 || min_pixels < 0 || max_pixels < 1)
+        return ORC_E_INVALID;
+    double hd = (double)h, wd = (double)w, f = (double)factor;
+    double big = hd > wd ? hd : wd, small = hd > wd ? wd : hd;
+    if (big / small > max_aspect)
+        return ORC_E_ASPECT;
+    double hb = py_round(hd / f) * f, wb = py_round(wd / f) * f;
+    if (hb * wb > (double)max_pixels) {
+        double beta = sqrt((hd * wd) / (double)max_pixels);
+        hb = floor(hd / beta / f) * f;
+        wb = floor(wd / beta / f) * f;
+        if (hb < f)
+            hb = f;
+        if (wb < f)
+            wb = f;
+    } else if (hb * wb < (double)min_pixels) {
+        double beta = sqrt((double)min_pixels / (hd * wd));
+        hb = ceil(hd * beta / f) * f;
+        wb = ceil(wd * beta / f) * f;
+    }
+    *out_h = (int64_t)hb;
+    *out_w = (int64_t)wb;
+    return ORC_OK;
+}
+
+/* Keys' cubic convolution kernel with a = -0.5 (the bicubic of PIL). */
+static double keys_cubic(double x)
+{
+    const double a = -0.5;
+    if (x < 0.0)
+        x = -x;
+    if (x < 1.0)
+        return ((a + 2.0) * x - (a + 3.0)) * x * x + 1.0;
+    if (x < 2.0)
+        return (((x - 5.0) * x + 8.0) * x - 4.0) * a;
+    return 0.0;
+}
+
+#define PIL_BITS 22 /* fractional bits of the 8-bit resampler's weights */
+
+/*
+ * Taps of one axis for PIL's antialiased bicubic, n_in -> n_out samples:
+ * scale = n_in / n_out; the kernel is widened by max(scale, 1) (support
+ * 2 * that); output i centred at (i + 0.5) * scale takes inputs
+ * [first, first + count) with weights keys((j - centre + 0.5) / widening),
+ * normalised to sum 1 and rounded half away from zero to PIL_BITS bits.
+ * first[i], count[i], weight[i * ksize + j]; returns ksize.
+ */
+static int64_t pil_axis_taps(int64_t n_in, int64_t n_out, int64_t **first_out,
+                             int64_t **count_out, int32_t **weight_out)
+{
+    double scale = (double)n_in / (double)n_out;
+    double widen = scale < 1.0 ? 1.0 : scale;
+    double support = 2.0 * widen;
+    int64_t ksize = (int64_t)ceil(support) * 2 + 1;
+    int64_t *first = malloc(sizeof(int64_t) * (size_t)n_out);
+    int64_t *count = malloc(sizeof(int64_t) * (size_t)n_out);
+    int32_t *weight = calloc((size_t)(n_out * ksize), sizeof(int32_t));
+    double *k = malloc(sizeof(double) * (size_t)ksize);
+    if (!first || !count || !weight || !k) {
+        free(first);
+        free(count);
+        free(weight);
+        free(k);
+        return ORC_E_NOMEM;
+    }
+    for (int64_t i = 0; i < n_out; ++i) {
+        double centre = ((double)i + 0.5) * scale;
+        int64_t lo = (int64_t)(centre - support + 0.5);
+        if (lo < 0)
+            lo = 0;
+        int64_t hi = (int64_t)(centre + support + 0.5);
+        if (hi > n_in)
+            hi = n_in;
+        int64_t n = hi - lo;
+        double total = 0.0;
+        for (int64_t j = 0; j < n; ++j) {
+            k[j] = keys_cubic(((double)(j + lo) - centre + 0.5) / widen);
+            total += k[j];
+        }
+        for (int64_t j = 0; j < n; ++j) {
+            double v = total != 0.0 ? k[j] / total : k[j];
+            double fixed = v * (double)(1 << PIL_BITS);
+            weight[i * ksize + j] = (int32_t)(v < 0.0 ? fixed - 0.5 : fixed + 0.5);
+        }
+        first[i] = lo;
+        count[i] = n;
+    }
+    free(k);
+    *first_out = first;
+    *count_out = count;
+    *weight_out = weight;
+    return ksize;
+}
+
+/* (acc + half) >> PIL_BITS clamped to a byte: the resampler's rounding. */
+static uint8_t pil_round_clip(int32_t acc)
+{
+    int32_t v = (acc + (1 << (PIL_BITS - 1))) >> PIL_BITS;
+    return (uint8_t)(v < 0 ? 0 : (v > 255 ? 255 : v));
+}
+
+/*
+ * PIL's 8-bit antialiased bicubic resize of an interleaved uint8 image
+ * [h][w][c] to [oh][ow][c]: a horizontal pass (only if ow != w) to bytes,
+ * then a vertical pass (only if oh != h) to bytes, each output the rounded,
+ * clamped fixed-point sum over its taps.
+ */
+int oracle_pil_resize_bicubic(const uint8_t *src, int64_t h, int64_t w, int64_t c, int64_t oh,
+                              int64_t ow, uint8_t *dst)
+{
+    if (h < 1 || w < 1 || c < 1 || oh < 1 || ow < 1)
+        return ORC_E_INVALID;
+    uint8_t *mid = malloc((size_t)(h * ow * c));
+    if (!mid)
+        return ORC_E_NOMEM;
+    if (ow != w) {
+        int64_t *first, *count;
+        int32_t *wt;
+        int64_t ks = pil_axis_taps(w, ow, &first, &count, &wt);
+        if (ks < 0) {
+            free(mid);
+            return (int)ks;
+        }
+        for (int64_t y = 0; y < h; ++y)
+            for (int64_t x = 0; x < ow; ++x)
+                for (int64_t ch = 0; ch < c; ++ch) {
+                    int32_t acc = 0;
+                    for (int64_t j = 0; j < count[x]; ++j)
+                        acc += (int32_t)src[(y * w + first[x] + j) * c + ch] * wt[x * ks + j];
+                    mid[(y * ow + x) * c + ch] = pil_round_clip(acc);
+                }
+        free(first);
+        free(count);
+        free(wt);
+    } else {
+        memcpy(mid, src, (size_t)(h * w * c));
+    }
+    if (oh != h) {
+        int64_t *first, *count;
+        int32_t *wt;
+        int64_t ks = pil_axis_taps(h, oh, &first, &count, &wt);
+        if (ks < 0) {
+            free(mid);
+            return (int)ks;
+        }
+        for (int64_t y = 0; y < oh; ++y)
+            for (int64_t x = 0; x < ow; ++x)
+                for (int64_t ch = 0; ch < c; ++ch) {
+                    int32_t acc = 0;
+                    for (int64_t j = 0; j < count[y]; ++j)
+                        acc += (int32_t)mid[((first[y] + j) * ow + x) * c + ch] * wt[y * ks + j];
+                    dst[(y * ow + x) * c + ch] = pil_round_clip(acc);
+                }
+        free(first);
+        free(count);
+        free(wt);
+    } else {
+        memcpy(dst, mid, (size_t)(oh * ow * c));
+    }
+    free(mid);
+    return ORC_OK;
+}
+
+/*
+ * The stock processor's pixel path for one image: the alpha channel (if any)
+ * is dropped, the RGB bytes resized with PIL bicubic to (oh, ow), each byte
+ * v rescaled as float32(float64(v) * (1 / 255)) and normalised in float32 as
+ * (x - mean01[c]) / std01[c], then rows laid out as in the MiMo path
+ * (T identical frames, (c, tt, py, px), merge-block order).
+ */
+int oracle_hf_preprocess_image(const uint8_t *src, int64_t h, int64_t w, int64_t c, int64_t oh,
+                               int64_t ow, int64_t patch, int64_t merge, int64_t temporal,
+                               const float *mean01, const float *std01, float *rows)
+{
+    if ((c != 3 && c != 4) || oh % (patch * merge) || ow % (patch * merge))
+        return ORC_E_INVALID;
+    uint8_t *rgb = malloc((size_t)(h * w * 3));
+    uint8_t *res = malloc((size_t)(oh * ow * 3));
+    float *planar = malloc(sizeof(float) * (size_t)(3 * oh * ow));
+    if (!rgb || !res || !planar) {
+        free(rgb);
+        free(res);
+        free(planar);
+        return ORC_E_NOMEM;
+    }
+    for (int64_t i = 0; i < h * w; ++i)
+        for (int64_t ch = 0; ch < 3; ++ch)
+            rgb[i * 3 + ch] = src[i * c + ch];
+    int st = oracle_pil_resize_bicubic(rgb, h, w, 3, oh, ow, res);
+    if (st == ORC_OK) {
+        const double rescale = 1.0 / 255.0;
+        for (int64_t ch = 0; ch < 3; ++ch)
+            for (int64_t i = 0; i < oh * ow; ++i) {
+                float x = (float)((double)res[i * 3 + ch] * rescale);
+                planar[ch * oh * ow + i] = (x - mean01[ch]) / std01[ch];
+            }
+        int64_t gh = oh / patch, gw = ow / patch, bh = gh / merge, bw = gw / merge;
+        int64_t row_len = 3 * temporal * patch * patch, r = 0;
+        for (int64_t br = 0; br < bh; ++br)
+            for (int64_t bc = 0; bc < bw; ++bc)
+                for (int64_t mh = 0; mh < merge; ++mh)
+                    for (int64_t mw = 0; mw < merge; ++mw) {
+                        float *row = rows + r * row_len;
+                        int64_t y0 = (br * merge + mh) * patch, x0 = (bc * merge + mw) * patch;
+                        for (int64_t ch = 0; ch < 3; ++ch)
+                            for (int64_t tt = 0; tt < temporal; ++tt)
+                                for (int64_t py = 0; py < patch; ++py)
+                                    for (int64_t px = 0; px < patch; ++px)
+                                        row[((ch * temporal + tt) * patch + py) * patch + px] =
+                                            planar[ch * oh * ow + (y0 + py) * ow + x0 + px];
+                        ++r;
+                    }
+    }
+    free(rgb);
+    free(res);
+    free(planar);
+    return st;
 }
