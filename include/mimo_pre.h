@@ -312,6 +312,51 @@ int mimo_window_index(int32_t n, const mimo_image_desc *desc, int32_t column_maj
 int64_t mimo_chunk_seqlens(int32_t n, const mimo_image_desc *desc, int32_t *cu, int64_t capacity);
 
 /* ------------------------------------------------------------------------
+ * Stock-HF contrast path.  NeMo Automodel "mimo_v2_flash.processing", module
+ * docstring: the stock Qwen2-VL processor that AutoProcessor resolves for
+ * these checkpoints drops alpha, resizes with PIL's antialiased bicubic back
+ * to bytes, normalises in 0-1 units, and its smart_resize clamps each side
+ * on its own instead of scaling a short side up first.  The page calls these
+ * the wrong pixels for the model; they are here so the shift can be measured
+ * and reproduced.
+ * ------------------------------------------------------------------------ */
+
+/* The stock smart_resize (round each side to the factor; shrink with floor,
+ * each side at least one factor; grow with ceil; aspect guard always).
+ * Returns MIMO_OK, MIMO_E_INVALID, MIMO_E_ASPECT or MIMO_E_TOO_LARGE. */
+int mimo_hf_smart_resize(int64_t h, int64_t w, const mimo_params *params, int64_t *out_h,
+                         int64_t *out_w);
+
+/* mimo_plan_geometry with the stock geometry (frames = 1, grid_t = 1). */
+int mimo_plan_hf(int32_t n, const int32_t *hwc, const mimo_params *params, mimo_image_desc *out,
+                 int64_t *total_rows, int64_t *total_src_bytes);
+
+/* Device workspace bytes mimo_preprocess_hf_batch needs for this plan (the
+ * per-item records, a normalisation table, and the resize taps). */
+size_t mimo_hf_workspace_bytes(int32_t n, const mimo_image_desc *desc);
+
+/*
+ * The stock processor's pixels for a planned batch (mimo_plan_hf), one
+ * kernel launch after one upload of the tables.  Alpha is ignored; each
+ * resampled axis uses PIL's antialiased bicubic with 22-bit fixed-point
+ * weights and a rounded byte result (horizontal first, each pass only if
+ * that side changes); bytes v become float32(float64(v) / 255), then
+ * (x - mean01[c]) / std01[c] in float32; rows as mimo_preprocess_batch
+ * writes them (two identical frames, either or both orders).  Results equal
+ * the stock processor's bit for bit.
+ *   mean01, std01  host float[3], statistics in 0-1 units.
+ *   workspace      device, >= mimo_hf_workspace_bytes(n, desc), 16-byte aligned.
+ * Other arguments as for mimo_preprocess_batch.  Returns MIMO_OK,
+ * MIMO_E_INVALID, MIMO_E_CAPACITY, MIMO_E_UNSUPPORTED (a vertical downscale
+ * whose taps for one output row exceed 481 source rows), MIMO_E_TOO_LARGE or
+ * MIMO_E_HIP.
+ */
+int mimo_preprocess_hf_batch(int32_t n, const mimo_image_desc *desc, const uint8_t *src,
+                             int64_t src_capacity, const float *mean01, const float *std01,
+                             int32_t out_dtype, void *rows, void *rows_col, int64_t capacity_rows,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * Patch embedding.  NeMo Automodel "mimo_v2_flash.vision",
  * MiMoVisionPatchEmbed: the rows' consumer, a Conv3d whose kernel and stride
  * are both (T, P, P) = (2, 16, 16), so each row is one window and the

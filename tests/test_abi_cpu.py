@@ -260,3 +260,57 @@ def test_vit_tables_argument_validation_without_gpu():
     # an empty batch is a no-op
     assert lib.mimo_rotary_tables(0, None, 0, 32, 1e4, dummy, None, None, 0, None, 0,
                                   None) == V.MIMO_OK
+
+
+def test_hf_plan_matches_oracle():
+    rng = np.random.default_rng(57)
+    shapes = [(16, 192, 3), (8, 500, 3), (31, 31, 4), (1, 64, 3), (1, 1, 3), (4000, 6000, 3),
+              (1, 8193, 3), (200, 300, 4)]
+    shapes += [(int(rng.integers(1, 3000)), int(rng.integers(1, 3000)), 3) for _ in range(500)]
+    desc, total_rows, total_src, _ = V.plan_hf(shapes, check=False)
+    rows = src = 0
+    for i, (h, w, c) in enumerate(shapes):
+        st, oh, ow = oracle.hf_smart_resize_status(h, w)
+        d = desc[i]
+        assert d["status"] == st, (h, w)
+        if st == 0:
+            assert (d["dst_h"], d["dst_w"]) == (oh, ow), (h, w)
+            assert (d["grid_t"], d["grid_h"], d["grid_w"], d["rows"]) == (1, oh // 16, ow // 16, oh * ow // 256)
+            assert d["row_offset"] == rows
+            rows += int(d["rows"])
+        assert d["src_offset"] == src
+        src += h * w * c
+    assert (total_rows, total_src) == (rows, src)
+    assert V.hf_smart_resize(16, 192) == oracle.hf_smart_resize(16, 192) == (32, 320)
+
+
+def test_hf_argument_validation_without_gpu():
+    lib = V.load()
+    desc, _, _, _ = V.plan_hf([(64, 64, 3)])
+    m = (ctypes.c_float * 3)(0.5, 0.5, 0.5)
+    s = (ctypes.c_float * 3)(0.2, 0.2, 0.2)
+    bad_s = (ctypes.c_float * 3)(0.2, 0.0, 0.2)
+    dummy = ctypes.c_void_p(0x1000)
+    ws = V.hf_workspace_bytes(desc)
+    assert lib.mimo_preprocess_hf_batch(1, desc.ctypes.data, dummy, 4096, m, s, 0, None, None,
+                                        1 << 20, dummy, ws, None) == V.MIMO_E_INVALID
+    assert lib.mimo_preprocess_hf_batch(1, desc.ctypes.data, dummy, 4096, m, bad_s, 0, dummy, None,
+                                        1 << 20, dummy, ws, None) == V.MIMO_E_INVALID
+    assert lib.mimo_preprocess_hf_batch(1, desc.ctypes.data, dummy, 1 << 20, m, s, 0, dummy, None,
+                                        1 << 20, dummy, 16, None) == V.MIMO_E_CAPACITY
+    assert lib.mimo_preprocess_hf_batch(1, desc.ctypes.data, dummy, 16, m, s, 0, dummy, None,
+                                        1 << 20, dummy, ws, None) == V.MIMO_E_CAPACITY
+
+
+def test_hf_extreme_vertical_downscale_is_refused_before_launch():
+    lib = V.load()
+    p = V.make_params(4096, 8192)
+    desc, _, _, _ = V.plan_hf([(20000, 20000, 3)], p)
+    assert desc["dst_h"][0] == 64  # a ~312x downscale: about 1250 taps per output row
+    m = (ctypes.c_float * 3)(0.5, 0.5, 0.5)
+    s = (ctypes.c_float * 3)(0.2, 0.2, 0.2)
+    dummy = ctypes.c_void_p(0x1000)
+    st = lib.mimo_preprocess_hf_batch(1, desc.ctypes.data, dummy, 20000 * 20000 * 3, m, s, 0, dummy,
+                                      None, 1 << 20, dummy, V.hf_workspace_bytes(desc), None)
+    assert st == V.MIMO_E_UNSUPPORTED
+    assert "downscale" in V.last_error()

@@ -16,9 +16,13 @@ from ._abi import (  # noqa: F401
     IMAGE_DESC_DTYPE, MIMO_BF16, MIMO_E_ASPECT, MIMO_E_CAPACITY, MIMO_E_DEGENERATE,
     MIMO_E_HIP, MIMO_E_INVALID, MIMO_E_TOO_LARGE, MIMO_E_UNSUPPORTED, MIMO_F32, MIMO_OK,
     ROW_LEN, LibraryNotBuilt, MimoError, MimoParams, column_permutation, column_permute,
-    chunk_seqlens, default_params, dispatch_count, fold_patch_weights, last_error, load,
-    make_params, patch_embed, plan_frames, plan_geometry, preprocess_batch, rope_inv_freq, rotary_tables, sample_frames,
+    chunk_seqlens, default_params, dispatch_count, fold_patch_weights, hf_smart_resize,
+    hf_workspace_bytes, last_error, load, make_params, patch_embed, plan_frames, plan_geometry,
+    plan_hf,
+    preprocess_hf_batch, preprocess_batch, rope_inv_freq, rotary_tables, sample_frames,
     set_launch_events, smart_nframes, smart_resize, status_string, video_max_pixels,
     window_index, workspace_bytes,
 )
-from .processor import BatchPlan, plan_batch, plan_media, preprocess, stats255, vit_tables  # noqa: F401
+from .processor import (  # noqa: F401
+    BatchPlan, plan_batch, plan_batch_hf, plan_media, preprocess, preprocess_hf, stats255, vit_tables,
+)

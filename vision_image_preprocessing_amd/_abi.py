@@ -93,6 +93,11 @@ SIGNATURES = {
     "mimo_window_index": ([_I32, _P, _I32, _P, _P, _I64, _P, _SZ, _P], ctypes.c_int),
     "mimo_chunk_seqlens": ([_I32, _P, _P, _I64], _I64),
     "mimo_fold_patch_weights": ([_I32, _P, _P, _P], ctypes.c_int),
+    "mimo_hf_smart_resize": ([_I64, _I64, _P, ctypes.POINTER(_I64), ctypes.POINTER(_I64)], ctypes.c_int),
+    "mimo_plan_hf": ([_I32, _P, _P, _P, _P, _P], ctypes.c_int),
+    "mimo_hf_workspace_bytes": ([_I32, _P], _SZ),
+    "mimo_preprocess_hf_batch": ([_I32, _P, _P, _I64, _P, _P, _I32, _P, _P, _I64, _P, _SZ, _P],
+                                 ctypes.c_int),
     "mimo_patch_embed": ([_I64, _P, _I32, _P, _I32, _P, _I32, _P, _P], ctypes.c_int),
 }
 
@@ -398,3 +403,49 @@ def patch_embed(rows, w, bias=None, out=None, out_dtype: str = "bf16", stream=No
                                    _stream_handle(stream, rows.device))
     _check(code, "patch_embed")
     return out
+
+
+def hf_smart_resize(h: int, w: int, params: MimoParams | None = None):
+    """mimo_hf_smart_resize: the stock Qwen2-VL geometry."""
+    oh, ow = ctypes.c_int64(), ctypes.c_int64()
+    _check(load().mimo_hf_smart_resize(int(h), int(w), ctypes.byref(params) if params else None,
+                                       ctypes.byref(oh), ctypes.byref(ow)), "hf_smart_resize")
+    return oh.value, ow.value
+
+
+def plan_hf(hwc, params: MimoParams | None = None, check: bool = True):
+    """mimo_plan_hf over an [n, 3] (height, width, channels) table."""
+    hwc = np.ascontiguousarray(np.asarray(hwc, dtype=np.int32).reshape(-1, 3))
+    n = hwc.shape[0]
+    desc = np.zeros(n, dtype=IMAGE_DESC_DTYPE)
+    total_rows, total_src = ctypes.c_int64(), ctypes.c_int64()
+    code = load().mimo_plan_hf(n, hwc.ctypes.data, ctypes.byref(params) if params else None,
+                               desc.ctypes.data, ctypes.byref(total_rows), ctypes.byref(total_src))
+    if check:
+        _check(code, "plan_hf")
+    return desc, total_rows.value, total_src.value, code
+
+
+def hf_workspace_bytes(desc: np.ndarray) -> int:
+    desc = np.ascontiguousarray(desc, dtype=IMAGE_DESC_DTYPE)
+    return int(load().mimo_hf_workspace_bytes(desc.shape[0], desc.ctypes.data))
+
+
+def preprocess_hf_batch(desc: np.ndarray, src, mean01, std01, rows=None, rows_col=None,
+                        workspace=None, stream=None):
+    """mimo_preprocess_hf_batch on device tensors (src uint8, rows / rows_col
+    float32 or bf16 [capacity, 1536], workspace uint8)."""
+    desc = np.ascontiguousarray(desc, dtype=IMAGE_DESC_DTYPE)
+    n = desc.shape[0]
+    out = rows if rows is not None else rows_col
+    code_dtype = _dtype_code(out)
+    m = (ctypes.c_float * 3)(*[float(v) for v in mean01])
+    s = (ctypes.c_float * 3)(*[float(v) for v in std01])
+    cap = min(t.shape[0] for t in (rows, rows_col) if t is not None)
+    code = load().mimo_preprocess_hf_batch(
+        n, desc.ctypes.data, src.data_ptr(), src.numel(), m, s, code_dtype,
+        rows.data_ptr() if rows is not None else None,
+        rows_col.data_ptr() if rows_col is not None else None,
+        cap, workspace.data_ptr() if workspace is not None else None,
+        workspace.numel() if workspace is not None else 0, _stream_handle(stream, out.device))
+    _check(code, "preprocess_hf_batch")

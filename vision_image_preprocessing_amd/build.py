@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libmimopre.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["plan.cpp", "runtime.hip", "preprocess.hip", "vit_tables.hip", "patch_embed.hip"]
+SOURCES = ["plan.cpp", "runtime.hip", "preprocess.hip", "vit_tables.hip", "patch_embed.hip", "hf_resize.hip"]
 ARCH = "gfx950"
 
 

@@ -44,7 +44,6 @@ constexpr int kBM = 256, kBN = 256, kBK = 64;
 constexpr int kEmbedThreads = 256;
 constexpr int kWaveM = 128, kWaveN = 128;       // one wave's quarter of the tile
 constexpr int kBlocksM = kWaveM / 32, kBlocksN = kWaveN / 32;
-constexpr int kChunks = kBK / 8;                // 16-byte chunks per LDS row
 constexpr int kGroups = kBM / 8 / (kEmbedThreads / 64);  // 1 KB LDS groups per wave per operand
 constexpr int kFoldSeg = 256;       // contiguous K run of one channel in the folded form
 constexpr int kFoldStride = 512;    // its stride in the row (the tt = 1 plane is skipped)

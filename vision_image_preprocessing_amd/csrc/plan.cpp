@@ -1,9 +1,11 @@
 // plan.cpp -- host-side geometry of the MiMo-V2 pixel path: smart_resize,
-// the per-image plan of a batch, and the column permutation indices.
+// the per-image plan of a batch, and the column permutation indices; the
+// stock Qwen2-VL geometry of the contrast path.
 //
 // Pages: NeMo Automodel "mimo_v2_flash.processing" (smart_resize,
-// get_number_of_image_patches, MimoV2ImageProcessor defaults) and docs.rs
-// "cortiq_engine::mimo_vision" (smart_resize, column_permutation).
+// get_number_of_image_patches, MimoV2ImageProcessor defaults, and the module
+// docstring on the stock processor) and docs.rs "cortiq_engine::mimo_vision"
+// (smart_resize, column_permutation).
 #include <algorithm>
 #include <cfenv>
 #include <cmath>
@@ -79,12 +81,57 @@ int smart_resize_impl(int64_t h, int64_t w, int64_t f, int64_t min_px, int64_t m
     return MIMO_OK;
 }
 
+// The stock Qwen2-VL smart_resize: no short-side upscale; each side is
+// rounded to the factor; a shrink floors each side and clamps it to at
+// least one factor on its own, a grow ceils; the aspect guard always applies.
+int stock_smart_resize_impl(int64_t h, int64_t w, int64_t f, int64_t min_px, int64_t max_px,
+                            double max_aspect, int64_t *oh, int64_t *ow) {
+    const double hd = double(h), wd = double(w), fd = double(f);
+    if (std::max(hd, wd) / std::min(hd, wd) > max_aspect) return MIMO_E_ASPECT;
+    double th = round_ties_even(hd / fd) * fd;
+    double tw = round_ties_even(wd / fd) * fd;
+    if (th * tw > double(max_px)) {
+        const double beta = std::sqrt(hd * wd / double(max_px));
+        th = std::max(fd, std::floor(hd / beta / fd) * fd);
+        tw = std::max(fd, std::floor(wd / beta / fd) * fd);
+    } else if (th * tw < double(min_px)) {
+        const double beta = std::sqrt(double(min_px) / (hd * wd));
+        th = std::ceil(hd * beta / fd) * fd;
+        tw = std::ceil(wd * beta / fd) * fd;
+    }
+    *oh = int64_t(th);
+    *ow = int64_t(tw);
+    return MIMO_OK;
+}
+
 }  // namespace
 }  // namespace mimo
 
 using namespace mimo;
 
 extern "C" {
+
+int mimo_hf_smart_resize(int64_t h, int64_t w, const mimo_params *params, int64_t *out_h,
+                         int64_t *out_w) {
+    clear_error();
+    mimo_params def;
+    mimo_default_params(&def);
+    const mimo_params &p = params ? *params : def;
+    if (!out_h || !out_w) return set_error(MIMO_E_INVALID, "hf_smart_resize: null output pointer");
+    if (!params_ok(p)) return set_error(MIMO_E_INVALID, "hf_smart_resize: invalid parameters");
+    if (h < 1 || w < 1) return set_error(MIMO_E_INVALID, "hf_smart_resize: sides must be >= 1");
+    if (h > (int64_t(1) << 31) || w > (int64_t(1) << 31))
+        return set_error(MIMO_E_TOO_LARGE, "hf_smart_resize: side above 2^31");
+    int64_t oh = 0, ow = 0;
+    const int st = stock_smart_resize_impl(h, w, int64_t(p.patch_size) * p.merge_size, p.min_pixels,
+                                           p.max_pixels, p.max_aspect, &oh, &ow);
+    if (st != MIMO_OK)
+        return set_error(st, "hf_smart_resize: aspect ratio of " + std::to_string(h) + "x" +
+                                 std::to_string(w) + " exceeds max_aspect");
+    *out_h = oh;
+    *out_w = ow;
+    return MIMO_OK;
+}
 
 void mimo_default_params(mimo_params *p) {
     if (!p) return;
@@ -131,10 +178,11 @@ namespace mimo {
 namespace {
 
 // Plans n items (still images or videos).  item(i) gives frames, h, w, c;
-// ceiling(i) the resized-area ceiling for item i.
-template <typename Item, typename Ceiling>
+// ceiling(i) the resized-area ceiling for item i; resize is the geometry
+// (smart_resize_impl, or the stock rules of the contrast path).
+template <typename Item, typename Ceiling, typename Resize>
 int plan_items(int32_t n, Item item, Ceiling ceiling, const mimo_params &p, mimo_image_desc *out,
-               int64_t *total_rows, int64_t *total_src_bytes) {
+               int64_t *total_rows, int64_t *total_src_bytes, Resize resize) {
     const int64_t patch = p.patch_size;
     const int64_t merge = p.merge_size;
     const int64_t temporal = p.temporal_patch_size;
@@ -163,7 +211,7 @@ int plan_items(int32_t n, Item item, Ceiling ceiling, const mimo_params &p, mimo
             msg = "item " + std::to_string(i) + ": side above 2^23 - 1";
         } else {
             int64_t oh = 0, ow = 0;
-            st = smart_resize_impl(h, w, patch * merge, p.min_pixels, max_px, p.max_aspect, &oh, &ow);
+            st = resize(h, w, patch * merge, p.min_pixels, max_px, p.max_aspect, &oh, &ow);
             const int64_t grid_t = (f + temporal - 1) / temporal;
             if (st == MIMO_OK && (oh > kMaxSide || ow > kMaxSide ||
                                   grid_t * (oh / patch) * (ow / patch) > kMaxRowsPerImage)) {
@@ -217,7 +265,29 @@ int mimo_plan_geometry(int32_t n, const int32_t *hwc, const mimo_params *params,
             w = hwc[3 * i + 1];
             c = hwc[3 * i + 2];
         },
-        [&](int32_t) { return p.max_pixels; }, p, out, total_rows, total_src_bytes);
+        [&](int32_t) { return p.max_pixels; }, p, out, total_rows, total_src_bytes,
+        smart_resize_impl);
+}
+
+int mimo_plan_hf(int32_t n, const int32_t *hwc, const mimo_params *params, mimo_image_desc *out,
+                 int64_t *total_rows, int64_t *total_src_bytes) {
+    clear_error();
+    if (n < 0 || (n > 0 && (!hwc || !out)))
+        return set_error(MIMO_E_INVALID, "plan_hf: bad n or null pointer");
+    mimo_params def;
+    mimo_default_params(&def);
+    const mimo_params &p = params ? *params : def;
+    if (!params_ok(p)) return set_error(MIMO_E_INVALID, "plan_hf: invalid parameters");
+    return plan_items(
+        n,
+        [&](int32_t i, int32_t &f, int32_t &h, int32_t &w, int32_t &c) {
+            f = 1;
+            h = hwc[3 * i];
+            w = hwc[3 * i + 1];
+            c = hwc[3 * i + 2];
+        },
+        [&](int32_t) { return p.max_pixels; }, p, out, total_rows, total_src_bytes,
+        stock_smart_resize_impl);
 }
 
 int mimo_plan_frames(int32_t n, const int32_t *fhwc, const int64_t *max_pixels,
@@ -241,7 +311,7 @@ int mimo_plan_frames(int32_t n, const int32_t *fhwc, const int64_t *max_pixels,
         [&](int32_t i) {
             return (max_pixels && max_pixels[i] > 0) ? max_pixels[i] : p.max_pixels;
         },
-        p, out, total_rows, total_src_bytes);
+        p, out, total_rows, total_src_bytes, smart_resize_impl);
 }
 
 int64_t mimo_video_max_pixels(int64_t n_sampled, int64_t total_max, const mimo_params *params) {

@@ -162,3 +162,38 @@ def vit_tables(plan: BatchPlan, device="cuda", column: bool = False, rope_dim: i
         "window_index": index[:rows // 4], "window_inverse": inverse[:rows // 4],
         "cu_seqlens": torch.from_numpy(_abi.chunk_seqlens(plan.desc)),
     }
+
+
+def plan_batch_hf(shapes, min_pixels=None, max_pixels=None, check: bool = True) -> BatchPlan:
+    """Plans images with the stock Qwen2-VL geometry (the contrast path)."""
+    params = _abi.make_params(min_pixels, max_pixels)
+    desc, rows, src, _ = _abi.plan_hf(np.asarray(shapes, dtype=np.int32).reshape(-1, 3), params,
+                                      check=check)
+    return BatchPlan(desc=desc, total_rows=rows, total_src_bytes=src)
+
+
+def preprocess_hf(src_dev, plan: BatchPlan, mean=IMAGENET_MEAN, std=IMAGENET_STD,
+                  out_dtype: str = "f32", merge_order: bool = True, column_order: bool = False,
+                  stream=None, rows=None, rows_col=None, workspace=None):
+    """The stock processor's pixels for a plan from plan_batch_hf (processing page,
+    module docstring: PIL antialiased bicubic to bytes, 0-1 statistics, alpha
+    dropped); same outputs as preprocess()."""
+    import torch
+    dev = src_dev.device
+    tdtype = {"f32": torch.float32, "bf16": torch.bfloat16}[out_dtype]
+    n_rows = max(plan.total_rows, 1)
+    if merge_order and rows is None:
+        rows = torch.empty((n_rows, _abi.ROW_LEN), dtype=tdtype, device=dev)
+    if column_order and rows_col is None:
+        rows_col = torch.empty((n_rows, _abi.ROW_LEN), dtype=tdtype, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(_abi.hf_workspace_bytes(plan.desc), 16), dtype=torch.uint8,
+                                device=dev)
+    _abi.preprocess_hf_batch(plan.desc, src_dev, mean, std, rows=rows if merge_order else None,
+                             rows_col=rows_col if column_order else None, workspace=workspace,
+                             stream=stream)
+    return {
+        "pixel_values": rows if merge_order else None,
+        "pixel_values_col": rows_col if column_order else None,
+        "image_grid_thw": torch.from_numpy(plan.image_grid_thw),
+    }
