@@ -146,6 +146,39 @@ def vit_tables_rates(V, plan, ws, reps: int, rope_dim: int = 32) -> dict:
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 
 
+def hf_contrast_rates(V, batch, plan, src, rows, reps: int) -> dict:
+    """The stock-HF contrast path on the same batch (stills only): kernel
+    time against the same algorithmic bytes as the MiMo kernel (sources read
+    once, rows written once per output), and the pixel shift between the two
+    paths' merge-order rows, in units of the channel standard deviation."""
+    import numpy as np
+    import torch
+
+    stream = torch.cuda.current_stream()
+    plan_h = V.plan_batch_hf(batch.shapes, check=False)
+    if (plan_h.desc["status"] != 0).any() or not np.array_equal(plan_h.image_grid_thw,
+                                                               plan.image_grid_thw):
+        return {"skipped": "the stock geometry refuses or differs from the MiMo one on this batch"}
+    tdtype = rows.dtype
+    out = torch.empty_like(rows)
+    out_col = torch.empty_like(rows) if batch.column_order else None
+    ws = torch.empty(V.hf_workspace_bytes(plan_h.desc), dtype=torch.uint8, device="cuda")
+    call = lambda: V.preprocess_hf(src, plan_h, mean=batch.mean, std=batch.std,
+                                   out_dtype="f32" if tdtype == torch.float32 else "bf16",
+                                   column_order=batch.column_order, rows=out, rows_col=out_col,
+                                   workspace=ws)
+    ms = time_launches(V, call, reps, stream)
+    bpv = 4 if tdtype == torch.float32 else 2
+    alg = plan_h.total_src_bytes + plan_h.total_rows * 1536 * bpv * (2 if batch.column_order else 1)
+    diff = (rows.float() - out.float()).abs()
+    res = {"kernel": "hf_preprocess_kernel", "ms": ms, "algorithmic_bytes": alg,
+           "GB/s": alg / (ms * 1e-3) / 1e9, "frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+           "shift_vs_mimo_std_units": {"mean": float(diff.mean()), "max": float(diff.max())}}
+    del out, out_col, ws, diff
+    torch.cuda.empty_cache()
+    return res
+
+
 def patch_embed_rates(V, batch, plan, src, ws, reps: int, embed_dim: int = 1280) -> dict:
     """The patch embedding (the rows' Conv3d consumer) on the same batch's
     rows emitted in bf16: the full weight (K = 1536) and, for a batch of
@@ -221,6 +254,8 @@ def main():
                     help="skip timing the ViT index-table kernels on the same batch")
     ap.add_argument("--no-embed", action="store_true",
                     help="skip timing the patch embedding on the same batch's rows")
+    ap.add_argument("--no-hf", action="store_true",
+                    help="skip timing the stock-HF contrast path on the same batch")
     ap.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GIB",
                     help="only run a plain copy kernel of this size (counter calibration)")
     args = ap.parse_args()
@@ -361,6 +396,10 @@ def main():
     if not args.no_vit_tables:
         log("vit tables")
         result["vit_tables"] = vit_tables_rates(V, plan, ws, reps=10)
+
+    if not args.no_hf and not batch.is_media:
+        log("stock-HF contrast path")
+        result["hf_contrast"] = hf_contrast_rates(V, batch, plan, src, rows, reps=5)
 
     if not args.no_embed:
         log("patch embed")
