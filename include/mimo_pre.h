@@ -347,9 +347,10 @@ size_t mimo_hf_workspace_bytes(int32_t n, const mimo_image_desc *desc);
  *   mean01, std01  host float[3], statistics in 0-1 units.
  *   workspace      device, >= mimo_hf_workspace_bytes(n, desc), 16-byte aligned.
  * Other arguments as for mimo_preprocess_batch.  Returns MIMO_OK,
- * MIMO_E_INVALID, MIMO_E_CAPACITY, MIMO_E_UNSUPPORTED (a vertical downscale
- * whose taps for one output row exceed 481 source rows), MIMO_E_TOO_LARGE or
- * MIMO_E_HIP.
+ * MIMO_E_INVALID, MIMO_E_CAPACITY, MIMO_E_UNSUPPORTED (a downscale beyond
+ * the kernel's LDS band: one output row's taps over more than 225 source
+ * rows, or one tile's columns over more than 8192 source columns),
+ * MIMO_E_TOO_LARGE or MIMO_E_HIP.
  */
 int mimo_preprocess_hf_batch(int32_t n, const mimo_image_desc *desc, const uint8_t *src,
                              int64_t src_capacity, const float *mean01, const float *std01,

@@ -20,12 +20,14 @@
 // float32); so the kernel is integer up to that lookup and its results are
 // bit-exact.
 //
-// Kernel: one workgroup per merge unit (32 x 32 output pixels).  It runs the
-// horizontal pass for the source rows its vertical taps need into LDS (one
-// dword per pixel, RGB bytes), in groups of output rows sized so the band
-// fits, the vertical pass into a 32 x 32 byte block, then writes the unit's
-// 4 rows (both temporal slots) with 16-byte stores, to merge-block and/or
-// column order.
+// Kernel: one workgroup per merge unit (32 x 32 output pixels), in groups
+// of output rows sized so that the band of source rows their vertical taps
+// need fits LDS.  Per group: the source block the tile's taps touch is
+// staged into LDS (one dword per pixel, RGB bytes; aligned dword buffer
+// loads realigned with v_alignbyte, in row chunks that fit), the horizontal
+// pass reads it from there into the band, the vertical pass turns the band
+// into a 32 x 32 byte block; then the unit's 4 rows (both temporal slots)
+// go out with 16-byte stores, to merge-block and/or column order.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -41,9 +43,12 @@
 namespace mimo {
 namespace {
 
-constexpr int kHfThreads = 256;
+constexpr int kHfThreads = 512;
 constexpr int kWeightBits = 22;           // fractional bits of the resampler's weights
-constexpr int kMidRows = 512;             // LDS band rows (32 pixels each)
+constexpr int kMidRows = 256;             // LDS band rows (32 pixels each)
+constexpr int kStageDwords = 4096;        // LDS source staging (one dword per pixel)
+constexpr int kTapBudget = 2048;          // LDS weights per axis (else they are read from memory)
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer resource word 3 (gfx9 family)
 
 // Per-item record of the contrast kernel (64 bytes).
 struct HfItem {
@@ -61,6 +66,7 @@ static_assert(sizeof(HfItem) == 64, "HfItem must stay 64 bytes");
 
 struct HfArgs {
     const uint8_t *src;
+    int64_t src_end;            // bytes readable from src
     const HfItem *items;
     const int64_t *tile_begin;  // [n + 1]
     const float *lut;           // [3][256]
@@ -80,8 +86,31 @@ __device__ __forceinline__ uint32_t round_clip_byte(int32_t acc) {
     return uint32_t(v < 0 ? 0 : (v > 255 ? 255 : v));
 }
 
-__device__ __forceinline__ uint32_t load_rgb(const uint8_t *p) {
-    return uint32_t(p[0]) | (uint32_t(p[1]) << 8) | (uint32_t(p[2]) << 16);
+// A raw buffer resource over [base & ~3, src_end): reads past the end
+// return zero.  `lead` is base's offset inside it.
+struct SrcWindow {
+    __amdgpu_buffer_rsrc_t rsrc;
+    uint32_t lead;
+};
+
+__device__ __forceinline__ SrcWindow src_window(const HfArgs &a, uint64_t base) {
+    const uint64_t start = base & ~uint64_t(3);
+    const uint64_t end = reinterpret_cast<uint64_t>(a.src) + uint64_t(a.src_end);
+    const uint64_t avail = end > start ? end - start : 0;
+    SrcWindow w;
+    w.rsrc = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(start), 0,
+                                               avail > 0x7FFFFFF0ull ? 0x7FFFFFF0 : int(avail),
+                                               kBufferWord3);
+    w.lead = uint32_t(base - start);
+    return w;
+}
+
+// RGB bytes of the pixel at byte offset `off` of the window (any alignment).
+__device__ __forceinline__ uint32_t load_rgb(const SrcWindow &w, uint32_t off) {
+    const uint32_t al = off & ~3u, sh = off & 3u;
+    const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b32(w.rsrc, int(al), 0, 0);
+    const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b32(w.rsrc, int(al) + 4, 0, 0);
+    return __builtin_amdgcn_alignbyte(hi, lo, sh) & 0x00FFFFFFu;
 }
 
 // One output value of the tile in the final layout: 4 floats (4 pixels of
@@ -110,6 +139,10 @@ __global__ __launch_bounds__(kHfThreads) void hf_preprocess_kernel(HfArgs a) {
     __shared__ float lut[3 * 256];
     __shared__ uint32_t block[kUnitPx * kUnitPx];  // the unit's output bytes (RGB per dword)
     __shared__ uint32_t mid[kMidRows * kUnitPx];   // horizontal-pass band
+    __shared__ uint32_t stage[kStageDwords];       // source pixels of the current row chunk
+    // the tile's taps: first (relative to the staged block / band), count, weights
+    __shared__ int32_t xfirst_s[kUnitPx], xcount_s[kUnitPx], xw_s[kTapBudget];
+    __shared__ int32_t yfirst_s[kUnitPx], ycount_s[kUnitPx], yw_s[kTapBudget];
     const int64_t tile = xcd_contiguous_tile(blockIdx.x, gridDim.x);
     const int img = find_segment(a.tile_begin, a.n, tile);
     const HfItem d = a.items[img];
@@ -126,42 +159,82 @@ __global__ __launch_bounds__(kHfThreads) void hf_preprocess_kernel(HfArgs a) {
     const int32_t *xf = d.kx ? a.taps + d.x_tab : nullptr;  // first[dst_w], count[dst_w], w[dst_w][kx]
     const int32_t *yf = d.ky ? a.taps + d.y_tab : nullptr;
     const int G = d.group;
+    // source columns the tile's 32 output columns read, and their taps in LDS
+    // (the weights too, when they fit; else they are read from memory)
+    const int xlo = xf ? xf[ox0] : ox0;
+    const int xhi = xf ? xf[ox0 + kUnitPx - 1] + xf[dst_w + ox0 + kUnitPx - 1] : ox0 + kUnitPx;
+    const int ncols = xhi - xlo;  // <= kStageDwords (the host checked)
+    const bool xw_in_lds = xf && kUnitPx * d.kx <= kTapBudget;
+    if (xf) {
+        for (int i = tid; i < kUnitPx; i += kHfThreads) {
+            xfirst_s[i] = xf[ox0 + i] - xlo;
+            xcount_s[i] = xf[dst_w + ox0 + i];
+        }
+        if (xw_in_lds)
+            for (int i = tid; i < kUnitPx * d.kx; i += kHfThreads)
+                xw_s[i] = xf[2 * dst_w + int64_t(ox0) * d.kx + i];
+    }
+    const bool yw_in_lds = yf && G * d.ky <= kTapBudget;
     for (int g0 = 0; g0 < kUnitPx; g0 += G) {
         const int oy_a = oy0 + g0, oy_b = oy_a + G - 1;
         const int ylo = yf ? yf[oy_a] : oy_a;
         const int yhi = yf ? yf[oy_b] + yf[dst_h + oy_b] : oy_b + 1;
         const int nrows = yhi - ylo;  // <= kMidRows (the host sized G)
-        // horizontal pass (or a copy) for band rows [ylo, yhi) x the unit's 32 columns
-        for (int idx = tid; idx < nrows * kUnitPx; idx += kHfThreads) {
-            const int r = idx >> 5, x = idx & 31;
-            const uint8_t *line = img_src + int64_t(ylo + r) * row_bytes;
-            const int ox = ox0 + x;
-            uint32_t px;
-            if (xf) {
-                const int first = xf[ox], count = xf[dst_w + ox];
-                const int32_t *w = xf + 2 * dst_w + int64_t(ox) * d.kx;
-                int32_t acc0 = 0, acc1 = 0, acc2 = 0;
-                for (int j = 0; j < count; ++j) {
-                    const uint8_t *p = line + int64_t(first + j) * d.channels;
-                    acc0 += int32_t(p[0]) * w[j];
-                    acc1 += int32_t(p[1]) * w[j];
-                    acc2 += int32_t(p[2]) * w[j];
-                }
-                px = round_clip_byte(acc0) | (round_clip_byte(acc1) << 8) | (round_clip_byte(acc2) << 16);
-            } else {
-                px = load_rgb(line + int64_t(ox) * d.channels);
+        if (yf) {
+            for (int i = tid; i < G; i += kHfThreads) {
+                yfirst_s[i] = yf[oy_a + i] - ylo;
+                ycount_s[i] = yf[dst_h + oy_a + i];
             }
-            mid[idx] = px;
+            if (yw_in_lds)
+                for (int i = tid; i < G * d.ky; i += kHfThreads)
+                    yw_s[i] = yf[2 * dst_h + int64_t(oy_a) * d.ky + i];
         }
-        __syncthreads();
+        const int chunk = min(nrows, kStageDwords / ncols);
+        const float inv_ncols = 1.0f / float(ncols);
+        for (int r0 = 0; r0 < nrows; r0 += chunk) {
+            const int nr = min(chunk, nrows - r0);
+            // stage source rows [ylo + r0, ylo + r0 + nr) x [xlo, xhi)
+            const SrcWindow win = src_window(a, reinterpret_cast<uint64_t>(img_src) +
+                                                    uint64_t(int64_t(ylo + r0) * row_bytes +
+                                                             int64_t(xlo) * d.channels));
+            for (int idx = tid; idx < nr * ncols; idx += kHfThreads) {
+                const int r = div_small(idx, ncols, inv_ncols);
+                const int c = idx - r * ncols;
+                stage[idx] = load_rgb(win, win.lead + uint32_t(int64_t(r) * row_bytes + c * d.channels));
+            }
+            __syncthreads();
+            // horizontal pass (or a copy) into band rows [r0, r0 + nr)
+            for (int idx = tid; idx < nr * kUnitPx; idx += kHfThreads) {
+                const int r = idx >> 5, x = idx & 31;
+                const uint32_t *line = &stage[r * ncols];
+                uint32_t px;
+                if (xf) {
+                    const int first = xfirst_s[x], count = xcount_s[x];
+                    const int32_t *w = xw_in_lds ? &xw_s[x * d.kx]
+                                                 : xf + 2 * dst_w + int64_t(ox0 + x) * d.kx;
+                    int32_t acc0 = 0, acc1 = 0, acc2 = 0;
+                    for (int j = 0; j < count; ++j) {
+                        const uint32_t p = line[first + j];
+                        acc0 += int32_t(p & 255u) * w[j];
+                        acc1 += int32_t((p >> 8) & 255u) * w[j];
+                        acc2 += int32_t((p >> 16) & 255u) * w[j];
+                    }
+                    px = round_clip_byte(acc0) | (round_clip_byte(acc1) << 8) | (round_clip_byte(acc2) << 16);
+                } else {
+                    px = line[x];
+                }
+                mid[(r0 + r) * kUnitPx + x] = px;
+            }
+            __syncthreads();
+        }
         // vertical pass (or a copy) for output rows [oy_a, oy_b]
         for (int idx = tid; idx < G * kUnitPx; idx += kHfThreads) {
             const int r = idx >> 5, x = idx & 31;
             const int oy = oy_a + r;
             uint32_t px;
             if (yf) {
-                const int first = yf[oy] - ylo, count = yf[dst_h + oy];
-                const int32_t *w = yf + 2 * dst_h + int64_t(oy) * d.ky;
+                const int first = yfirst_s[r], count = ycount_s[r];
+                const int32_t *w = yw_in_lds ? &yw_s[r * d.ky] : yf + 2 * dst_h + int64_t(oy) * d.ky;
                 int32_t acc0 = 0, acc1 = 0, acc2 = 0;
                 for (int j = 0; j < count; ++j) {
                     const uint32_t p = mid[(first + j) * kUnitPx + x];
@@ -308,7 +381,9 @@ int build_hf_tables(int32_t n, const mimo_image_desc *desc, const float *mean01,
             s.rows != int64_t(s.grid_h) * s.grid_w || s.row_offset != rows || s.src_offset < 0)
             return set_error(MIMO_E_INVALID, "preprocess_hf: descriptor " + std::to_string(i) +
                                                  " is not a still-image plan of the 16/2/2 kernels");
-        if (s.src_h > kMaxSide || s.src_w > kMaxSide || s.dst_h > kMaxSide || s.dst_w > kMaxSide)
+        // the staging window addresses up to kMidRows source rows with 32-bit offsets
+        if (s.src_h > kMaxSide || s.src_w > kMaxSide || s.dst_h > kMaxSide || s.dst_w > kMaxSide ||
+            int64_t(s.src_w) * s.channels * (kMidRows + 1) >= 0x7FFFFFF0ll)
             return set_error(MIMO_E_TOO_LARGE, "preprocess_hf: descriptor " + std::to_string(i) + ": side too large");
         d.src_h = s.src_h;
         d.src_w = s.src_w;
@@ -330,6 +405,17 @@ int build_hf_tables(int32_t n, const mimo_image_desc *desc, const float *mean01,
             if (d.group == 0)
                 return set_error(MIMO_E_UNSUPPORTED, "preprocess_hf: descriptor " + std::to_string(i) +
                                                          ": vertical downscale beyond the kernel's band");
+        }
+        if (d.kx) {
+            // the widest source block one tile's 32 output columns read
+            const int32_t *xfirst = out.taps.data() + d.x_tab;
+            const int32_t *xcount = xfirst + s.dst_w;
+            for (int32_t x0 = 0; x0 < s.dst_w; x0 += kUnitPx) {
+                const int32_t x1 = x0 + kUnitPx - 1;
+                if (xfirst[x1] + xcount[x1] - xfirst[x0] > kStageDwords)
+                    return set_error(MIMO_E_UNSUPPORTED, "preprocess_hf: descriptor " + std::to_string(i) +
+                                                             ": horizontal downscale beyond the kernel's staging");
+            }
         }
         items[i] = d;
         tiles += int64_t(d.blocks_h) * d.blocks_w;
@@ -412,6 +498,7 @@ int mimo_preprocess_hf_batch(int32_t n, const mimo_image_desc *desc, const uint8
     if (e != hipSuccess) return hip_error(e, "preprocess_hf: table upload");
     HfArgs a;
     a.src = src;
+    a.src_end = src_capacity;
     a.items = reinterpret_cast<const HfItem *>(ws);
     a.tile_begin = reinterpret_cast<const int64_t *>(ws + hf_items_bytes(n));
     a.lut = reinterpret_cast<const float *>(ws + hf_items_bytes(n) + hf_prefix_bytes(n));
