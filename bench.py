@@ -89,8 +89,9 @@ def cpu_baseline(batch, plan, sample: int, threads: int) -> dict:
     unit = "frames/s" if batch.is_media else "images/s"
     what = "clips" if batch.is_media else "images"
     return {"value": units / dt, "unit": unit, "cores": threads, "kind": "oracle",
-            "sample": f"first {len(idx)} of {len(batch)} {what} of the same batch ({units} "
-                      f"{unit[:-2]}), one item per thread, {threads} threads, {dt:.2f} s wall",
+            "sample": f"first {len(idx)} of {len(batch)} {what} of the same batch"
+                      + (f" ({units} frames)" if batch.is_media else "")
+                      + f", one item per thread, {threads} threads, {dt:.2f} s wall",
             "seconds": dt, "cpu_model": platform.processor() or platform.machine()}
 
 

@@ -348,8 +348,9 @@ size_t mimo_hf_workspace_bytes(int32_t n, const mimo_image_desc *desc);
  *   workspace      device, >= mimo_hf_workspace_bytes(n, desc), 16-byte aligned.
  * Other arguments as for mimo_preprocess_batch.  Returns MIMO_OK,
  * MIMO_E_INVALID, MIMO_E_CAPACITY, MIMO_E_UNSUPPORTED (a downscale beyond
- * the kernel's LDS band: one output row's taps over more than 225 source
- * rows, or one tile's columns over more than 8192 source columns),
+ * the kernel's LDS band: one output row's taps over more than 256 source
+ * rows, or one tile's 32 output columns over more than 4096 source
+ * columns),
  * MIMO_E_TOO_LARGE or MIMO_E_HIP.
  */
 int mimo_preprocess_hf_batch(int32_t n, const mimo_image_desc *desc, const uint8_t *src,

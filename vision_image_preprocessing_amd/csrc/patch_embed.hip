@@ -20,14 +20,16 @@
 // per matrix-core flop at (128 + 128) / (128 * 128) of a 16-wide k step.  K
 // advances 64 at a time through double-buffered LDS; rows are 128 bytes and
 // their eight 16-byte chunks are XOR-swizzled by the row index, so the
-// fragment reads of 16 consecutive rows hit distinct banks.  Operand
-// tiles go from global memory straight into LDS (global_load_lds_dwordx4,
-// no register staging): while the waves multiply one stage, the next
-// stage's loads fill the other buffer.  W is the MFMA's first operand, so
-// each lane ends with four consecutive output columns of one row, stored as
-// one 16-byte (float32) or 8-byte (bf16) write.  Tiles are ordered N fastest
-// and assigned to XCDs in contiguous runs, so one XCD's L2 serves an A tile
-// to all of its N tiles, and W (<= 4 MB) stays L2-resident.
+// fragment reads of 16 consecutive rows hit distinct banks.  Operand tiles
+// go from global memory straight into LDS (global_load_lds_dwordx4, no
+// register staging); the next stage's loads are spread between the MFMAs of
+// the current one, and a dword touch of each A line three stages ahead
+// pulls the A panel into L2 before the tiles sharing it ask for it.  The
+// tile is written back through LDS so that every store covers whole row
+// segments (non-temporal, 16 bytes per lane); W is the MFMA's first operand,
+// which gives each lane four consecutive output columns to stage.  Tiles are
+// ordered N fastest and assigned to XCDs in contiguous runs, so one XCD's L2
+// serves an A tile to all of its N tiles.
 #include <hip/hip_runtime.h>
 
 #include <cstring>
@@ -45,6 +47,7 @@ constexpr int kEmbedThreads = 256;
 constexpr int kWaveM = 128, kWaveN = 128;       // one wave's quarter of the tile
 constexpr int kBlocksM = kWaveM / 32, kBlocksN = kWaveN / 32;
 constexpr int kGroups = kBM / 8 / (kEmbedThreads / 64);  // 1 KB LDS groups per wave per operand
+constexpr int kPrefetchAhead = 3;  // stages between an L2 prefetch of A and its real load
 constexpr int kFoldSeg = 256;       // contiguous K run of one channel in the folded form
 constexpr int kFoldStride = 512;    // its stride in the row (the tt = 1 plane is skipped)
 
@@ -70,7 +73,7 @@ __device__ __forceinline__ int a_column(int k0, bool folded) {
     return folded ? (k0 / kFoldSeg) * kFoldStride + k0 % kFoldSeg : k0;
 }
 
-// Four consecutive outputs of one row.
+// Four consecutive outputs of one row (into the LDS staging area).
 __device__ __forceinline__ void store_out4(float *p, const f32x4 &v) {
     *reinterpret_cast<f32x4 *>(p) = v;
 }
@@ -88,13 +91,20 @@ __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 // LDS offset (in bf16) of logical 16-byte chunk v of row r.
 __device__ __forceinline__ int lds_at(int r, int v) { return r * kBK + ((v ^ swz(r)) << 3); }
 
+// s_waitcnt immediates (gfx9 layout: vmcnt in bits 3:0 and 15:14, expcnt
+// in 6:4, lgkmcnt in 11:8; a field at its maximum does not wait).
+constexpr int kWaitAll = 0;                 // every counter at zero
+constexpr int kWaitVmemButOne = 0x0F71;     // vmcnt(1) only
+
 template <typename OutT>
 __global__ __launch_bounds__(kEmbedThreads) void patch_embed_kernel(EmbedArgs a) {
     // Two LDS stages as four distinct arrays: the compiler then sees that the
     // loads filling one stage never alias the reads of the other, and does
-    // not make those reads wait for the loads in flight.
+    // not make those reads wait for the loads in flight.  The sink takes the
+    // L2 prefetches and is never read.
     __shared__ uint16_t sa0[kBM * kBK], sa1[kBM * kBK];
     __shared__ uint16_t sb0[kBN * kBK], sb1[kBN * kBK];
+    __shared__ uint32_t sink[kEmbedThreads];
     const int64_t tile = xcd_contiguous_tile(blockIdx.x, gridDim.x);
     const int64_t mt = tile / a.n_tiles;
     const int nt = int(tile - mt * a.n_tiles);
@@ -104,12 +114,13 @@ __global__ __launch_bounds__(kEmbedThreads) void patch_embed_kernel(EmbedArgs a)
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;  // the wave's quarter
     const bool folded = a.folded != 0;
+    const int stages = a.k / kBK;
 
     // Global -> LDS loads of one stage: 256 rows x 64 k of A and of W.  Wave
     // w fills LDS row groups [8 kGroups w, 8 kGroups (w + 1)); within a 1 KB
     // group lane l lands at row l / 8, physical chunk l % 8, so it fetches
-    // the logical chunk (l % 8) ^ swz(row) of its row.  Rows
-    // past n_rows read the last row instead; their results are never stored.
+    // the logical chunk (l % 8) ^ swz(row) of its row.  Rows past n_rows
+    // read the last row instead; their results are never stored.
     const uint16_t *a_src[kGroups];
     const uint16_t *w_src[kGroups];
 #pragma unroll
@@ -120,17 +131,38 @@ __global__ __launch_bounds__(kEmbedThreads) void patch_embed_kernel(EmbedArgs a)
         a_src[i] = a.rows + row * kRowLen + v * 8;
         w_src[i] = a.w + int64_t(n0 + r) * a.k + v * 8;
     }
-    auto load_stage = [&](int k0, uint16_t *da, uint16_t *db) {
-        const int acol = a_column(k0, folded);
-#pragma unroll
-        for (int i = 0; i < kGroups; ++i) {
-            const int g = wave * kGroups + i;
-            __builtin_amdgcn_global_load_lds(a_src[i] + acol, (lds_void_ptr)(da + g * 8 * kBK), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(w_src[i] + k0, (lds_void_ptr)(db + g * 8 * kBK), 16, 0, 0);
-        }
+    // Load number l (0 .. 2 kGroups - 1) of a stage: A group l / 2 for even
+    // l, W group l / 2 for odd l.
+    auto load_one = [&](int l, int k0, int acol, uint16_t *da, uint16_t *db) {
+        const int grp = l >> 1;
+        const int g = wave * kGroups + grp;
+        if ((l & 1) == 0)
+            __builtin_amdgcn_global_load_lds(a_src[grp] + acol, (lds_void_ptr)(da + g * 8 * kBK), 16, 0, 0);
+        else
+            __builtin_amdgcn_global_load_lds(w_src[grp] + k0, (lds_void_ptr)(db + g * 8 * kBK), 16, 0, 0);
     };
-    // every direct load of this thread has landed in LDS
-    auto wait_loads = [] { __builtin_amdgcn_s_waitcnt(0); };
+    // L2 prefetch: during stage s, thread t touches the 128-byte line of A
+    // row t that stage s + kPrefetchAhead reads (one dword into the sink),
+    // two stages before that stage's real loads go out, so they and the
+    // other tiles sharing the A panel find it in L2.  Past the last stage it
+    // touches a line of the last stage again.
+    static_assert(kEmbedThreads == kBM, "one prefetched A row per thread");
+    const int64_t pf_row = m0 + tid < a.n_rows ? m0 + tid : a.n_rows - 1;
+    const uint16_t *pf_base = a.rows + pf_row * kRowLen;
+    auto prefetch = [&](int s) {  // s: the stage whose line is touched
+        __builtin_amdgcn_global_load_lds(pf_base + a_column(min(s, stages - 1) * kBK, folded),
+                                         (lds_void_ptr)(sink + wave * 64), 4, 0, 0);
+    };
+    // The barrier between stages.  __syncthreads would add a fence that
+    // waits for every load in flight, the prefetch included; each thread has
+    // already waited for its own stage loads (kWaitVmemButOne: the prefetch
+    // is its newest vector memory operation), and LDS-DMA data counts as
+    // written once vmcnt has passed it.
+    auto barrier = [] {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
 
     f32x16 acc[kBlocksM][kBlocksN];
 #pragma unroll
@@ -138,10 +170,13 @@ __global__ __launch_bounds__(kEmbedThreads) void patch_embed_kernel(EmbedArgs a)
 #pragma unroll
         for (int j = 0; j < kBlocksN; ++j) acc[i][j] = f32x16{};
 
-    const int stages = a.k / kBK;
-    load_stage(0, sa0, sb0);
-    wait_loads();
-    __syncthreads();
+    {
+        const int acol0 = a_column(0, folded);
+#pragma unroll
+        for (int l = 0; l < 2 * kGroups; ++l) load_one(l, 0, acol0, sa0, sb0);
+        __builtin_amdgcn_s_waitcnt(kWaitAll);
+        barrier();
+    }
     // MFMA operand rows of this lane: A block i covers C rows wm*128 + i*32 +
     // (lane % 32); B block j covers C columns wn*128 + j*32 + (lane % 32);
     // the lane supplies k = 8 * (lane / 32) .. + 7 of each 16-wide k step.
@@ -160,11 +195,16 @@ __global__ __launch_bounds__(kEmbedThreads) void patch_embed_kernel(EmbedArgs a)
                 &tb[lds_at(wn * kWaveN + j * 32 + frag_row, 2 * ks + frag_chunk)]);
     };
     constexpr int kSteps = kBK / 16;
-    // One stage: start filling the other LDS stage with stage s + 1, multiply
-    // this one (the next k step's fragments are read while this step's
-    // MFMAs run), then wait for the loads and for every wave.
+    static_assert(kSteps * kBlocksM == 2 * kGroups, "one stage load after each row of MFMA blocks");
+    // One stage: multiply this LDS stage (the next k step's fragments are
+    // read while this step's MFMAs run) while the next stage's loads go out
+    // one after each row of four MFMAs (issued in a burst they would hold the
+    // wave at issue), the prefetch last; then wait for all but the prefetch,
+    // and for every wave.
     auto stage = [&](int s, const uint16_t *ta, const uint16_t *tb, uint16_t *na, uint16_t *nb) {
-        if (s + 1 < stages) load_stage((s + 1) * kBK, na, nb);
+        const bool more = s + 1 < stages;
+        const int k1 = (s + 1) * kBK;
+        const int acol1 = a_column(more ? k1 : 0, folded);
         bf16x8 fa[2][kBlocksM], fb[2][kBlocksN];
         read_frags(ta, tb, 0, fa[0], fb[0]);
 #pragma unroll
@@ -174,41 +214,65 @@ __global__ __launch_bounds__(kEmbedThreads) void patch_embed_kernel(EmbedArgs a)
             // otherwise sink each read to its first use and expose its latency)
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < kBlocksM; ++i)
+            for (int i = 0; i < kBlocksM; ++i) {
 #pragma unroll
                 for (int j = 0; j < kBlocksN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks & 1][j], fa[ks & 1][i],
                                                                         acc[i][j], 0, 0, 0);
+                const int l = ks * kBlocksM + i;
+                if (more) load_one(l, k1, acol1, na, nb);
+                if (l == 2 * kGroups - 1) prefetch(s + kPrefetchAhead);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-        wait_loads();
-        __syncthreads();
+        __builtin_amdgcn_s_waitcnt(kWaitVmemButOne);
+        barrier();
     };
     // stages is even (1536 / 64 or 768 / 64), so stages alternate in pairs
     for (int s = 0; s < stages; s += 2) {
         stage(s, sa0, sb0, sa1, sb1);
         stage(s + 1, sa1, sb1, sa0, sb0);
     }
+    __builtin_amdgcn_s_waitcnt(kWaitAll);  // the last prefetch, before LDS is reused
 
-    // Epilogue.  With W as the first operand, value q of block (i, j) is
-    // output row (lane % 32) of A block i and column 8 * (q / 4) +
-    // 4 * (lane / 32) + q % 4 of W block j: four consecutive columns per
-    // group q / 4.
+    // Epilogue through LDS, free now that every wave has passed the last
+    // stage's barrier.  Each wave stages its 128 x 128 block 32 rows at a
+    // time in a private region (one of the four stage arrays), then writes
+    // whole row segments, 16 bytes per lane, with non-temporal stores.  With
+    // W as the first operand, value q of block (i, j) is row (lane % 32) of
+    // A block i and column 8 * (q / 4) + 4 * (lane / 32) + q % 4 of W block j.
     OutT *out = static_cast<OutT *>(a.out);
     const bool full_tile = m0 + kBM <= a.n_rows;
+    constexpr int kRowBytes = kWaveN * int(sizeof(OutT));  // one staged row
+    constexpr int kStride = kRowBytes + 16;                // padded against bank conflicts
+    constexpr int kLanesPerRow = kRowBytes / 16;
+    constexpr int kRowsPerPass = 64 / kLanesPerRow;
+    static_assert(32 * kStride <= kBM * kBK * 2, "a wave's staging fits one stage array");
+    uint8_t *region = reinterpret_cast<uint8_t *>(wave == 0 ? sa0 : wave == 1 ? sa1 : wave == 2 ? sb0 : sb1);
+    const int col0 = n0 + wn * kWaveN;
 #pragma unroll
     for (int i = 0; i < kBlocksM; ++i) {
-        const int64_t row = m0 + wm * kWaveM + i * 32 + (lane & 31);
-        if (!full_tile && row >= a.n_rows) continue;
 #pragma unroll
         for (int j = 0; j < kBlocksN; ++j)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int col = n0 + wn * kWaveN + j * 32 + 8 * g + 4 * (lane >> 5);
+                const int c = j * 32 + 8 * g + 4 * (lane >> 5);
                 f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                            acc[i][j][4 * g + 3]};
-                if (a.bias) v += *reinterpret_cast<const f32x4 *>(a.bias + col);
-                store_out4(out + row * a.embed_dim + col, v);
+                if (a.bias) v += *reinterpret_cast<const f32x4 *>(a.bias + col0 + c);
+                store_out4(reinterpret_cast<OutT *>(region + (lane & 31) * kStride) + c, v);
             }
+#pragma unroll
+        for (int p = 0; p < 32 / kRowsPerPass; ++p) {
+            const int r = p * kRowsPerPass + lane / kLanesPerRow;
+            const int chunk = lane % kLanesPerRow;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(region + r * kStride + chunk * 16);
+            const int64_t row = m0 + wm * kWaveM + i * 32 + r;
+            if (full_tile || row < a.n_rows)
+                __builtin_nontemporal_store(
+                    v, reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(out + row * a.embed_dim + col0) +
+                                                 chunk * 16));
+        }
     }
 }
 
