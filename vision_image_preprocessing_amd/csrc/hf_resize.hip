@@ -20,14 +20,18 @@
 // float32); so the kernel is integer up to that lookup and its results are
 // bit-exact.
 //
-// Kernel: one workgroup per merge unit (32 x 32 output pixels), in groups
-// of output rows sized so that the band of source rows their vertical taps
-// need fits LDS.  Per group: the source block the tile's taps touch is
-// staged into LDS (one dword per pixel, RGB bytes; aligned dword buffer
-// loads realigned with v_alignbyte, in row chunks that fit), the horizontal
-// pass reads it from there into the band, the vertical pass turns the band
-// into a 32 x 32 byte block; then the unit's 4 rows (both temporal slots)
-// go out with 16-byte stores, to merge-block and/or column order.
+// Kernel: one workgroup per merge unit (32 x 32 output pixels).  A unit
+// that neither axis resizes reads its source pixels straight into the
+// output block.  Otherwise it works in groups of output rows sized so that
+// the band of source rows their vertical taps need fits LDS.  Per group:
+// the source block the tile's taps touch is staged into LDS (one dword per
+// pixel, RGB bytes; 4 pixels per load, realigned with v_alignbyte, in row
+// chunks that fit), the horizontal pass reads it from there into the band,
+// the vertical pass turns the band into a 32 x 32 byte block; then the
+// unit's 4 rows (both temporal slots) go out with 16-byte stores, to
+// merge-block and/or column order.  The LDS is dynamic, sized by the host
+// for the batch's widest band, staging and tap tables, so that batches of
+// mild resizes keep several workgroups on each CU.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -43,11 +47,15 @@
 namespace mimo {
 namespace {
 
-constexpr int kHfThreads = 512;
+#ifndef MIMO_HF_THREADS
+#define MIMO_HF_THREADS 512
+#endif
+constexpr int kHfThreads = MIMO_HF_THREADS;
 constexpr int kWeightBits = 22;           // fractional bits of the resampler's weights
-constexpr int kMidRows = 256;             // LDS band rows (32 pixels each)
-constexpr int kStageDwords = 4096;        // LDS source staging (one dword per pixel)
-constexpr int kTapBudget = 2048;          // LDS weights per axis (else they are read from memory)
+constexpr int kMidRows = 256;             // most LDS band rows (32 pixels each)
+constexpr int kStageDwords = 4096;        // most LDS source staging (one dword per pixel)
+constexpr int kTapBudget = 2048;          // most LDS weights per axis (else they are read from memory)
+constexpr int kFixedDwords = 3 * 256 + kUnitPx * kUnitPx + 4 * kUnitPx;  // lut, block, first/count
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer resource word 3 (gfx9 family)
 
 // Per-item record of the contrast kernel (64 bytes).
@@ -74,6 +82,9 @@ struct HfArgs {
     void *rows;                 // merge-block order, nullable
     void *rows_col;             // column order, nullable
     int32_t n;
+    // dynamic LDS, sized for the batch (dwords, each a multiple of 4):
+    // [fixed][x weights][y weights][band mid_rows x 32][stage]
+    int32_t xw_budget, yw_budget, mid_rows, stage_dwords;
 };
 
 // workspace: [HfItem x n][int64 tile_begin x (n+1)][float lut x 768][int32 taps]
@@ -105,12 +116,37 @@ __device__ __forceinline__ SrcWindow src_window(const HfArgs &a, uint64_t base) 
     return w;
 }
 
-// RGB bytes of the pixel at byte offset `off` of the window (any alignment).
-__device__ __forceinline__ uint32_t load_rgb(const SrcWindow &w, uint32_t off) {
+// RGB bytes of the four consecutive pixels at byte offset `off` of the
+// window (any alignment), one pixel per dword; alpha is dropped.  One
+// 12-byte (RGB) or 16-byte (RGBA) load when `off` is dword aligned, else a
+// 16-byte load (plus a dword for RGBA) realigned with v_alignbyte.
+__device__ __forceinline__ void load_quad(const SrcWindow &w, uint32_t off, int channels, u32x4 &p) {
     const uint32_t al = off & ~3u, sh = off & 3u;
-    const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b32(w.rsrc, int(al), 0, 0);
-    const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b32(w.rsrc, int(al) + 4, 0, 0);
-    return __builtin_amdgcn_alignbyte(hi, lo, sh) & 0x00FFFFFFu;
+    if (channels == 3) {
+        uint32_t u0, u1, u2;
+        if (sh == 0) {
+            const u32x3 v = __builtin_bit_cast(u32x3, __builtin_amdgcn_raw_buffer_load_b96(w.rsrc, int(al), 0, 0));
+            u0 = v.x; u1 = v.y; u2 = v.z;
+        } else {
+            const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.rsrc, int(al), 0, 0));
+            u0 = __builtin_amdgcn_alignbyte(v.y, v.x, sh);
+            u1 = __builtin_amdgcn_alignbyte(v.z, v.y, sh);
+            u2 = __builtin_amdgcn_alignbyte(v.w, v.z, sh);
+        }
+        // bytes R0 G0 B0 R1 | G1 B1 R2 G2 | B2 R3 G3 B3 -> one pixel per dword
+        p.x = u0 & 0x00FFFFFFu;
+        p.y = __builtin_amdgcn_perm(u1, u0, 0x0C050403u);
+        p.z = __builtin_amdgcn_perm(u2, u1, 0x0C040302u);
+        p.w = u2 >> 8;
+    } else {
+        u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.rsrc, int(al), 0, 0));
+        if (sh != 0) {
+            const uint32_t v4 = __builtin_amdgcn_raw_buffer_load_b32(w.rsrc, int(al) + 16, 0, 0);
+            v = {__builtin_amdgcn_alignbyte(v.y, v.x, sh), __builtin_amdgcn_alignbyte(v.z, v.y, sh),
+                 __builtin_amdgcn_alignbyte(v.w, v.z, sh), __builtin_amdgcn_alignbyte(v4, v.w, sh)};
+        }
+        p = v & 0x00FFFFFFu;
+    }
 }
 
 // One output value of the tile in the final layout: 4 floats (4 pixels of
@@ -136,13 +172,18 @@ __device__ __forceinline__ void store_pair<uint16_t>(uint16_t *p, const float (&
 
 template <typename OutT>
 __global__ __launch_bounds__(kHfThreads) void hf_preprocess_kernel(HfArgs a) {
-    __shared__ float lut[3 * 256];
-    __shared__ uint32_t block[kUnitPx * kUnitPx];  // the unit's output bytes (RGB per dword)
-    __shared__ uint32_t mid[kMidRows * kUnitPx];   // horizontal-pass band
-    __shared__ uint32_t stage[kStageDwords];       // source pixels of the current row chunk
-    // the tile's taps: first (relative to the staged block / band), count, weights
-    __shared__ int32_t xfirst_s[kUnitPx], xcount_s[kUnitPx], xw_s[kTapBudget];
-    __shared__ int32_t yfirst_s[kUnitPx], ycount_s[kUnitPx], yw_s[kTapBudget];
+    // LDS, sized by the host for the batch (see HfArgs)
+    extern __shared__ uint32_t lds[];
+    float *lut = reinterpret_cast<float *>(lds);                     // [3][256]
+    uint32_t *block = lds + 3 * 256;                                  // the unit's output bytes (RGB per dword)
+    int32_t *xfirst_s = reinterpret_cast<int32_t *>(block + kUnitPx * kUnitPx);  // the tile's taps: first
+    int32_t *xcount_s = xfirst_s + kUnitPx;                           // (relative to the staged block /
+    int32_t *yfirst_s = xcount_s + kUnitPx;                           // band), count, weights
+    int32_t *ycount_s = yfirst_s + kUnitPx;
+    int32_t *xw_s = reinterpret_cast<int32_t *>(lds + kFixedDwords);
+    int32_t *yw_s = xw_s + a.xw_budget;
+    uint32_t *mid = reinterpret_cast<uint32_t *>(yw_s + a.yw_budget);  // horizontal-pass band
+    uint32_t *stage = mid + a.mid_rows * kUnitPx;                     // source pixels of a row chunk
     const int64_t tile = xcd_contiguous_tile(blockIdx.x, gridDim.x);
     const int img = find_segment(a.tile_begin, a.n, tile);
     const HfItem d = a.items[img];
@@ -155,6 +196,18 @@ __global__ __launch_bounds__(kHfThreads) void hf_preprocess_kernel(HfArgs a) {
 
     const uint8_t *img_src = a.src + d.src_offset;
     const int64_t row_bytes = int64_t(d.src_w) * d.channels;
+    if (!d.kx && !d.ky) {
+        // no resize: the unit's 32 x 32 source pixels go straight to the block
+        const SrcWindow win = src_window(a, reinterpret_cast<uint64_t>(img_src) +
+                                                uint64_t(int64_t(oy0) * row_bytes + int64_t(ox0) * d.channels));
+        for (int idx = tid; idx < kUnitPx * kUnitPx / 4; idx += kHfThreads) {
+            const int r = idx >> 3, q = idx & 7;
+            u32x4 px;
+            load_quad(win, win.lead + uint32_t(int64_t(r) * row_bytes + 4 * q * d.channels), d.channels, px);
+            *reinterpret_cast<u32x4 *>(&block[r * kUnitPx + 4 * q]) = px;
+        }
+        __syncthreads();
+    } else {
     const int dst_w = d.blocks_w * kUnitPx, dst_h = d.blocks_h * kUnitPx;
     const int32_t *xf = d.kx ? a.taps + d.x_tab : nullptr;  // first[dst_w], count[dst_w], w[dst_w][kx]
     const int32_t *yf = d.ky ? a.taps + d.y_tab : nullptr;
@@ -163,8 +216,9 @@ __global__ __launch_bounds__(kHfThreads) void hf_preprocess_kernel(HfArgs a) {
     // (the weights too, when they fit; else they are read from memory)
     const int xlo = xf ? xf[ox0] : ox0;
     const int xhi = xf ? xf[ox0 + kUnitPx - 1] + xf[dst_w + ox0 + kUnitPx - 1] : ox0 + kUnitPx;
-    const int ncols = xhi - xlo;  // <= kStageDwords (the host checked)
-    const bool xw_in_lds = xf && kUnitPx * d.kx <= kTapBudget;
+    const int quads = (xhi - xlo + 3) >> 2;  // staged 4 pixels at a time
+    const int spitch = 4 * quads;             // <= a.stage_dwords (the host checked)
+    const bool xw_in_lds = xf && kUnitPx * d.kx <= a.xw_budget;
     if (xf) {
         for (int i = tid; i < kUnitPx; i += kHfThreads) {
             xfirst_s[i] = xf[ox0 + i] - xlo;
@@ -174,12 +228,12 @@ __global__ __launch_bounds__(kHfThreads) void hf_preprocess_kernel(HfArgs a) {
             for (int i = tid; i < kUnitPx * d.kx; i += kHfThreads)
                 xw_s[i] = xf[2 * dst_w + int64_t(ox0) * d.kx + i];
     }
-    const bool yw_in_lds = yf && G * d.ky <= kTapBudget;
+    const bool yw_in_lds = yf && G * d.ky <= a.yw_budget;
     for (int g0 = 0; g0 < kUnitPx; g0 += G) {
         const int oy_a = oy0 + g0, oy_b = oy_a + G - 1;
         const int ylo = yf ? yf[oy_a] : oy_a;
         const int yhi = yf ? yf[oy_b] + yf[dst_h + oy_b] : oy_b + 1;
-        const int nrows = yhi - ylo;  // <= kMidRows (the host sized G)
+        const int nrows = yhi - ylo;  // <= a.mid_rows (the host sized G)
         if (yf) {
             for (int i = tid; i < G; i += kHfThreads) {
                 yfirst_s[i] = yf[oy_a + i] - ylo;
@@ -189,24 +243,27 @@ __global__ __launch_bounds__(kHfThreads) void hf_preprocess_kernel(HfArgs a) {
                 for (int i = tid; i < G * d.ky; i += kHfThreads)
                     yw_s[i] = yf[2 * dst_h + int64_t(oy_a) * d.ky + i];
         }
-        const int chunk = min(nrows, kStageDwords / ncols);
-        const float inv_ncols = 1.0f / float(ncols);
+        const int chunk = min(nrows, a.stage_dwords / spitch);
+        const float inv_quads = 1.0f / float(quads);
         for (int r0 = 0; r0 < nrows; r0 += chunk) {
             const int nr = min(chunk, nrows - r0);
-            // stage source rows [ylo + r0, ylo + r0 + nr) x [xlo, xhi)
+            // stage source rows [ylo + r0, ylo + r0 + nr) x [xlo, xlo + spitch);
+            // the up to 3 pixels past xhi are never read
             const SrcWindow win = src_window(a, reinterpret_cast<uint64_t>(img_src) +
                                                     uint64_t(int64_t(ylo + r0) * row_bytes +
                                                              int64_t(xlo) * d.channels));
-            for (int idx = tid; idx < nr * ncols; idx += kHfThreads) {
-                const int r = div_small(idx, ncols, inv_ncols);
-                const int c = idx - r * ncols;
-                stage[idx] = load_rgb(win, win.lead + uint32_t(int64_t(r) * row_bytes + c * d.channels));
+            for (int idx = tid; idx < nr * quads; idx += kHfThreads) {
+                const int r = div_small(idx, quads, inv_quads);
+                const int q = idx - r * quads;
+                u32x4 px;
+                load_quad(win, win.lead + uint32_t(int64_t(r) * row_bytes + 4 * q * d.channels), d.channels, px);
+                *reinterpret_cast<u32x4 *>(&stage[r * spitch + 4 * q]) = px;
             }
             __syncthreads();
             // horizontal pass (or a copy) into band rows [r0, r0 + nr)
             for (int idx = tid; idx < nr * kUnitPx; idx += kHfThreads) {
                 const int r = idx >> 5, x = idx & 31;
-                const uint32_t *line = &stage[r * ncols];
+                const uint32_t *line = &stage[r * spitch];
                 uint32_t px;
                 if (xf) {
                     const int first = xfirst_s[x], count = xcount_s[x];
@@ -249,6 +306,7 @@ __global__ __launch_bounds__(kHfThreads) void hf_preprocess_kernel(HfArgs a) {
             block[(g0 + r) * kUnitPx + x] = px;
         }
         __syncthreads();
+    }
     }
 
     // 4 rows x 3 channels x 16 patch rows x 4 quads of 4 pixels; each thread
@@ -332,19 +390,30 @@ struct HfTables {
     std::vector<int32_t> taps;
     int64_t tiles = 0;
     int64_t rows = 0;
+    // dynamic LDS the batch needs (dwords, multiples of 4; see HfArgs)
+    int32_t xw_budget = 0, yw_budget = 0, mid_rows = 0, stage_dwords = 0;
+    size_t lds_bytes() const {
+        return 4 * (size_t(kFixedDwords) + xw_budget + yw_budget + size_t(mid_rows) * kUnitPx + stage_dwords);
+    }
 };
+
+int32_t round4(int64_t v) { return int32_t((v + 3) & ~int64_t(3)); }
+
+// The most source rows one group of g output rows reads.
+int band_rows(const int32_t *yfirst, const int32_t *ycount, int dst_h, int g) {
+    int most = 0;
+    for (int y0 = 0; y0 < dst_h; y0 += g) {
+        const int y1 = y0 + g - 1;
+        most = std::max(most, yfirst[y1] + ycount[y1] - yfirst[y0]);
+    }
+    return most;
+}
 
 // Output rows per vertical group so that the band of source rows one group
 // needs fits kMidRows: the largest of 32, 16, ..., 1 that fits everywhere.
 int choose_group(const int32_t *yfirst, const int32_t *ycount, int dst_h) {
-    for (int g = kUnitPx; g >= 1; g >>= 1) {
-        bool fits = true;
-        for (int y0 = 0; y0 < dst_h && fits; y0 += g) {
-            const int y1 = y0 + g - 1;
-            fits = yfirst[y1] + ycount[y1] - yfirst[y0] <= kMidRows;
-        }
-        if (fits) return g;
-    }
+    for (int g = kUnitPx; g >= 1; g >>= 1)
+        if (band_rows(yfirst, ycount, dst_h, g) <= kMidRows) return g;
     return 0;
 }
 
@@ -406,16 +475,30 @@ int build_hf_tables(int32_t n, const mimo_image_desc *desc, const float *mean01,
                 return set_error(MIMO_E_UNSUPPORTED, "preprocess_hf: descriptor " + std::to_string(i) +
                                                          ": vertical downscale beyond the kernel's band");
         }
+        int spitch = kUnitPx;  // staged pixels per source row (whole quads)
         if (d.kx) {
             // the widest source block one tile's 32 output columns read
             const int32_t *xfirst = out.taps.data() + d.x_tab;
             const int32_t *xcount = xfirst + s.dst_w;
             for (int32_t x0 = 0; x0 < s.dst_w; x0 += kUnitPx) {
                 const int32_t x1 = x0 + kUnitPx - 1;
-                if (xfirst[x1] + xcount[x1] - xfirst[x0] > kStageDwords)
-                    return set_error(MIMO_E_UNSUPPORTED, "preprocess_hf: descriptor " + std::to_string(i) +
-                                                             ": horizontal downscale beyond the kernel's staging");
+                spitch = std::max(spitch, round4(xfirst[x1] + xcount[x1] - xfirst[x0]));
             }
+            if (spitch > kStageDwords)
+                return set_error(MIMO_E_UNSUPPORTED, "preprocess_hf: descriptor " + std::to_string(i) +
+                                                         ": horizontal downscale beyond the kernel's staging");
+            if (kUnitPx * d.kx <= kTapBudget) out.xw_budget = std::max(out.xw_budget, round4(kUnitPx * d.kx));
+        }
+        if (d.kx || d.ky) {
+            // band rows of one group, and staging for all of them at once when that fits
+            const int nrows = d.ky ? band_rows(out.taps.data() + d.y_tab, out.taps.data() + d.y_tab + s.dst_h,
+                                               s.dst_h, d.group)
+                                   : d.group;
+            out.mid_rows = std::max(out.mid_rows, round4(nrows));
+            out.stage_dwords = std::max<int32_t>(
+                out.stage_dwords, int32_t(std::min<int64_t>(kStageDwords, int64_t(nrows) * spitch)));
+            if (d.ky && d.group * d.ky <= kTapBudget)
+                out.yw_budget = std::max(out.yw_budget, round4(d.group * d.ky));
         }
         items[i] = d;
         tiles += int64_t(d.blocks_h) * d.blocks_w;
@@ -506,12 +589,21 @@ int mimo_preprocess_hf_batch(int32_t n, const mimo_image_desc *desc, const uint8
     a.rows = rows;
     a.rows_col = rows_col;
     a.n = n;
+    a.xw_budget = t.xw_budget;
+    a.yw_budget = t.yw_budget;
+    a.mid_rows = t.mid_rows;
+    a.stage_dwords = t.stage_dwords;
+    const size_t lds = t.lds_bytes();
+    const void *kernel = out_dtype == MIMO_F32 ? reinterpret_cast<const void *>(hf_preprocess_kernel<float>)
+                                               : reinterpret_cast<const void *>(hf_preprocess_kernel<uint16_t>);
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return hip_error(e, "preprocess_hf: LDS size");
     const dim3 grid{unsigned(t.tiles), 1, 1}, block{unsigned(kHfThreads), 1, 1};
     e = timed_launch(s, [&] {
         if (out_dtype == MIMO_F32)
-            hipLaunchKernelGGL(hf_preprocess_kernel<float>, grid, block, 0, s, a);
+            hipLaunchKernelGGL(hf_preprocess_kernel<float>, grid, block, lds, s, a);
         else
-            hipLaunchKernelGGL(hf_preprocess_kernel<uint16_t>, grid, block, 0, s, a);
+            hipLaunchKernelGGL(hf_preprocess_kernel<uint16_t>, grid, block, lds, s, a);
     });
     if (e != hipSuccess) return hip_error(e, "preprocess_hf: kernel launch");
     g_dispatches.fetch_add(1);
