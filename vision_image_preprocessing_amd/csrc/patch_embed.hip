@@ -18,18 +18,18 @@
 // per SIMD) owns a 256 x 256 tile of C; each wave a 128 x 128 quarter as
 // 4 x 4 MFMA blocks (256 accumulators per lane), which keeps the LDS bytes
 // per matrix-core flop at (128 + 128) / (128 * 128) of a 16-wide k step.  K
-// advances 64 at a time through double-buffered LDS; rows are 128 bytes and
-// their eight 16-byte chunks are XOR-swizzled by the row index, so the
-// fragment reads of 16 consecutive rows hit distinct banks.  Operand tiles
-// go from global memory straight into LDS (global_load_lds_dwordx4, no
-// register staging); the next stage's loads are spread between the MFMAs of
-// the current one, and a dword touch of each A line three stages ahead
-// pulls the A panel into L2 before the tiles sharing it ask for it.  The
-// tile is written back through LDS so that every store covers whole row
-// segments (non-temporal, 16 bytes per lane); W is the MFMA's first operand,
-// which gives each lane four consecutive output columns to stage.  Tiles are
-// ordered N fastest and assigned to XCDs in contiguous runs, so one XCD's L2
-// serves an A tile to all of its N tiles.
+// advances 64 at a time; rows are 128 bytes and their eight 16-byte chunks
+// are XOR-swizzled by the row index, so the fragment reads of 16
+// consecutive rows hit distinct banks.  Operand tiles go from global memory
+// straight into LDS (global_load_lds_dwordx4, no register staging), A two
+// stages ahead of the MFMAs (three LDS buffers) and W one (two buffers):
+// the kernel is bound by how fast a CU takes its tiles from L2, so the
+// loads go out early, in the first half of each stage and spread between
+// the MFMAs.  The tile is written back through LDS so that every store
+// covers whole row segments (non-temporal, 16 bytes per lane); W is the
+// MFMA's first operand, which gives each lane four consecutive output
+// columns to stage.  Tiles are ordered N fastest and assigned to XCDs in
+// contiguous runs, so one XCD's L2 serves an A tile to all of its N tiles.
 #include <hip/hip_runtime.h>
 
 #include <cstring>
@@ -47,7 +47,6 @@ constexpr int kEmbedThreads = 256;
 constexpr int kWaveM = 128, kWaveN = 128;       // one wave's quarter of the tile
 constexpr int kBlocksM = kWaveM / 32, kBlocksN = kWaveN / 32;
 constexpr int kGroups = kBM / 8 / (kEmbedThreads / 64);  // 1 KB LDS groups per wave per operand
-constexpr int kPrefetchAhead = 3;  // stages between an L2 prefetch of A and its real load
 constexpr int kFoldSeg = 256;       // contiguous K run of one channel in the folded form
 constexpr int kFoldStride = 512;    // its stride in the row (the tt = 1 plane is skipped)
 
@@ -94,17 +93,21 @@ __device__ __forceinline__ int lds_at(int r, int v) { return r * kBK + ((v ^ swz
 // s_waitcnt immediates (gfx9 layout: vmcnt in bits 3:0 and 15:14, expcnt
 // in 6:4, lgkmcnt in 11:8; a field at its maximum does not wait).
 constexpr int kWaitAll = 0;                 // every counter at zero
-constexpr int kWaitVmemButOne = 0x0F71;     // vmcnt(1) only
+constexpr int kWaitVmemButA = 0x0F78;       // vmcnt(8): one stage of A loads may stay in flight
 
-template <typename OutT>
+// kFolded: K = 768 over the tt = 0 half of each row, else K = 1536.  K is
+// a compile-time constant so that the stage loop unrolls fully: every
+// buffer choice and every tail condition is then a constant, and the
+// compiler can track each direct load exactly (a loop back edge makes it
+// wait for all loads in flight before reading LDS).
+template <typename OutT, bool kFolded>
 __global__ __launch_bounds__(kEmbedThreads) void patch_embed_kernel(EmbedArgs a) {
-    // Two LDS stages as four distinct arrays: the compiler then sees that the
-    // loads filling one stage never alias the reads of the other, and does
-    // not make those reads wait for the loads in flight.  The sink takes the
-    // L2 prefetches and is never read.
-    __shared__ uint16_t sa0[kBM * kBK], sa1[kBM * kBK];
+    // Three A stages and two W stages (160 KB, all of the CU's LDS) as five
+    // distinct arrays: the compiler then sees that the loads filling one
+    // stage never alias the reads of another, and does not make those reads
+    // wait for the loads in flight.
+    __shared__ uint16_t sa0[kBM * kBK], sa1[kBM * kBK], sa2[kBM * kBK];
     __shared__ uint16_t sb0[kBN * kBK], sb1[kBN * kBK];
-    __shared__ uint32_t sink[kEmbedThreads];
     const int64_t tile = xcd_contiguous_tile(blockIdx.x, gridDim.x);
     const int64_t mt = tile / a.n_tiles;
     const int nt = int(tile - mt * a.n_tiles);
@@ -113,8 +116,8 @@ __global__ __launch_bounds__(kEmbedThreads) void patch_embed_kernel(EmbedArgs a)
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;  // the wave's quarter
-    const bool folded = a.folded != 0;
-    const int stages = a.k / kBK;
+    constexpr bool folded = kFolded;
+    constexpr int stages = (kFolded ? kRowLen / 2 : kRowLen) / kBK;  // 12 or 24
 
     // Global -> LDS loads of one stage: 256 rows x 64 k of A and of W.  Wave
     // w fills LDS row groups [8 kGroups w, 8 kGroups (w + 1)); within a 1 KB
@@ -131,33 +134,22 @@ __global__ __launch_bounds__(kEmbedThreads) void patch_embed_kernel(EmbedArgs a)
         a_src[i] = a.rows + row * kRowLen + v * 8;
         w_src[i] = a.w + int64_t(n0 + r) * a.k + v * 8;
     }
-    // Load number l (0 .. 2 kGroups - 1) of a stage: A group l / 2 for even
-    // l, W group l / 2 for odd l.
-    auto load_one = [&](int l, int k0, int acol, uint16_t *da, uint16_t *db) {
-        const int grp = l >> 1;
+    // One group (8 rows x 64 k) of a stage's A or W tile into LDS.
+    auto load_a = [&](int grp, int k0, uint16_t *da) {
         const int g = wave * kGroups + grp;
-        if ((l & 1) == 0)
-            __builtin_amdgcn_global_load_lds(a_src[grp] + acol, (lds_void_ptr)(da + g * 8 * kBK), 16, 0, 0);
-        else
-            __builtin_amdgcn_global_load_lds(w_src[grp] + k0, (lds_void_ptr)(db + g * 8 * kBK), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(a_src[grp] + a_column(k0, folded), (lds_void_ptr)(da + g * 8 * kBK),
+                                         16, 0, 0);
     };
-    // L2 prefetch: during stage s, thread t touches the 128-byte line of A
-    // row t that stage s + kPrefetchAhead reads (one dword into the sink),
-    // two stages before that stage's real loads go out, so they and the
-    // other tiles sharing the A panel find it in L2.  Past the last stage it
-    // touches a line of the last stage again.
-    static_assert(kEmbedThreads == kBM, "one prefetched A row per thread");
-    const int64_t pf_row = m0 + tid < a.n_rows ? m0 + tid : a.n_rows - 1;
-    const uint16_t *pf_base = a.rows + pf_row * kRowLen;
-    auto prefetch = [&](int s) {  // s: the stage whose line is touched
-        __builtin_amdgcn_global_load_lds(pf_base + a_column(min(s, stages - 1) * kBK, folded),
-                                         (lds_void_ptr)(sink + wave * 64), 4, 0, 0);
+    auto load_w = [&](int grp, int k0, uint16_t *db) {
+        const int g = wave * kGroups + grp;
+        __builtin_amdgcn_global_load_lds(w_src[grp] + k0, (lds_void_ptr)(db + g * 8 * kBK), 16, 0, 0);
     };
     // The barrier between stages.  __syncthreads would add a fence that
-    // waits for every load in flight, the prefetch included; each thread has
-    // already waited for its own stage loads (kWaitVmemButOne: the prefetch
-    // is its newest vector memory operation), and LDS-DMA data counts as
-    // written once vmcnt has passed it.
+    // waits for every load in flight, the A loads two stages ahead included;
+    // each thread has already waited for the loads of the next stage
+    // (kWaitVmemButA: the A loads of the stage after it are its newest 8
+    // vector memory operations), and LDS-DMA data counts as written once
+    // vmcnt has passed it.
     auto barrier = [] {
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_barrier();
@@ -170,13 +162,16 @@ __global__ __launch_bounds__(kEmbedThreads) void patch_embed_kernel(EmbedArgs a)
 #pragma unroll
         for (int j = 0; j < kBlocksN; ++j) acc[i][j] = f32x16{};
 
-    {
-        const int acol0 = a_column(0, folded);
+    // A runs two stages ahead of the MFMAs, W one: stage s reads A buffer
+    // s % 3 and W buffer s % 2.
 #pragma unroll
-        for (int l = 0; l < 2 * kGroups; ++l) load_one(l, 0, acol0, sa0, sb0);
-        __builtin_amdgcn_s_waitcnt(kWaitAll);
-        barrier();
-    }
+    for (int grp = 0; grp < kGroups; ++grp) load_a(grp, 0, sa0);
+#pragma unroll
+    for (int grp = 0; grp < kGroups; ++grp) load_w(grp, 0, sb0);
+#pragma unroll
+    for (int grp = 0; grp < kGroups; ++grp) load_a(grp, kBK, sa1);
+    __builtin_amdgcn_s_waitcnt(kWaitVmemButA);
+    barrier();
     // MFMA operand rows of this lane: A block i covers C rows wm*128 + i*32 +
     // (lane % 32); B block j covers C columns wn*128 + j*32 + (lane % 32);
     // the lane supplies k = 8 * (lane / 32) .. + 7 of each 16-wide k step.
@@ -195,16 +190,16 @@ __global__ __launch_bounds__(kEmbedThreads) void patch_embed_kernel(EmbedArgs a)
                 &tb[lds_at(wn * kWaveN + j * 32 + frag_row, 2 * ks + frag_chunk)]);
     };
     constexpr int kSteps = kBK / 16;
-    static_assert(kSteps * kBlocksM == 2 * kGroups, "one stage load after each row of MFMA blocks");
+    static_assert(kGroups == 8 && kSteps * kBlocksM == 16, "two loads after each of the first 8 MFMA rows");
     // One stage: multiply this LDS stage (the next k step's fragments are
-    // read while this step's MFMAs run) while the next stage's loads go out
-    // one after each row of four MFMAs (issued in a burst they would hold the
-    // wave at issue), the prefetch last; then wait for all but the prefetch,
-    // and for every wave.
-    auto stage = [&](int s, const uint16_t *ta, const uint16_t *tb, uint16_t *na, uint16_t *nb) {
-        const bool more = s + 1 < stages;
-        const int k1 = (s + 1) * kBK;
-        const int acol1 = a_column(more ? k1 : 0, folded);
+    // read while this step's MFMAs run).  During the first two k steps, two
+    // loads go out after each row of four MFMAs (issued in a burst they would
+    // hold the wave at issue): W for stage s + 1, then A for stage s + 2, so
+    // the later half of the stage covers their latency.  Then wait for all
+    // but the A loads, and for every wave.
+    auto stage = [&](int s, const uint16_t *ta, const uint16_t *tb, uint16_t *nb, uint16_t *na2) {
+        const bool more_w = s + 1 < stages, more_a = s + 2 < stages;
+        const int kw = (s + 1) * kBK, ka = (s + 2) * kBK;
         bf16x8 fa[2][kBlocksM], fb[2][kBlocksN];
         read_frags(ta, tb, 0, fa[0], fb[0]);
 #pragma unroll
@@ -219,21 +214,29 @@ __global__ __launch_bounds__(kEmbedThreads) void patch_embed_kernel(EmbedArgs a)
                 for (int j = 0; j < kBlocksN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks & 1][j], fa[ks & 1][i],
                                                                         acc[i][j], 0, 0, 0);
-                const int l = ks * kBlocksM + i;
-                if (more) load_one(l, k1, acol1, na, nb);
-                if (l == 2 * kGroups - 1) prefetch(s + kPrefetchAhead);
+                const int slot = ks * kBlocksM + i;  // W groups after slots 0-3, A groups after 4-7
+                if (slot < 4 && more_w) {
+                    load_w(2 * slot, kw, nb);
+                    load_w(2 * slot + 1, kw, nb);
+                } else if (slot >= 4 && slot < 8 && more_a) {
+                    load_a(2 * slot - 8, ka, na2);
+                    load_a(2 * slot - 7, ka, na2);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        __builtin_amdgcn_s_waitcnt(kWaitVmemButOne);
+        if (more_a)
+            __builtin_amdgcn_s_waitcnt(kWaitVmemButA);
+        else
+            __builtin_amdgcn_s_waitcnt(kWaitAll);
         barrier();
     };
-    // stages is even (1536 / 64 or 768 / 64), so stages alternate in pairs
-    for (int s = 0; s < stages; s += 2) {
-        stage(s, sa0, sb0, sa1, sb1);
-        stage(s + 1, sa1, sb1, sa0, sb0);
+#pragma unroll
+    for (int s = 0; s < stages; ++s) {
+        uint16_t *const abuf[3] = {sa0, sa1, sa2};
+        uint16_t *const wbuf[2] = {sb0, sb1};
+        stage(s, abuf[s % 3], wbuf[s % 2], wbuf[(s + 1) % 2], abuf[(s + 2) % 3]);
     }
-    __builtin_amdgcn_s_waitcnt(kWaitAll);  // the last prefetch, before LDS is reused
 
     // Epilogue through LDS, free now that every wave has passed the last
     // stage's barrier.  Each wave stages its 128 x 128 block 32 rows at a
@@ -346,10 +349,17 @@ int mimo_patch_embed(int64_t n_rows, const void *rows, int32_t embed_dim, const 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const dim3 grid{unsigned(m_tiles * n_tiles), 1, 1}, block{unsigned(kEmbedThreads), 1, 1};
     const hipError_t e = timed_launch(s, [&] {
-        if (out_dtype == MIMO_F32)
-            hipLaunchKernelGGL(patch_embed_kernel<float>, grid, block, 0, s, a);
-        else
-            hipLaunchKernelGGL(patch_embed_kernel<uint16_t>, grid, block, 0, s, a);
+        if (out_dtype == MIMO_F32) {
+            if (folded)
+                hipLaunchKernelGGL((patch_embed_kernel<float, true>), grid, block, 0, s, a);
+            else
+                hipLaunchKernelGGL((patch_embed_kernel<float, false>), grid, block, 0, s, a);
+        } else {
+            if (folded)
+                hipLaunchKernelGGL((patch_embed_kernel<uint16_t, true>), grid, block, 0, s, a);
+            else
+                hipLaunchKernelGGL((patch_embed_kernel<uint16_t, false>), grid, block, 0, s, a);
+        }
     });
     if (e != hipSuccess) return hip_error(e, "patch_embed: kernel launch");
     g_dispatches.fetch_add(1);
