@@ -187,9 +187,16 @@ __global__ __launch_bounds__(kHfThreads) void hf_preprocess_kernel(HfArgs a) {
     const int64_t tile = xcd_contiguous_tile(blockIdx.x, gridDim.x);
     const int img = find_segment(a.tile_begin, a.n, tile);
     const HfItem d = a.items[img];
+    // An item lists one tile per (merge unit, group of G output rows); G is
+    // a power of two, 32 (one tile per unit) unless the vertical taps of 32
+    // rows do not fit the band.
+    const int G = d.group;
+    const int gsh = __builtin_ctz(unsigned(G));
     const int local = int(tile - a.tile_begin[img]);
-    const int br = div_small(local, d.blocks_w, 1.0f / float(d.blocks_w));
-    const int bc = local - br * d.blocks_w;
+    const int unit = local >> (5 - gsh);
+    const int g0 = (local & ((kUnitPx >> gsh) - 1)) << gsh;  // the group's first row in the unit
+    const int br = div_small(unit, d.blocks_w, 1.0f / float(d.blocks_w));
+    const int bc = unit - br * d.blocks_w;
     const int oy0 = br * kUnitPx, ox0 = bc * kUnitPx;
     const int tid = threadIdx.x;
     for (int i = tid; i < 3 * 256; i += kHfThreads) lut[i] = a.lut[i];
@@ -211,7 +218,6 @@ __global__ __launch_bounds__(kHfThreads) void hf_preprocess_kernel(HfArgs a) {
     const int dst_w = d.blocks_w * kUnitPx, dst_h = d.blocks_h * kUnitPx;
     const int32_t *xf = d.kx ? a.taps + d.x_tab : nullptr;  // first[dst_w], count[dst_w], w[dst_w][kx]
     const int32_t *yf = d.ky ? a.taps + d.y_tab : nullptr;
-    const int G = d.group;
     // source columns the tile's 32 output columns read, and their taps in LDS
     // (the weights too, when they fit; else they are read from memory)
     const int xlo = xf ? xf[ox0] : ox0;
@@ -229,7 +235,7 @@ __global__ __launch_bounds__(kHfThreads) void hf_preprocess_kernel(HfArgs a) {
                 xw_s[i] = xf[2 * dst_w + int64_t(ox0) * d.kx + i];
     }
     const bool yw_in_lds = yf && G * d.ky <= a.yw_budget;
-    for (int g0 = 0; g0 < kUnitPx; g0 += G) {
+    {
         const int oy_a = oy0 + g0, oy_b = oy_a + G - 1;
         const int ylo = yf ? yf[oy_a] : oy_a;
         const int yhi = yf ? yf[oy_b] + yf[dst_h + oy_b] : oy_b + 1;
@@ -309,16 +315,19 @@ __global__ __launch_bounds__(kHfThreads) void hf_preprocess_kernel(HfArgs a) {
     }
     }
 
-    // 4 rows x 3 channels x 16 patch rows x 4 quads of 4 pixels; each thread
-    // stores one quad into both temporal slots
-    for (int idx = tid; idx < kRowsPerUnit * 3 * kPatch * 4; idx += kHfThreads) {
-        const int q = idx / (3 * kPatch * 4);
-        const int rem = idx - q * (3 * kPatch * 4);
-        const int c = rem / (kPatch * 4);
-        const int py = (rem >> 2) & (kPatch - 1);
-        const int qd = rem & 3;
-        const int mh = q >> 1, mw = q & 1;
-        const uint32_t *src_px = &block[(mh * kPatch + py) * kUnitPx + mw * kPatch + qd * 4];
+    // The group's G pixel rows x 2 patch columns x 3 channels x 4 quads of 4
+    // pixels; each thread stores one quad into both temporal slots, a wave
+    // one contiguous run of a (c, tt) plane.
+    for (int idx = tid; idx < G * 2 * 3 * 4; idx += kHfThreads) {
+        const int qd = idx & 3;
+        const int yl = (idx >> 2) & (G - 1);
+        const int mc = idx >> (2 + gsh);  // (mw, c): 0 .. 5
+        const int mw = mc >= 3 ? 1 : 0;
+        const int c = mc - 3 * mw;
+        const int y = g0 + yl;            // pixel row in the unit
+        const int mh = y >> 4, py = y & (kPatch - 1);
+        const int q = mh * kMerge + mw;   // row of the unit
+        const uint32_t *src_px = &block[y * kUnitPx + mw * kPatch + qd * 4];
         float v[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) v[j] = lut[c * 256 + ((src_px[j] >> (8 * c)) & 255u)];
@@ -501,7 +510,7 @@ int build_hf_tables(int32_t n, const mimo_image_desc *desc, const float *mean01,
                 out.yw_budget = std::max(out.yw_budget, round4(d.group * d.ky));
         }
         items[i] = d;
-        tiles += int64_t(d.blocks_h) * d.blocks_w;
+        tiles += int64_t(d.blocks_h) * d.blocks_w * (kUnitPx / d.group);
         rows += s.rows;
     }
     tile_begin[n] = tiles;
