@@ -21,7 +21,7 @@
 // advances 64 at a time; rows are 128 bytes and their eight 16-byte chunks
 // are XOR-swizzled by the row index, so the fragment reads of 16
 // consecutive rows hit distinct banks.  Operand tiles go from global memory
-// straight into LDS (global_load_lds_dwordx4, no register staging), A two
+// straight into LDS (buffer_load_dwordx4 ... lds, no register staging), A two
 // stages ahead of the MFMAs (three LDS buffers) and W one (two buffers):
 // the kernel is bound by how fast a CU takes its tiles from L2, so the
 // loads go out early, in the first half of each stage and spread between
@@ -49,6 +49,8 @@ constexpr int kBlocksM = kWaveM / 32, kBlocksN = kWaveN / 32;
 constexpr int kGroups = kBM / 8 / (kEmbedThreads / 64);  // 1 KB LDS groups per wave per operand
 constexpr int kFoldSeg = 256;       // contiguous K run of one channel in the folded form
 constexpr int kFoldStride = 512;    // its stride in the row (the tt = 1 plane is skipped)
+
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer resource word 3 (gfx9 family)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void *lds_void_ptr;
@@ -123,26 +125,33 @@ __global__ __launch_bounds__(kEmbedThreads) void patch_embed_kernel(EmbedArgs a)
     // w fills LDS row groups [8 kGroups w, 8 kGroups (w + 1)); within a 1 KB
     // group lane l lands at row l / 8, physical chunk l % 8, so it fetches
     // the logical chunk (l % 8) ^ swz(row) of its row.  Rows past n_rows
-    // read the last row instead; their results are never stored.
-    const uint16_t *a_src[kGroups];
-    const uint16_t *w_src[kGroups];
+    // read the last row instead; their results are never stored.  The loads
+    // are buffer loads: one resource over the tile's A rows and one over its
+    // W rows, a 32-bit byte offset per lane (< 768 KB) and the stage's K
+    // offset as the uniform scalar offset.
+    const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(a.rows + m0 * kRowLen), 0, 0x7FFFFFF0, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(a.w + int64_t(n0) * a.k), 0, 0x7FFFFFF0, kBufferWord3);
+    uint32_t a_off[kGroups], w_off[kGroups];
 #pragma unroll
     for (int i = 0; i < kGroups; ++i) {
         const int r = (wave * kGroups + i) * 8 + (lane >> 3);
         const int v = (lane & 7) ^ swz(r);
         const int64_t row = m0 + r < a.n_rows ? m0 + r : a.n_rows - 1;
-        a_src[i] = a.rows + row * kRowLen + v * 8;
-        w_src[i] = a.w + int64_t(n0 + r) * a.k + v * 8;
+        a_off[i] = uint32_t((row - m0) * kRowLen * 2 + v * 16);
+        w_off[i] = uint32_t(r * a.k * 2 + v * 16);
     }
     // One group (8 rows x 64 k) of a stage's A or W tile into LDS.
     auto load_a = [&](int grp, int k0, uint16_t *da) {
         const int g = wave * kGroups + grp;
-        __builtin_amdgcn_global_load_lds(a_src[grp] + a_column(k0, folded), (lds_void_ptr)(da + g * 8 * kBK),
-                                         16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void_ptr)(da + g * 8 * kBK), 16, a_off[grp],
+                                                 a_column(k0, folded) * 2, 0, 0);
     };
     auto load_w = [&](int grp, int k0, uint16_t *db) {
         const int g = wave * kGroups + grp;
-        __builtin_amdgcn_global_load_lds(w_src[grp] + k0, (lds_void_ptr)(db + g * 8 * kBK), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_void_ptr)(db + g * 8 * kBK), 16, w_off[grp],
+                                                 k0 * 2, 0, 0);
     };
     // The barrier between stages.  __syncthreads would add a fence that
     // waits for every load in flight, the A loads two stages ahead included;
