@@ -96,6 +96,8 @@ __device__ __forceinline__ int lds_at(int r, int v) { return r * kBK + ((v ^ swz
 // in 6:4, lgkmcnt in 11:8; a field at its maximum does not wait).
 constexpr int kWaitAll = 0;                 // every counter at zero
 constexpr int kWaitVmemButA = 0x0F78;       // vmcnt(8): one stage of A loads may stay in flight
+constexpr int kWaitLdsVmemButA = 0x0078;    // lgkmcnt(0) and vmcnt(8)
+constexpr int kWaitLdsVmem = 0x0070;        // lgkmcnt(0) and vmcnt(0)
 
 // kFolded: K = 768 over the tt = 0 half of each row, else K = 1536.  K is
 // a compile-time constant so that the stage loop unrolls fully: every
@@ -204,18 +206,34 @@ __global__ __launch_bounds__(kEmbedThreads) void patch_embed_kernel(EmbedArgs a)
     // read while this step's MFMAs run).  During the first two k steps, two
     // loads go out after each row of four MFMAs (issued in a burst they would
     // hold the wave at issue): W for stage s + 1, then A for stage s + 2, so
-    // the later half of the stage covers their latency.  Then wait for all
-    // but the A loads, and for every wave.
-    auto stage = [&](int s, const uint16_t *ta, const uint16_t *tb, uint16_t *nb, uint16_t *na2) {
+    // the later half of the stage covers their latency.  Before the last k
+    // step's MFMAs, whose fragments are already in registers, the wave waits
+    // for its own LDS reads and for all but the A loads, meets the others,
+    // and reads the next stage's first fragments: the stage change then costs
+    // no MFMA idle time.  The loads issued after that barrier overwrite this
+    // stage's buffers, which no wave reads any more.  The fragments are
+    // double-buffered across stages.
+    bf16x8 fa[2][kBlocksM], fb[2][kBlocksN];
+    read_frags(sa0, sb0, 0, fa[0], fb[0]);
+    auto stage = [&](int s, const uint16_t *ta, const uint16_t *tb, uint16_t *nb, uint16_t *na2,
+                     const uint16_t *ta_next, const uint16_t *tb_next) {
         const bool more_w = s + 1 < stages, more_a = s + 2 < stages;
         const int kw = (s + 1) * kBK, ka = (s + 2) * kBK;
-        bf16x8 fa[2][kBlocksM], fb[2][kBlocksN];
-        read_frags(ta, tb, 0, fa[0], fb[0]);
 #pragma unroll
         for (int ks = 0; ks < kSteps; ++ks) {
-            if (ks + 1 < kSteps) read_frags(ta, tb, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
-            // keep those reads ahead of this step's MFMAs (the scheduler would
-            // otherwise sink each read to its first use and expose its latency)
+            if (ks + 1 < kSteps) {
+                read_frags(ta, tb, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+            } else if (more_w) {
+                // every read of this stage is issued: wait for them and for the
+                // next stage's data, meet, and read the next stage's first
+                // fragments while this last k step's MFMAs run
+                if (more_a)
+                    __builtin_amdgcn_s_waitcnt(kWaitLdsVmemButA);
+                else
+                    __builtin_amdgcn_s_waitcnt(kWaitLdsVmem);
+                barrier();
+                read_frags(ta_next, tb_next, 0, fa[0], fb[0]);
+            }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < kBlocksM; ++i) {
@@ -223,7 +241,7 @@ __global__ __launch_bounds__(kEmbedThreads) void patch_embed_kernel(EmbedArgs a)
                 for (int j = 0; j < kBlocksN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks & 1][j], fa[ks & 1][i],
                                                                         acc[i][j], 0, 0, 0);
-                const int slot = ks * kBlocksM + i;  // W groups after slots 0-3, A groups after 4-7
+                const int slot = ks * kBlocksM + i;
                 if (slot < 4 && more_w) {
                     load_w(2 * slot, kw, nb);
                     load_w(2 * slot + 1, kw, nb);
@@ -234,18 +252,16 @@ __global__ __launch_bounds__(kEmbedThreads) void patch_embed_kernel(EmbedArgs a)
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        if (more_a)
-            __builtin_amdgcn_s_waitcnt(kWaitVmemButA);
-        else
-            __builtin_amdgcn_s_waitcnt(kWaitAll);
-        barrier();
     };
 #pragma unroll
     for (int s = 0; s < stages; ++s) {
         uint16_t *const abuf[3] = {sa0, sa1, sa2};
         uint16_t *const wbuf[2] = {sb0, sb1};
-        stage(s, abuf[s % 3], wbuf[s % 2], wbuf[(s + 1) % 2], abuf[(s + 2) % 3]);
+        stage(s, abuf[s % 3], wbuf[s % 2], wbuf[(s + 1) % 2], abuf[(s + 2) % 3], abuf[(s + 1) % 3],
+              wbuf[(s + 1) % 2]);
     }
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+    barrier();
 
     // Epilogue through LDS, free now that every wave has passed the last
     // stage's barrier.  Each wave stages its 128 x 128 block 32 rows at a
