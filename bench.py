@@ -63,9 +63,12 @@ def measured_traffic(workload: str):
     return rec.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(batch, plan, sample: int, threads: int) -> dict:
+def cpu_baseline(batch, plan, sample: int, threads: int, out_bytes_per_value: int = 4) -> dict:
     """The oracle, as it is, on the first `sample` items (images, or clips
-    for a video batch), one item per thread at a time."""
+    for a video batch), one item per thread at a time.  "GB/s" counts the
+    sampled items' source bytes plus their rows once at out_bytes_per_value
+    (the oracle computes merge-block order; the column order is an index
+    permutation of it)."""
     from concurrent.futures import ThreadPoolExecutor
 
     import oracle
@@ -86,13 +89,16 @@ def cpu_baseline(batch, plan, sample: int, threads: int) -> dict:
     dt = time.perf_counter() - t0
     counts = batch.frame_counts
     units = sum(counts[i] for i in idx)
+    nbytes = sum(int(plan.desc["src_h"][i]) * int(plan.desc["src_w"][i]) * int(plan.desc["channels"][i]) *
+                 counts[i] + int(plan.desc["rows"][i]) * 1536 * out_bytes_per_value for i in idx)
     unit = "frames/s" if batch.is_media else "images/s"
     what = "clips" if batch.is_media else "images"
     return {"value": units / dt, "unit": unit, "cores": threads, "kind": "oracle",
             "sample": f"first {len(idx)} of {len(batch)} {what} of the same batch"
                       + (f" ({units} frames)" if batch.is_media else "")
                       + f", one item per thread, {threads} threads, {dt:.2f} s wall",
-            "seconds": dt, "cpu_model": platform.processor() or platform.machine()}
+            "seconds": dt, "GB/s": nbytes / dt / 1e9,
+            "cpu_model": platform.processor() or platform.machine()}
 
 
 def time_launches(V, fn, reps: int, stream):
@@ -284,11 +290,17 @@ def main():
     V.load()  # fails loudly if the HIP library is not built
     log("generating", args.workload)
     batch = workloads.WORKLOADS[args.workload]()
+    t_plan = time.perf_counter()
     if batch.is_media:
         plan = V.plan_media(batch.items, video_budget=batch.video_budget)
     else:
         plan = V.plan_batch(batch.shapes)
+    plan_ms = (time.perf_counter() - t_plan) * 1e3
+    torch.cuda.synchronize()
+    t_up = time.perf_counter()
     src = V.processor.upload_sources(batch.packed, plan)
+    torch.cuda.synchronize()
+    upload_ms = (time.perf_counter() - t_up) * 1e3
     out_dtype = batch.out_dtype
     tdtype = torch.float32 if out_dtype == "f32" else torch.bfloat16
     bpv = 4 if out_dtype == "f32" else 2
@@ -375,6 +387,10 @@ def main():
         "launch_ms_min": float(np.min(per_launch_ms)),
         "launch_ms_median": float(np.median(per_launch_ms)),
         "published_throughput": "none (the pages publish no throughput for this path)",
+        # host work outside the timed region: the geometry plan, and the one
+        # copy of the packed sources from pageable host memory into HBM
+        "host": {"plan_ms": plan_ms, "source_upload_ms": upload_ms,
+                 "source_upload_GB/s": alg["read"] / (upload_ms * 1e-3) / 1e9},
     }
 
     if args.gather and rows_col is not None:
@@ -409,7 +425,9 @@ def main():
     if not args.no_cpu_baseline:
         threads = max(1, min(16, os.cpu_count() or 1))
         log("cpu baseline (oracle)", args.cpu_sample, "images,", threads, "threads")
-        result["cpu_baseline"] = cpu_baseline(batch, plan, args.cpu_sample, threads)
+        result["cpu_baseline"] = cpu_baseline(batch, plan, args.cpu_sample, threads, bpv)
+        log("cpu baseline (oracle), one thread")
+        result["cpu_baseline"]["single_thread"] = cpu_baseline(batch, plan, min(args.cpu_sample, 32), 1, bpv)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

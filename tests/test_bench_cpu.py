@@ -55,3 +55,6 @@ def test_cpu_baseline_reports_its_sample():
     assert res["kind"] == "oracle" and res["cores"] == 2 and res["unit"] == "images/s"
     assert res["value"] > 0 and np.isfinite(res["value"])
     assert res["sample"].startswith("first 2 of 3 images")
+    src = 64 * 64 * 3 + 40 * 90 * 4
+    rows = int(plan.desc["rows"][0] + plan.desc["rows"][1])
+    assert res["GB/s"] == pytest.approx((src + rows * 1536 * 4) / res["seconds"] / 1e9)
