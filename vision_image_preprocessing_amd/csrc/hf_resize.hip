@@ -215,27 +215,26 @@ __global__ __launch_bounds__(kHfThreads) void hf_preprocess_kernel(HfArgs a) {
         }
         __syncthreads();
     } else {
-    const int dst_w = d.blocks_w * kUnitPx, dst_h = d.blocks_h * kUnitPx;
-    const int32_t *xf = d.kx ? a.taps + d.x_tab : nullptr;  // first[dst_w], count[dst_w], w[dst_w][kx]
-    const int32_t *yf = d.ky ? a.taps + d.y_tab : nullptr;
-    // source columns the tile's 32 output columns read, and their taps in LDS
-    // (the weights too, when they fit; else they are read from memory)
-    const int xlo = xf ? xf[ox0] : ox0;
-    const int xhi = xf ? xf[ox0 + kUnitPx - 1] + xf[dst_w + ox0 + kUnitPx - 1] : ox0 + kUnitPx;
-    const int quads = (xhi - xlo + 3) >> 2;  // staged 4 pixels at a time
-    const int spitch = 4 * quads;             // <= a.stage_dwords (the host checked)
-    const bool xw_in_lds = xf && kUnitPx * d.kx <= a.xw_budget;
-    if (xf) {
-        for (int i = tid; i < kUnitPx; i += kHfThreads) {
-            xfirst_s[i] = xf[ox0 + i] - xlo;
-            xcount_s[i] = xf[dst_w + ox0 + i];
+        const int dst_w = d.blocks_w * kUnitPx, dst_h = d.blocks_h * kUnitPx;
+        const int32_t *xf = d.kx ? a.taps + d.x_tab : nullptr;  // first[dst_w], count[dst_w], w[dst_w][kx]
+        const int32_t *yf = d.ky ? a.taps + d.y_tab : nullptr;
+        // source columns the tile's 32 output columns read, and their taps in LDS
+        // (the weights too, when they fit; else they are read from memory)
+        const int xlo = xf ? xf[ox0] : ox0;
+        const int xhi = xf ? xf[ox0 + kUnitPx - 1] + xf[dst_w + ox0 + kUnitPx - 1] : ox0 + kUnitPx;
+        const int quads = (xhi - xlo + 3) >> 2;  // staged 4 pixels at a time
+        const int spitch = 4 * quads;             // <= a.stage_dwords (the host checked)
+        const bool xw_in_lds = xf && kUnitPx * d.kx <= a.xw_budget;
+        if (xf) {
+            for (int i = tid; i < kUnitPx; i += kHfThreads) {
+                xfirst_s[i] = xf[ox0 + i] - xlo;
+                xcount_s[i] = xf[dst_w + ox0 + i];
+            }
+            if (xw_in_lds)
+                for (int i = tid; i < kUnitPx * d.kx; i += kHfThreads)
+                    xw_s[i] = xf[2 * dst_w + int64_t(ox0) * d.kx + i];
         }
-        if (xw_in_lds)
-            for (int i = tid; i < kUnitPx * d.kx; i += kHfThreads)
-                xw_s[i] = xf[2 * dst_w + int64_t(ox0) * d.kx + i];
-    }
-    const bool yw_in_lds = yf && G * d.ky <= a.yw_budget;
-    {
+        const bool yw_in_lds = yf && G * d.ky <= a.yw_budget;
         const int oy_a = oy0 + g0, oy_b = oy_a + G - 1;
         const int ylo = yf ? yf[oy_a] : oy_a;
         const int yhi = yf ? yf[oy_b] + yf[dst_h + oy_b] : oy_b + 1;
@@ -312,7 +311,6 @@ __global__ __launch_bounds__(kHfThreads) void hf_preprocess_kernel(HfArgs a) {
             block[(g0 + r) * kUnitPx + x] = px;
         }
         __syncthreads();
-    }
     }
 
     // The group's G pixel rows x 2 patch columns x 3 channels x 4 quads of 4
