@@ -387,7 +387,7 @@ int mimo_fold_patch_weights(int32_t embed_dim, const void *w, void *w_folded, vo
  *              [E][768] (folded = 1: only the tt = 0 half of every row is
  *              read, which is exact only for rows whose two frames are
  *              equal), 16-byte aligned.
- *   bias       device float32 [E], or NULL.
+ *   bias       device float32 [E], 16-byte aligned, or NULL.
  *   out        device [n_rows][E] of out_dtype (MIMO_F32 or MIMO_BF16,
  *              rounded to nearest even), 16-byte aligned.
  * Returns MIMO_OK, MIMO_E_INVALID, MIMO_E_TOO_LARGE or MIMO_E_HIP.
