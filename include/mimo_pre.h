@@ -268,7 +268,7 @@ int mimo_rope_inv_freq(int32_t rope_dim, double theta, float *inv);
  *   rope_dim   table width: a multiple of 8 in [8, MIMO_ROPE_DIM_MAX]
  *              (head_dim / 2 of the tower; 32 for head_dim 64).
  *   theta      rotary base (10000 in the tower).
- *   pos_hw     device int32 [rows][2] (h, w), or NULL.
+ *   pos_hw     device int32 [rows][2] (h, w), 8-byte aligned, or NULL.
  *   rope_cos, rope_sin  device float32 [rows][rope_dim], or NULL: column k <
  *              rope_dim / 2 holds cos / sin of float32(h * inv_freq[k]),
  *              column rope_dim / 2 + k the same for w (the h half, then the w
@@ -277,7 +277,8 @@ int mimo_rope_inv_freq(int32_t rope_dim, double theta, float *inv);
  *   capacity_rows  rows the outputs hold (>= the plan's total).
  *   workspace  device, >= mimo_workspace_bytes(n), 16-byte aligned.
  * At least one output must be given.  Returns MIMO_OK, MIMO_E_INVALID,
- * MIMO_E_CAPACITY or MIMO_E_HIP.
+ * MIMO_E_CAPACITY, MIMO_E_TOO_LARGE (an item with more than 2^24 rows, or
+ * more than 2^31 - 1 workgroup tiles) or MIMO_E_HIP.
  */
 int mimo_rotary_tables(int32_t n, const mimo_image_desc *desc, int32_t order, int32_t rope_dim,
                        double theta, int32_t *pos_hw, float *rope_cos, float *rope_sin,
@@ -292,10 +293,12 @@ int mimo_rotary_tables(int32_t n, const mimo_image_desc *desc, int32_t order, in
  * temporal slice, units listed by (block col, block row) -- the unit-level
  * form of mimo_column_permutation.  inverse[src] = dst undoes it.
  * Applying it (_apply_merge_index) is a gather of whole units.
- *   index, inverse  device int64 [units], either may be NULL (not both).
+ *   index, inverse  device int64 [units], 8-byte aligned; either may be NULL
+ *              (not both).
  *   capacity_units  entries the outputs hold (>= total rows / 4).
  *   workspace  device, >= mimo_workspace_bytes(n), 16-byte aligned.
- * Returns MIMO_OK, MIMO_E_INVALID, MIMO_E_CAPACITY or MIMO_E_HIP.
+ * Returns MIMO_OK, MIMO_E_INVALID, MIMO_E_CAPACITY, MIMO_E_TOO_LARGE (as for
+ * mimo_rotary_tables) or MIMO_E_HIP.
  */
 int mimo_window_index(int32_t n, const mimo_image_desc *desc, int32_t column_major,
                       int64_t *index, int64_t *inverse, int64_t capacity_units, void *workspace,
