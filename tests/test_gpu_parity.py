@@ -129,6 +129,26 @@ def test_ragged_small_batch_full(V, out_dtype):
     _check_properties(out)
 
 
+@pytest.mark.parametrize("seed", [91, 92])
+def test_random_shapes_full(V, seed):
+    """120 random images: sides log-uniform in [1, 700] on each axis (so
+    every branch of smart_resize, upscales, downscales and identity on a
+    multiple of 32 all occur), RGB and RGBA, both row orders, every row
+    compared with the oracle."""
+    rng = np.random.default_rng(seed)
+    shapes = []
+    for _ in range(120):
+        h, w = (int(np.exp(rng.uniform(0.0, np.log(700.0)))) for _ in range(2))
+        if rng.random() < 0.1:  # land some on multiples of 32 (identity resize)
+            h, w = 32 * max(3, h // 32), 32 * max(3, w // 32)
+        shapes.append((max(h, 1), max(w, 1), int(rng.choice([3, 4]))))
+    _say("random shapes", seed)
+    b = W.uniform_images(shapes, seed=seed)
+    plan, out = _run(V, b, "f32", merge=True, column=True, check=False)
+    _check_full(V, b, plan, out, "f32", column=True)
+    _check_properties(out)
+
+
 def test_rgba_content_and_alpha_extremes(V):
     _say("rgba extremes")
     rng = np.random.default_rng(5)
