@@ -97,6 +97,25 @@ __device__ __forceinline__ uint32_t round_clip_byte(int32_t acc) {
     return uint32_t(v < 0 ? 0 : (v > 255 ? 255 : v));
 }
 
+typedef const __attribute__((address_space(3))) int32_t *lds_weights;
+
+// One resampled pixel: count taps of px[j * stride] (RGB bytes in a dword,
+// in LDS) weighted by w[j], summed per channel in int32 and rounded back to
+// a byte.  The weights come from LDS or from memory; the two are separate
+// overloads so that neither goes through flat (generic) addressing.
+template <typename Weights>
+__device__ __forceinline__ uint32_t resample_px(const uint32_t *px, int stride, Weights w, int count) {
+    int32_t acc0 = 0, acc1 = 0, acc2 = 0;
+    for (int j = 0; j < count; ++j) {
+        const uint32_t p = px[j * stride];
+        const int32_t wj = w[j];
+        acc0 += int32_t(p & 255u) * wj;
+        acc1 += int32_t((p >> 8) & 255u) * wj;
+        acc2 += int32_t((p >> 16) & 255u) * wj;
+    }
+    return round_clip_byte(acc0) | (round_clip_byte(acc1) << 8) | (round_clip_byte(acc2) << 16);
+}
+
 // A raw buffer resource over [base & ~3, src_end): reads past the end
 // return zero.  `lead` is base's offset inside it.
 struct SrcWindow {
@@ -272,16 +291,10 @@ __global__ __launch_bounds__(kHfThreads) void hf_preprocess_kernel(HfArgs a) {
                 uint32_t px;
                 if (xf) {
                     const int first = xfirst_s[x], count = xcount_s[x];
-                    const int32_t *w = xw_in_lds ? &xw_s[x * d.kx]
-                                                 : xf + 2 * dst_w + int64_t(ox0 + x) * d.kx;
-                    int32_t acc0 = 0, acc1 = 0, acc2 = 0;
-                    for (int j = 0; j < count; ++j) {
-                        const uint32_t p = line[first + j];
-                        acc0 += int32_t(p & 255u) * w[j];
-                        acc1 += int32_t((p >> 8) & 255u) * w[j];
-                        acc2 += int32_t((p >> 16) & 255u) * w[j];
-                    }
-                    px = round_clip_byte(acc0) | (round_clip_byte(acc1) << 8) | (round_clip_byte(acc2) << 16);
+                    if (xw_in_lds)
+                        px = resample_px(line + first, 1, (lds_weights)(&xw_s[x * d.kx]), count);
+                    else
+                        px = resample_px(line + first, 1, xf + 2 * dst_w + int64_t(ox0 + x) * d.kx, count);
                 } else {
                     px = line[x];
                 }
@@ -296,15 +309,11 @@ __global__ __launch_bounds__(kHfThreads) void hf_preprocess_kernel(HfArgs a) {
             uint32_t px;
             if (yf) {
                 const int first = yfirst_s[r], count = ycount_s[r];
-                const int32_t *w = yw_in_lds ? &yw_s[r * d.ky] : yf + 2 * dst_h + int64_t(oy) * d.ky;
-                int32_t acc0 = 0, acc1 = 0, acc2 = 0;
-                for (int j = 0; j < count; ++j) {
-                    const uint32_t p = mid[(first + j) * kUnitPx + x];
-                    acc0 += int32_t(p & 255u) * w[j];
-                    acc1 += int32_t((p >> 8) & 255u) * w[j];
-                    acc2 += int32_t((p >> 16) & 255u) * w[j];
-                }
-                px = round_clip_byte(acc0) | (round_clip_byte(acc1) << 8) | (round_clip_byte(acc2) << 16);
+                const uint32_t *col = &mid[first * kUnitPx + x];
+                if (yw_in_lds)
+                    px = resample_px(col, kUnitPx, (lds_weights)(&yw_s[r * d.ky]), count);
+                else
+                    px = resample_px(col, kUnitPx, yf + 2 * dst_h + int64_t(oy) * d.ky, count);
             } else {
                 px = mid[idx];
             }
