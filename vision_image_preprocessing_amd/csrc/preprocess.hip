@@ -368,7 +368,7 @@ __device__ __forceinline__ Band tile_band(const PreArgs &a, const DevImage &d, c
     b.c_end = make_tap(d.scale_x, g.ox_last, d.src_w).i0 + 1;
     b.rows = r_end - b.r_lo + 1;
     b.groups = (b.c_end - b.c_lo + 4) >> 2;
-    b.pitch = 4 * b.groups;
+    b.pitch = 4 * (b.groups | 1);  // an odd number of 16-byte groups spreads rows over the banks
     b.fits = int64_t(b.rows) * b.pitch <= a.band_capacity &&
              int64_t(b.rows) * d.src_w * d.channels < 0x7FFF0000ll;
     return b;
