@@ -303,6 +303,70 @@ __device__ __forceinline__ void bilinear_patch(const Pixels &px, const DevImage 
     for (int c = 0; c < 3; ++c) store_frames<TT>(dst, c, v[c]);
 }
 
+// Four consecutive pixels as dwords R | G<<8 | B<<16 (RGBA flattened onto
+// white) from the 16 bytes `v` at a dword boundary, the dword `v4` after
+// them (RGBA only) and the pixels' byte offset `sh` (0..3) past that
+// boundary.
+template <int C>
+__device__ __forceinline__ u32x4 unpack_4px(const u32x4 &v, uint32_t v4, uint32_t sh) {
+    if (C == 3) {
+        const uint32_t u0 = __builtin_amdgcn_alignbyte(v.y, v.x, sh);
+        const uint32_t u1 = __builtin_amdgcn_alignbyte(v.z, v.y, sh);
+        const uint32_t u2 = __builtin_amdgcn_alignbyte(v.w, v.z, sh);
+        // bytes R0 G0 B0 R1 | G1 B1 R2 G2 | B2 R3 G3 B3 -> one pixel per dword
+        return u32x4{u0 & 0x00FFFFFFu, __builtin_amdgcn_perm(u1, u0, 0x0C050403u),
+                     __builtin_amdgcn_perm(u2, u1, 0x0C040302u), u2 >> 8};
+    } else {
+        return u32x4{flatten_rgba(__builtin_amdgcn_alignbyte(v.y, v.x, sh)),
+                     flatten_rgba(__builtin_amdgcn_alignbyte(v.z, v.y, sh)),
+                     flatten_rgba(__builtin_amdgcn_alignbyte(v.w, v.z, sh)),
+                     flatten_rgba(__builtin_amdgcn_alignbyte(v4, v.w, sh))};
+    }
+}
+
+// This thread's share of a band: pixel group g (4 pixels) of band rows r0,
+// r0 + step, ... below `rows`.  The loads of kStageBatch rows go out
+// together before any of them is unpacked, so a thread waits for one memory
+// round trip per kStageBatch rows.  No load is conditional: a row past the
+// band gets an offset past the buffer's range, which reads zero without a
+// memory access, and is not written.
+#ifndef MIMO_STAGE_BATCH
+#define MIMO_STAGE_BATCH 4
+#endif
+constexpr int kStageBatch = MIMO_STAGE_BATCH;
+constexpr uint32_t kOutOfRange = 0x80000000u;  // past any window's range
+template <int C>
+__device__ __forceinline__ void stage_rows(uint32_t *band, const SourceWindow &w, int64_t row_bytes,
+                                           int r0, int step, int rows, int last_row, int g, int pitch) {
+    const uint32_t col_bytes = w.lead + uint32_t(g * 4 * C);
+    for (int r = r0; r < rows; r += kStageBatch * step) {
+        u32x4 v[kStageBatch];
+        uint32_t v4[kStageBatch], sh[kStageBatch];
+#pragma unroll
+        for (int i = 0; i < kStageBatch; ++i) {
+            const int sr = min(r + i * step, last_row);
+            const uint32_t off = col_bytes + uint32_t(int64_t(sr) * row_bytes);
+            sh[i] = off & 3u;
+            const uint32_t at = r + i * step < rows ? off & ~3u : kOutOfRange;
+            v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.rsrc, int(at), 0, 0));
+            v4[i] = C == 4 ? __builtin_amdgcn_raw_buffer_load_b32(w.rsrc, int(at) + 16, 0, 0) : 0u;
+        }
+        // The batch is consumed here, all at once: otherwise the compiler
+        // moves each load into the branch that writes its row, behind a
+        // wait for the loads before it.
+#pragma unroll
+        for (int i = 0; i < kStageBatch; ++i) {
+            asm volatile("" : "+v"(v[i]));
+            if (C == 4) asm volatile("" : "+v"(v4[i]));
+        }
+#pragma unroll
+        for (int i = 0; i < kStageBatch; ++i)
+            if (r + i * step < rows)
+                *reinterpret_cast<u32x4 *>(band + (r + i * step) * pitch + 4 * g) =
+                    unpack_4px<C>(v[i], v4[i], sh[i]);
+    }
+}
+
 // Stages source rows [r_lo, r_lo + rows) x columns [c_lo, c_lo + 4*groups)
 // into LDS, one dword per pixel.  Rows past the last image row repeat it;
 // a column past the last image column is patched afterwards.
@@ -322,13 +386,10 @@ __device__ __forceinline__ void stage_band(uint32_t *band, const PreArgs &a, con
         const int r0 = div_small(threadIdx.x, groups, 1.0f / float(groups));
         const int g = threadIdx.x - r0 * groups;
         if (r0 < step) {
-            for (int r = r0; r < rows; r += step) {
-                const int sr = min(r, last_row);
-                uint32_t p[4];
-                load_4px(w, w.lead + uint32_t(int64_t(sr) * row_bytes) + uint32_t(g * 4 * C), C, p);
-                const u32x4 o = {p[0], p[1], p[2], p[3]};
-                *reinterpret_cast<u32x4 *>(band + r * pitch + 4 * g) = o;
-            }
+            if (C == 3)
+                stage_rows<3>(band, w, row_bytes, r0, step, rows, last_row, g, pitch);
+            else
+                stage_rows<4>(band, w, row_bytes, r0, step, rows, last_row, g, pitch);
         }
     } else {
         for (int i = threadIdx.x; i < rows * groups; i += nthreads) {
