@@ -55,7 +55,7 @@ constexpr int kWeightBits = 22;           // fractional bits of the resampler's 
 constexpr int kMidRows = 256;             // most LDS band rows (32 pixels each)
 constexpr int kStageDwords = 4096;        // most LDS source staging (one dword per pixel)
 constexpr int kTapBudget = 2048;          // most LDS weights per axis (else they are read from memory)
-constexpr int kFixedDwords = 3 * 256 + kUnitPx * kUnitPx + 4 * kUnitPx;  // lut, block, first/count
+constexpr int kFixedDwords = 3 * 256 + kUnitPx * kUnitPx + 2 * kUnitPx;  // lut, block, first x/y
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer resource word 3 (gfx9 family)
 
 // Per-item record of the contrast kernel (64 bytes).
@@ -99,16 +99,21 @@ __device__ __forceinline__ uint32_t round_clip_byte(int32_t acc) {
 
 typedef const __attribute__((address_space(3))) int32_t *lds_weights;
 
-// One resampled pixel: count taps of px[j * stride] (RGB bytes in a dword,
+// One resampled pixel: `taps` taps of px[j * stride] (RGB bytes in a dword,
 // in LDS) weighted by w[j], summed per channel in int32 and rounded back to
-// a byte.  The weights come from LDS or from memory; the two are separate
-// overloads so that neither goes through flat (generic) addressing.
+// a byte.  `taps` is the same for every output of an axis (unused taps have
+// zero weight), so the loop is uniform across the wavefront.  The weights
+// have kWeightBits fraction bits and magnitude below 2, so they are 24-bit
+// signed values: said so explicitly, the products run on the full-rate
+// 24-bit multiplier instead of a 64-bit multiply-add.  The weights come from
+// LDS or from memory; the two are separate overloads so that neither goes
+// through flat (generic) addressing.
 template <typename Weights>
-__device__ __forceinline__ uint32_t resample_px(const uint32_t *px, int stride, Weights w, int count) {
+__device__ __forceinline__ uint32_t resample_px(const uint32_t *px, int stride, Weights w, int taps) {
     int32_t acc0 = 0, acc1 = 0, acc2 = 0;
-    for (int j = 0; j < count; ++j) {
+    for (int j = 0; j < taps; ++j) {
         const uint32_t p = px[j * stride];
-        const int32_t wj = w[j];
+        const int32_t wj = __builtin_amdgcn_sbfe(w[j], 0, 24);
         acc0 += int32_t(p & 255u) * wj;
         acc1 += int32_t((p >> 8) & 255u) * wj;
         acc2 += int32_t((p >> 16) & 255u) * wj;
@@ -196,9 +201,8 @@ __global__ __launch_bounds__(kHfThreads) void hf_preprocess_kernel(HfArgs a) {
     float *lut = reinterpret_cast<float *>(lds);                     // [3][256]
     uint32_t *block = lds + 3 * 256;                                  // the unit's output bytes (RGB per dword)
     int32_t *xfirst_s = reinterpret_cast<int32_t *>(block + kUnitPx * kUnitPx);  // the tile's taps: first
-    int32_t *xcount_s = xfirst_s + kUnitPx;                           // (relative to the staged block /
-    int32_t *yfirst_s = xcount_s + kUnitPx;                           // band), count, weights
-    int32_t *ycount_s = yfirst_s + kUnitPx;
+    int32_t *yfirst_s = xfirst_s + kUnitPx;                           // (relative to the staged block /
+                                                                      // band) and weights
     int32_t *xw_s = reinterpret_cast<int32_t *>(lds + kFixedDwords);
     int32_t *yw_s = xw_s + a.xw_budget;
     uint32_t *mid = reinterpret_cast<uint32_t *>(yw_s + a.yw_budget);  // horizontal-pass band
@@ -245,10 +249,7 @@ __global__ __launch_bounds__(kHfThreads) void hf_preprocess_kernel(HfArgs a) {
         const int spitch = 4 * quads;             // <= a.stage_dwords (the host checked)
         const bool xw_in_lds = xf && kUnitPx * d.kx <= a.xw_budget;
         if (xf) {
-            for (int i = tid; i < kUnitPx; i += kHfThreads) {
-                xfirst_s[i] = xf[ox0 + i] - xlo;
-                xcount_s[i] = xf[dst_w + ox0 + i];
-            }
+            for (int i = tid; i < kUnitPx; i += kHfThreads) xfirst_s[i] = xf[ox0 + i] - xlo;
             if (xw_in_lds)
                 for (int i = tid; i < kUnitPx * d.kx; i += kHfThreads)
                     xw_s[i] = xf[2 * dst_w + int64_t(ox0) * d.kx + i];
@@ -259,10 +260,7 @@ __global__ __launch_bounds__(kHfThreads) void hf_preprocess_kernel(HfArgs a) {
         const int yhi = yf ? yf[oy_b] + yf[dst_h + oy_b] : oy_b + 1;
         const int nrows = yhi - ylo;  // <= a.mid_rows (the host sized G)
         if (yf) {
-            for (int i = tid; i < G; i += kHfThreads) {
-                yfirst_s[i] = yf[oy_a + i] - ylo;
-                ycount_s[i] = yf[dst_h + oy_a + i];
-            }
+            for (int i = tid; i < G; i += kHfThreads) yfirst_s[i] = yf[oy_a + i] - ylo;
             if (yw_in_lds)
                 for (int i = tid; i < G * d.ky; i += kHfThreads)
                     yw_s[i] = yf[2 * dst_h + int64_t(oy_a) * d.ky + i];
@@ -290,11 +288,11 @@ __global__ __launch_bounds__(kHfThreads) void hf_preprocess_kernel(HfArgs a) {
                 const uint32_t *line = &stage[r * spitch];
                 uint32_t px;
                 if (xf) {
-                    const int first = xfirst_s[x], count = xcount_s[x];
+                    const int first = xfirst_s[x];
                     if (xw_in_lds)
-                        px = resample_px(line + first, 1, (lds_weights)(&xw_s[x * d.kx]), count);
+                        px = resample_px(line + first, 1, (lds_weights)(&xw_s[x * d.kx]), d.kx);
                     else
-                        px = resample_px(line + first, 1, xf + 2 * dst_w + int64_t(ox0 + x) * d.kx, count);
+                        px = resample_px(line + first, 1, xf + 2 * dst_w + int64_t(ox0 + x) * d.kx, d.kx);
                 } else {
                     px = line[x];
                 }
@@ -308,12 +306,11 @@ __global__ __launch_bounds__(kHfThreads) void hf_preprocess_kernel(HfArgs a) {
             const int oy = oy_a + r;
             uint32_t px;
             if (yf) {
-                const int first = yfirst_s[r], count = ycount_s[r];
-                const uint32_t *col = &mid[first * kUnitPx + x];
+                const uint32_t *col = &mid[yfirst_s[r] * kUnitPx + x];
                 if (yw_in_lds)
-                    px = resample_px(col, kUnitPx, (lds_weights)(&yw_s[r * d.ky]), count);
+                    px = resample_px(col, kUnitPx, (lds_weights)(&yw_s[r * d.ky]), d.ky);
                 else
-                    px = resample_px(col, kUnitPx, yf + 2 * dst_h + int64_t(oy) * d.ky, count);
+                    px = resample_px(col, kUnitPx, yf + 2 * dst_h + int64_t(oy) * d.ky, d.ky);
             } else {
                 px = mid[idx];
             }
@@ -367,18 +364,22 @@ int axis_taps_per_output(int64_t n_in, int64_t n_out) {
     return int(std::ceil(support)) * 2 + 1;
 }
 
-// Appends first[n_out], count[n_out], weights[n_out][k] of one axis.
-void append_axis_taps(int64_t n_in, int64_t n_out, std::vector<int32_t> &tab) {
+// Appends first[n_out], count[n_out], weights[n_out][k] of one axis and
+// returns k.  Every output gets the same k taps, the most any output of the
+// axis has: its window [first, first + k) is moved left where it would run
+// past the last input (its own taps then sit further right in the row), and
+// the weights it does not use are zero.  The kernel then runs one tap count
+// for every output and never reads outside the image; the sums are those
+// of the outputs' own taps, since the extra terms are zero.
+int append_axis_taps(int64_t n_in, int64_t n_out, std::vector<int32_t> &tab) {
     const double scale = double(n_in) / double(n_out);
     const double widen = scale < 1.0 ? 1.0 : scale;
     const double support = 2.0 * widen;
-    const int k = axis_taps_per_output(n_in, n_out);
-    const size_t base = tab.size();
-    tab.resize(base + size_t(n_out) * (2 + k), 0);
-    int32_t *first = tab.data() + base;
-    int32_t *count = first + n_out;
-    int32_t *weight = count + n_out;
-    std::vector<double> w(size_t(k) + 1);
+    const int k_max = axis_taps_per_output(n_in, n_out);
+    std::vector<int32_t> lo_of(static_cast<size_t>(n_out)), cnt_of(static_cast<size_t>(n_out));
+    std::vector<int32_t> wts(size_t(n_out) * k_max, 0);
+    std::vector<double> w(size_t(k_max) + 1);
+    int k = 1;
     for (int64_t i = 0; i < n_out; ++i) {
         const double centre = (double(i) + 0.5) * scale;
         int64_t lo = int64_t(centre - support + 0.5);
@@ -394,11 +395,26 @@ void append_axis_taps(int64_t n_in, int64_t n_out, std::vector<int32_t> &tab) {
         for (int64_t j = 0; j < cnt; ++j) {
             const double v = sum != 0.0 ? w[j] / sum : w[j];
             const double fixed = v * double(1 << kWeightBits);
-            weight[i * k + j] = int32_t(v < 0.0 ? fixed - 0.5 : fixed + 0.5);
+            wts[size_t(i) * k_max + j] = int32_t(v < 0.0 ? fixed - 0.5 : fixed + 0.5);
         }
-        first[i] = int32_t(lo);
-        count[i] = int32_t(cnt);
+        lo_of[i] = int32_t(lo);
+        cnt_of[i] = int32_t(cnt);
+        k = std::max<int>(k, int(cnt));
     }
+    const size_t base = tab.size();
+    tab.resize(base + size_t(n_out) * (2 + k), 0);
+    int32_t *first = tab.data() + base;
+    int32_t *count = first + n_out;
+    int32_t *weight = count + n_out;
+    for (int64_t i = 0; i < n_out; ++i) {
+        // k <= n_in, since no output has more taps than there are inputs
+        const int32_t lo = std::min<int32_t>(lo_of[i], int32_t(n_in - k));
+        const int32_t shift = lo_of[i] - lo;
+        for (int32_t j = 0; j < cnt_of[i]; ++j) weight[i * k + shift + j] = wts[size_t(i) * k_max + j];
+        first[i] = lo;
+        count[i] = k;
+    }
+    return k;
 }
 
 struct HfTables {
@@ -477,14 +493,12 @@ int build_hf_tables(int32_t n, const mimo_image_desc *desc, const float *mean01,
         d.blocks_w = s.dst_w / kUnitPx;
         d.group = kUnitPx;
         if (s.dst_w != s.src_w) {
-            d.kx = axis_taps_per_output(s.src_w, s.dst_w);
             d.x_tab = int64_t(out.taps.size());
-            append_axis_taps(s.src_w, s.dst_w, out.taps);
+            d.kx = append_axis_taps(s.src_w, s.dst_w, out.taps);
         }
         if (s.dst_h != s.src_h) {
-            d.ky = axis_taps_per_output(s.src_h, s.dst_h);
             d.y_tab = int64_t(out.taps.size());
-            append_axis_taps(s.src_h, s.dst_h, out.taps);
+            d.ky = append_axis_taps(s.src_h, s.dst_h, out.taps);
             const int32_t *yfirst = out.taps.data() + d.y_tab;
             d.group = choose_group(yfirst, yfirst + s.dst_h, s.dst_h);
             if (d.group == 0)
