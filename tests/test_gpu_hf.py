@@ -96,6 +96,23 @@ def test_ragged_batch_bitwise(V, out_dtype):
     _check(V, b, plan, out, out_dtype)
 
 
+@pytest.mark.parametrize("seed", [93, 94])
+def test_random_shapes_bitwise(V, seed):
+    """60 random images: sides log-uniform in [1, 700] on each axis, so
+    upscales of sides shorter than the tap count, mild and strong
+    downscales and sizes the stock geometry leaves alone all occur; RGB and
+    RGBA, both orders, every row compared with the oracle bit for bit."""
+    rng = np.random.default_rng(seed)
+    shapes = []
+    for _ in range(60):
+        h, w = (int(np.exp(rng.uniform(0.0, np.log(700.0)))) for _ in range(2))
+        shapes.append((max(h, 1), max(w, 1), int(rng.choice([3, 4]))))
+    _say("random shapes", seed)
+    b = W.uniform_images(shapes, seed=seed)
+    plan, out = _run(V, b, "f32", merge=True, column=True)
+    _check(V, b, plan, out, "f32")
+
+
 def test_column_order_only(V):
     _say("column only")
     b = W.uniform_images(SHAPES[:8], seed=82)
