@@ -26,10 +26,13 @@
 // the kernel is bound by how fast a CU takes its tiles from L2, so the
 // loads go out early, in the first half of each stage and spread between
 // the MFMAs.  The tile is written back through LDS so that every store
-// covers whole row segments (non-temporal, 16 bytes per lane); W is the
-// MFMA's first operand, which gives each lane four consecutive output
-// columns to stage.  Tiles are ordered N fastest and assigned to XCDs in
-// contiguous runs, so one XCD's L2 serves an A tile to all of its N tiles.
+// covers whole row segments (non-temporal, 16 bytes per lane): the fp32
+// accumulators are staged, and each lane adds the bias of its own output
+// columns (the same for every row it stores, loaded once) on the way out.
+// W is the MFMA's first operand, which gives each lane four consecutive
+// output columns to stage.  Tiles are ordered N fastest and assigned to
+// XCDs in contiguous runs, so one XCD's L2 serves an A tile to all of its N
+// tiles.
 #include <hip/hip_runtime.h>
 
 #include <cstring>
@@ -74,16 +77,6 @@ __device__ __forceinline__ int a_column(int k0, bool folded) {
     return folded ? (k0 / kFoldSeg) * kFoldStride + k0 % kFoldSeg : k0;
 }
 
-// Four consecutive outputs of one row (into the LDS staging area).
-__device__ __forceinline__ void store_out4(float *p, const f32x4 &v) {
-    *reinterpret_cast<f32x4 *>(p) = v;
-}
-__device__ __forceinline__ void store_out4(uint16_t *p, const f32x4 &v) {
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-    const bf16x4 h = {__bf16(v.x), __bf16(v.y), __bf16(v.z), __bf16(v.w)};  // nearest even
-    *reinterpret_cast<bf16x4 *>(p) = h;
-}
-
 // Swizzle key of LDS row r: the same logical chunk of rows r .. r + 7 lands
 // in 8 distinct 16-byte positions, and that of rows r .. r + 15 in 16
 // distinct (row parity, position) pairs, so a 16-byte read by 8 or by 16
@@ -98,6 +91,87 @@ constexpr int kWaitAll = 0;                 // every counter at zero
 constexpr int kWaitVmemButA = 0x0F78;       // vmcnt(8): one stage of A loads may stay in flight
 constexpr int kWaitLdsVmemButA = 0x0078;    // lgkmcnt(0) and vmcnt(8)
 constexpr int kWaitLdsVmem = 0x0070;        // lgkmcnt(0) and vmcnt(0)
+
+// Output columns one lane writes per 16-byte store, and the lanes per
+// staged row.
+template <typename OutT>
+struct EpilogueShape {
+    static constexpr int kOutPerChunk = 16 / int(sizeof(OutT));  // 4 fp32 or 8 bf16
+    static constexpr int kLanesPerRow = kWaveN / kOutPerChunk;   // 32 or 16
+    static constexpr int kRowsPerPass = 64 / kLanesPerRow;       // 2 or 4
+};
+
+// The bias of the output columns this lane stores (the same for every row
+// it stores), or zeros.
+template <typename OutT>
+__device__ __forceinline__ void load_lane_bias(const float *bias, int col0, int lane,
+                                               f32x4 (&bv)[EpilogueShape<OutT>::kOutPerChunk / 4]) {
+    constexpr int kOut = EpilogueShape<OutT>::kOutPerChunk;
+    const int chunk = lane % EpilogueShape<OutT>::kLanesPerRow;
+#pragma unroll
+    for (int k = 0; k < kOut / 4; ++k)
+        bv[k] = bias ? *reinterpret_cast<const f32x4 *>(bias + col0 + chunk * kOut + 4 * k) : f32x4{};
+}
+
+// One 16-byte store of converted outputs.
+__device__ __forceinline__ u32x4 pack_out(const f32x4 (&v)[1], float *) {
+    return __builtin_bit_cast(u32x4, v[0]);
+}
+__device__ __forceinline__ u32x4 pack_out(const f32x4 (&v)[2], uint16_t *) {
+    typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+    const bf16x8 h = {__bf16(v[0].x), __bf16(v[0].y), __bf16(v[0].z), __bf16(v[0].w),
+                      __bf16(v[1].x), __bf16(v[1].y), __bf16(v[1].z), __bf16(v[1].w)};  // nearest even
+    return __builtin_bit_cast(u32x4, h);
+}
+
+// A wave's 128 x 128 block to memory.  Per 32-row block row, the fp32
+// accumulators are staged in the wave's 16 KB LDS region (rows of 512
+// bytes, 16-byte chunks XOR-swizzled by the row so that the 32 rows a
+// staging store covers fall in distinct chunks); then each lane reads whole
+// row segments back, adds the bias of its columns (bv), converts and
+// writes 16 bytes, non-temporal.  With W as the MFMA's first operand, value
+// q of block (i, j) is row (lane % 32) of A block i and column 8 * (q / 4) +
+// 4 * (lane / 32) + q % 4 of W block j.
+template <typename OutT>
+__device__ __forceinline__ void write_block(const f32x16 (&acc)[kBlocksM][kBlocksN], uint8_t *region,
+                                            const f32x4 (&bv)[EpilogueShape<OutT>::kOutPerChunk / 4],
+                                            OutT *out, int64_t row0, int col0, int64_t n_rows, int embed_dim,
+                                            int lane) {
+    typedef EpilogueShape<OutT> S;
+    constexpr int kRowBytes = kWaveN * 4;  // fp32 staging
+    constexpr int kChunks = kRowBytes / 16;
+    static_assert(32 * kRowBytes == 16384, "a wave stages 16 KB");
+    const bool full = row0 + kWaveM <= n_rows;
+    const int chunk = lane % S::kLanesPerRow;
+#pragma unroll
+    for (int i = 0; i < kBlocksM; ++i) {
+        const int r = lane & 31;
+#pragma unroll
+        for (int j = 0; j < kBlocksN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int c = j * 8 + 2 * g + (lane >> 5);  // 16-byte chunk of 4 columns
+                const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                 acc[i][j][4 * g + 3]};
+                *reinterpret_cast<f32x4 *>(region + r * kRowBytes + ((c ^ r) % kChunks) * 16) = v;
+            }
+#pragma unroll
+        for (int p = 0; p < 32 / S::kRowsPerPass; ++p) {
+            const int rr = p * S::kRowsPerPass + lane / S::kLanesPerRow;
+            f32x4 v[S::kOutPerChunk / 4];
+#pragma unroll
+            for (int k = 0; k < S::kOutPerChunk / 4; ++k) {
+                const int c = chunk * (S::kOutPerChunk / 4) + k;
+                v[k] = *reinterpret_cast<const f32x4 *>(region + rr * kRowBytes + ((c ^ rr) % kChunks) * 16) + bv[k];
+            }
+            const int64_t row = row0 + i * 32 + rr;
+            if (full || row < n_rows)
+                __builtin_nontemporal_store(pack_out(v, static_cast<OutT *>(nullptr)),
+                                            reinterpret_cast<u32x4 *>(out + row * embed_dim + col0 +
+                                                                      chunk * S::kOutPerChunk));
+        }
+    }
+}
 
 // kFolded: K = 768 over the tt = 0 half of each row, else K = 1536.  K is
 // a compile-time constant so that the stage loop unrolls fully: every
@@ -264,44 +338,16 @@ __global__ __launch_bounds__(kEmbedThreads) void patch_embed_kernel(EmbedArgs a)
     barrier();
 
     // Epilogue through LDS, free now that every wave has passed the last
-    // stage's barrier.  Each wave stages its 128 x 128 block 32 rows at a
-    // time in a private region (one of the four stage arrays), then writes
-    // whole row segments, 16 bytes per lane, with non-temporal stores.  With
-    // W as the first operand, value q of block (i, j) is row (lane % 32) of
-    // A block i and column 8 * (q / 4) + 4 * (lane / 32) + q % 4 of W block j.
-    OutT *out = static_cast<OutT *>(a.out);
-    const bool full_tile = m0 + kBM <= a.n_rows;
-    constexpr int kRowBytes = kWaveN * int(sizeof(OutT));  // one staged row
-    constexpr int kStride = kRowBytes + 16;                // padded against bank conflicts
-    constexpr int kLanesPerRow = kRowBytes / 16;
-    constexpr int kRowsPerPass = 64 / kLanesPerRow;
-    static_assert(32 * kStride <= kBM * kBK * 2, "a wave's staging fits one stage array");
-    uint8_t *region = reinterpret_cast<uint8_t *>(wave == 0 ? sa0 : wave == 1 ? sa1 : wave == 2 ? sb0 : sb1);
+    // stage's barrier: each wave stages its block in half of one stage array.
+    uint8_t *region = reinterpret_cast<uint8_t *>(wave < 2 ? sa0 : sa1) + (wave & 1) * (kBM * kBK);
     const int col0 = n0 + wn * kWaveN;
+    f32x4 bv[EpilogueShape<OutT>::kOutPerChunk / 4];
+    load_lane_bias<OutT>(a.bias, col0, lane, bv);
+    // waited for here, once, so that no store of the epilogue waits on memory
 #pragma unroll
-    for (int i = 0; i < kBlocksM; ++i) {
-#pragma unroll
-        for (int j = 0; j < kBlocksN; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int c = j * 32 + 8 * g + 4 * (lane >> 5);
-                f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                           acc[i][j][4 * g + 3]};
-                if (a.bias) v += *reinterpret_cast<const f32x4 *>(a.bias + col0 + c);
-                store_out4(reinterpret_cast<OutT *>(region + (lane & 31) * kStride) + c, v);
-            }
-#pragma unroll
-        for (int p = 0; p < 32 / kRowsPerPass; ++p) {
-            const int r = p * kRowsPerPass + lane / kLanesPerRow;
-            const int chunk = lane % kLanesPerRow;
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(region + r * kStride + chunk * 16);
-            const int64_t row = m0 + wm * kWaveM + i * 32 + r;
-            if (full_tile || row < a.n_rows)
-                __builtin_nontemporal_store(
-                    v, reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(out + row * a.embed_dim + col0) +
-                                                 chunk * 16));
-        }
-    }
+    for (int k = 0; k < EpilogueShape<OutT>::kOutPerChunk / 4; ++k) asm volatile("" : "+v"(bv[k]));
+    write_block<OutT>(acc, region, bv, static_cast<OutT *>(a.out), m0 + wm * kWaveM, col0, a.n_rows, a.embed_dim,
+                      lane);
 }
 
 // W'[e][c][p] = bf16(W[e][c][0][p] + W[e][c][1][p]): the two bf16 values
