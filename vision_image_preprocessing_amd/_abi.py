@@ -115,6 +115,16 @@ def load() -> ctypes.CDLL:
             raise LibraryNotBuilt(
                 f"{LIB_PATH} is missing: build it with "
                 "`python -c 'import __graft_entry__ as g; g.build()'` (hipcc, gfx950)")
+        # torch ships its own HIP runtime under the same sonames as the
+        # system's; whichever loads first serves the whole process.  The
+        # device memory handed to the library comes from torch, so torch's
+        # runtime must be the one: import torch before opening the library
+        # (loaded first, the library would pull in the system runtime and
+        # torch would then find no device).
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         lib = ctypes.CDLL(LIB_PATH)
         for name, (args, res) in SIGNATURES.items():
             fn = getattr(lib, name)
