@@ -113,6 +113,18 @@ def test_random_shapes_bitwise(V, seed):
     _check(V, b, plan, out, "f32")
 
 
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_mild_resizes_bitwise(V, out_dtype):
+    """A batch of over 1024 tiles whose every resized axis has at most 5
+    taps per output (mild up- and downscales under the stock geometry) runs
+    in 256-thread workgroups; same bar."""
+    _say("mild resizes", out_dtype)
+    b = W.uniform_images([(200, 300, 3), (300, 200, 4), (250, 250, 3), (90, 500, 4), (1000, 700, 3),
+                          (1000, 1400, 4), (2000, 1500, 3)], seed=88)
+    plan, out = _run(V, b, out_dtype, merge=True, column=True)
+    _check(V, b, plan, out, out_dtype)
+
+
 def test_column_order_only(V):
     _say("column only")
     b = W.uniform_images(SHAPES[:8], seed=82)
