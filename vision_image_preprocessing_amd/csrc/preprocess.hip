@@ -564,14 +564,17 @@ __global__ __launch_bounds__(kThreads) void preprocess_kernel(PreArgs a) {
     }
 }
 
-// Column-order gather: one wavefront copies one merge unit (4 contiguous
-// rows) from its merge-order position to its column-order position.
+// Column-order gather: one workgroup copies one merge unit (4 contiguous
+// rows) from its merge-order position to its column-order position, one
+// wavefront per row; units go to XCDs in contiguous runs, as the fused
+// kernel's tiles do (4.55 ms for 2 x 12.9 GB, against 4.93 ms for a
+// wavefront per unit in dispatch order with one load in flight).
 template <typename OutT>
 __global__ __launch_bounds__(kThreads) void column_permute_kernel(PermArgs a) {
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
-    const int64_t unit = int64_t(blockIdx.x) * kWaves + wave;
-    if (unit >= a.total_units) return;  // wave-uniform
+    const int64_t unit = xcd_contiguous_tile(blockIdx.x, gridDim.x);
+    if (unit >= a.total_units) return;  // workgroup-uniform
     const int64_t drow = unit * kRowsPerUnit;
     const int img = find_segment(a.row_begin, a.n, drow);
     const DevImage d = a.images[img];
@@ -583,14 +586,18 @@ __global__ __launch_bounds__(kThreads) void column_permute_kernel(PermArgs a) {
     const int br = j - bc * d.blocks_h;
     const int64_t src_row =
         d.row_offset + (int64_t(t) * units + int64_t(br) * d.blocks_w + bc) * kRowsPerUnit;
-    constexpr int kVecs = kRowsPerUnit * kRowLen * int(sizeof(OutT)) / 16;  // 16-byte vectors per unit
-    const u32x4 *in = reinterpret_cast<const u32x4 *>(static_cast<const OutT *>(a.in) + src_row * kRowLen);
-    u32x4 *out = reinterpret_cast<u32x4 *>(static_cast<OutT *>(a.out) + drow * kRowLen);
-#pragma unroll 4
-    for (int i = lane; i < kVecs; i += 64) {
-        const u32x4 v = __builtin_nontemporal_load(in + i);
-        __builtin_nontemporal_store(v, out + i);
-    }
+    static_assert(kWaves == kRowsPerUnit, "one wavefront per row of the unit");
+    constexpr int kPerLane = kRowLen * int(sizeof(OutT)) / 16 / 64;  // 16-byte vectors: 6 (fp32) or 3 (bf16)
+    const u32x4 *in = reinterpret_cast<const u32x4 *>(static_cast<const OutT *>(a.in) + (src_row + wave) * kRowLen);
+    u32x4 *out = reinterpret_cast<u32x4 *>(static_cast<OutT *>(a.out) + (drow + wave) * kRowLen);
+    // All of the row's loads go out before any store: the compiler cannot
+    // move a load above a store to `out` (it may alias `in`), so a plain
+    // load-store loop would keep one load in flight.
+    u32x4 v[kPerLane];
+#pragma unroll
+    for (int k = 0; k < kPerLane; ++k) v[k] = __builtin_nontemporal_load(in + k * 64 + lane);
+#pragma unroll
+    for (int k = 0; k < kPerLane; ++k) __builtin_nontemporal_store(v[k], out + k * 64 + lane);
 }
 
 // ------------------------------------------------------------- host side
@@ -827,7 +834,7 @@ int mimo_column_permute(int32_t n, const mimo_image_desc *desc, const void *rows
         return set_error(MIMO_E_CAPACITY, "column_permute: capacity_rows below the total rows");
     if (t.total_rows == 0) return MIMO_OK;
     const int64_t units = t.total_rows / kRowsPerUnit;
-    const int64_t blocks = (units + kWaves - 1) / kWaves;
+    const int64_t blocks = units;
     if (blocks > 0x7FFFFFFFll)
         return set_error(MIMO_E_TOO_LARGE, "column_permute: too many merge units");
 
