@@ -324,46 +324,63 @@ __device__ __forceinline__ u32x4 unpack_4px(const u32x4 &v, uint32_t v4, uint32_
     }
 }
 
-// This thread's share of a band: pixel group g (4 pixels) of band rows r0,
-// r0 + step, ... below `rows`.  The loads of kStageBatch rows go out
-// together before any of them is unpacked, so a thread waits for one memory
-// round trip per kStageBatch rows.  No load is conditional: a row past the
-// band gets an offset past the buffer's range, which reads zero without a
-// memory access, and is not written.
+// Band staging is batched: a thread issues the loads of kStageBatch of its
+// band rows before it unpacks any of them, so it waits for one memory round
+// trip per kStageBatch rows.  No load is conditional: a row past the band
+// gets an offset past the buffer's range, which reads zero without a memory
+// access, and is not written.
 #ifndef MIMO_STAGE_BATCH
 #define MIMO_STAGE_BATCH 4
 #endif
 constexpr int kStageBatch = MIMO_STAGE_BATCH;
 constexpr uint32_t kOutOfRange = 0x80000000u;  // past any window's range
+// The loads of one batch of a thread's band rows (rows r, r + step, ...).
+struct RowBatch {
+    u32x4 v[kStageBatch];
+    uint32_t v4[kStageBatch], sh[kStageBatch];
+};
+
+template <int C>
+__device__ __forceinline__ void issue_rows(RowBatch &b, const SourceWindow &w, int64_t row_bytes,
+                                           uint32_t col_bytes, int r, int step, int rows, int last_row) {
+#pragma unroll
+    for (int i = 0; i < kStageBatch; ++i) {
+        const int sr = min(r + i * step, last_row);
+        const uint32_t off = col_bytes + uint32_t(int64_t(sr) * row_bytes);
+        b.sh[i] = off & 3u;
+        const uint32_t at = r + i * step < rows ? off & ~3u : kOutOfRange;
+        b.v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.rsrc, int(at), 0, 0));
+        b.v4[i] = C == 4 ? __builtin_amdgcn_raw_buffer_load_b32(w.rsrc, int(at) + 16, 0, 0) : 0u;
+    }
+}
+
+template <int C>
+__device__ __forceinline__ void write_rows(uint32_t *band, RowBatch &b, int r, int step, int rows, int g,
+                                           int pitch) {
+    // The batch is consumed here, all at once: otherwise the compiler
+    // moves each load into the branch that writes its row, behind a wait
+    // for the loads before it.
+#pragma unroll
+    for (int i = 0; i < kStageBatch; ++i) {
+        asm volatile("" : "+v"(b.v[i]));
+        if (C == 4) asm volatile("" : "+v"(b.v4[i]));
+    }
+#pragma unroll
+    for (int i = 0; i < kStageBatch; ++i)
+        if (r + i * step < rows)
+            *reinterpret_cast<u32x4 *>(band + (r + i * step) * pitch + 4 * g) = unpack_4px<C>(b.v[i], b.v4[i], b.sh[i]);
+}
+
+// This thread's share of a band: pixel group g (4 pixels) of band rows r0,
+// r0 + step, ... below `rows`.
 template <int C>
 __device__ __forceinline__ void stage_rows(uint32_t *band, const SourceWindow &w, int64_t row_bytes,
                                            int r0, int step, int rows, int last_row, int g, int pitch) {
     const uint32_t col_bytes = w.lead + uint32_t(g * 4 * C);
     for (int r = r0; r < rows; r += kStageBatch * step) {
-        u32x4 v[kStageBatch];
-        uint32_t v4[kStageBatch], sh[kStageBatch];
-#pragma unroll
-        for (int i = 0; i < kStageBatch; ++i) {
-            const int sr = min(r + i * step, last_row);
-            const uint32_t off = col_bytes + uint32_t(int64_t(sr) * row_bytes);
-            sh[i] = off & 3u;
-            const uint32_t at = r + i * step < rows ? off & ~3u : kOutOfRange;
-            v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.rsrc, int(at), 0, 0));
-            v4[i] = C == 4 ? __builtin_amdgcn_raw_buffer_load_b32(w.rsrc, int(at) + 16, 0, 0) : 0u;
-        }
-        // The batch is consumed here, all at once: otherwise the compiler
-        // moves each load into the branch that writes its row, behind a
-        // wait for the loads before it.
-#pragma unroll
-        for (int i = 0; i < kStageBatch; ++i) {
-            asm volatile("" : "+v"(v[i]));
-            if (C == 4) asm volatile("" : "+v"(v4[i]));
-        }
-#pragma unroll
-        for (int i = 0; i < kStageBatch; ++i)
-            if (r + i * step < rows)
-                *reinterpret_cast<u32x4 *>(band + (r + i * step) * pitch + 4 * g) =
-                    unpack_4px<C>(v[i], v4[i], sh[i]);
+        RowBatch b;
+        issue_rows<C>(b, w, row_bytes, col_bytes, r, step, rows, last_row);
+        write_rows<C>(band, b, r, step, rows, g, pitch);
     }
 }
 
@@ -488,10 +505,67 @@ __device__ __forceinline__ void tile_pass(const PreArgs &a, const DevImage &d, c
     }
 }
 
+// Two distinct frames of a clip tile whose band fits the LDS (and is at
+// most one row of groups per thread pass): frame 1's first batch of band
+// loads goes out before frame 0 is resampled, so its latency is spent there.
+template <typename OutT, int C>
+__device__ __forceinline__ void clip_pair_pass(const PreArgs &a, const DevImage &d, const TileGeom &g,
+                                               const Band &b, int64_t off0, int64_t off1, OutT *out,
+                                               bool column, uint32_t *band) {
+    const int64_t row_bytes = int64_t(d.src_w) * C;
+    const uint64_t lead = uint64_t(int64_t(b.r_lo) * row_bytes + int64_t(b.c_lo) * C);
+    const uint64_t base = reinterpret_cast<uint64_t>(a.src);
+    const SourceWindow w0 = source_window(a, base + uint64_t(off0) + lead);
+    const SourceWindow w1 = source_window(a, base + uint64_t(off1) + lead);
+    const int last_row = d.src_h - 1 - b.r_lo;
+    const int step = blockDim.x / b.groups;
+    const int r0 = div_small(threadIdx.x, b.groups, 1.0f / float(b.groups));
+    const int gi = threadIdx.x - r0 * b.groups;
+    const bool active = r0 < step;
+    const int wave = threadIdx.x >> 6, waves = blockDim.x >> 6;
+    const BandPixels px{band, b.pitch, b.r_lo, b.c_lo};
+    RowBatch next;
+    if (active) {
+        stage_rows<C>(band, w0, row_bytes, r0, step, b.rows, last_row, gi, b.pitch);
+        issue_rows<C>(next, w1, row_bytes, w1.lead + uint32_t(gi * 4 * C), r0, step, b.rows, last_row);
+    }
+    __syncthreads();
+    if (b.c_end == d.src_w) {
+        replicate_right_edge(band, d, b);
+        __syncthreads();
+    }
+    for (int p = wave; p < g.count; p += waves) {
+        const int qr = g.first + p;
+        bilinear_patch<OutT, 0>(px, d, a, g.t, g.br, qr >> 2, (qr >> 1) & 1, qr & 1, out, column);
+    }
+    __syncthreads();  // the first frame's band is no longer read
+    if (active) {
+        write_rows<C>(band, next, r0, step, b.rows, gi, b.pitch);
+        const uint32_t col_bytes = w1.lead + uint32_t(gi * 4 * C);
+        for (int r = r0 + kStageBatch * step; r < b.rows; r += kStageBatch * step) {
+            RowBatch rb;
+            issue_rows<C>(rb, w1, row_bytes, col_bytes, r, step, b.rows, last_row);
+            write_rows<C>(band, rb, r, step, b.rows, gi, b.pitch);
+        }
+    }
+    __syncthreads();
+    if (b.c_end == d.src_w) {
+        replicate_right_edge(band, d, b);
+        __syncthreads();
+    }
+    for (int p = wave; p < g.count; p += waves) {
+        const int qr = g.first + p;
+        bilinear_patch<OutT, 1>(px, d, a, g.t, g.br, qr >> 2, (qr >> 1) & 1, qr & 1, out, column);
+    }
+}
+
 // kClips: the batch holds at least one clip (an item with two or more
 // frames); batches of still images compile without the temporal decode.
+// At least 6 waves per SIMD: the register budget of a clip tile's LDS
+// occupancy (its band holds a CU to 6 workgroups), which the clip pair path
+// would exceed; batches of stills stay within it anyway.
 template <typename OutT, bool kClips>
-__global__ __launch_bounds__(kThreads) void preprocess_kernel(PreArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) void preprocess_kernel(PreArgs a) {
     extern __shared__ uint32_t band[];
     int64_t tile = a.xcd_order ? xcd_contiguous_tile(blockIdx.x, gridDim.x) : int64_t(blockIdx.x);
     // Pass 0 writes merge-block order (if requested), pass 1 column order:
@@ -558,9 +632,20 @@ __global__ __launch_bounds__(kThreads) void preprocess_kernel(PreArgs a) {
     if (f0 == f1) {
         tile_pass<OutT, -1>(a, d, g, off0, out, column, band);
     } else {
+        const int64_t off1 = d.src_offset + int64_t(f1) * frame_bytes;
+        if (!(d.flags & kFlagIdentity)) {
+            const Band b = tile_band(a, d, g);
+            if (b.fits && b.groups <= int(blockDim.x)) {
+                if (d.channels == 3)
+                    clip_pair_pass<OutT, 3>(a, d, g, b, off0, off1, out, column, band);
+                else
+                    clip_pair_pass<OutT, 4>(a, d, g, b, off0, off1, out, column, band);
+                return;
+            }
+        }
         tile_pass<OutT, 0>(a, d, g, off0, out, column, band);
         __syncthreads();  // the first frame's band is no longer read
-        tile_pass<OutT, 1>(a, d, g, d.src_offset + int64_t(f1) * frame_bytes, out, column, band);
+        tile_pass<OutT, 1>(a, d, g, off1, out, column, band);
     }
 }
 
