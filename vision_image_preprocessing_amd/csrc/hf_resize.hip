@@ -37,7 +37,9 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <map>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "device_util.h"
@@ -469,6 +471,21 @@ int build_hf_tables(int32_t n, const mimo_image_desc *desc, const float *mean01,
             lut[c * 256 + v] = (x - mean01[c]) / std01[c];
         }
     int64_t tiles = 0, rows = 0;
+    // One tap table per (input length, output length) pair in the batch:
+    // items of the same size share it (built and uploaded once).
+    std::map<std::pair<int32_t, int32_t>, std::pair<int64_t, int32_t>> tables;
+    auto axis_table = [&](int32_t n_in, int32_t n_out, int64_t &tab, int32_t &k) {
+        const auto key = std::make_pair(n_in, n_out);
+        const auto it = tables.find(key);
+        if (it != tables.end()) {
+            tab = it->second.first;
+            k = it->second.second;
+            return;
+        }
+        tab = int64_t(out.taps.size());
+        k = append_axis_taps(n_in, n_out, out.taps);
+        tables.emplace(key, std::make_pair(tab, k));
+    };
     for (int32_t i = 0; i < n; ++i) {
         const mimo_image_desc &s = desc[i];
         HfItem d;
@@ -498,13 +515,9 @@ int build_hf_tables(int32_t n, const mimo_image_desc *desc, const float *mean01,
         d.blocks_h = s.dst_h / kUnitPx;
         d.blocks_w = s.dst_w / kUnitPx;
         d.group = kUnitPx;
-        if (s.dst_w != s.src_w) {
-            d.x_tab = int64_t(out.taps.size());
-            d.kx = append_axis_taps(s.src_w, s.dst_w, out.taps);
-        }
+        if (s.dst_w != s.src_w) axis_table(s.src_w, s.dst_w, d.x_tab, d.kx);
         if (s.dst_h != s.src_h) {
-            d.y_tab = int64_t(out.taps.size());
-            d.ky = append_axis_taps(s.src_h, s.dst_h, out.taps);
+            axis_table(s.src_h, s.dst_h, d.y_tab, d.ky);
             const int32_t *yfirst = out.taps.data() + d.y_tab;
             d.group = choose_group(yfirst, yfirst + s.dst_h, s.dst_h);
             if (d.group == 0)
