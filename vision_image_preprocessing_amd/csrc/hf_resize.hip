@@ -39,6 +39,7 @@
 #include <cstring>
 #include <map>
 #include <string>
+#include <thread>
 #include <utility>
 #include <vector>
 
@@ -62,6 +63,7 @@ constexpr int kWeightBits = 22;           // fractional bits of the resampler's 
 constexpr int kMidRows = 256;             // most LDS band rows (32 pixels each)
 constexpr int kStageDwords = 4096;        // most LDS source staging (one dword per pixel)
 constexpr int kTapBudget = 2048;          // most LDS weights per axis (else they are read from memory)
+constexpr int64_t kParallelTapWork = 1 << 18;  // weights (outputs x taps) worth several host threads
 constexpr int kFixedDwords = 3 * 256 + kUnitPx * kUnitPx + 2 * kUnitPx;  // lut, block, first x/y
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer resource word 3 (gfx9 family)
 
@@ -371,57 +373,81 @@ int axis_taps_per_output(int64_t n_in, int64_t n_out) {
     return int(std::ceil(support)) * 2 + 1;
 }
 
-// Appends first[n_out], count[n_out], weights[n_out][k] of one axis and
-// returns k.  Every output gets the same k taps, the most any output of the
-// axis has: its window [first, first + k) is moved left where it would run
-// past the last input (its own taps then sit further right in the row), and
-// the weights it does not use are zero.  The kernel then runs one tap count
-// for every output and never reads outside the image; the sums are those
-// of the outputs' own taps, since the extra terms are zero.
-int append_axis_taps(int64_t n_in, int64_t n_out, std::vector<int32_t> &tab) {
-    const double scale = double(n_in) / double(n_out);
-    const double widen = scale < 1.0 ? 1.0 : scale;
-    const double support = 2.0 * widen;
-    const int k_max = axis_taps_per_output(n_in, n_out);
-    std::vector<int32_t> lo_of(static_cast<size_t>(n_out)), cnt_of(static_cast<size_t>(n_out));
-    std::vector<int32_t> wts(size_t(n_out) * k_max, 0);
-    std::vector<double> w(size_t(k_max) + 1);
-    int k = 1;
-    for (int64_t i = 0; i < n_out; ++i) {
-        const double centre = (double(i) + 0.5) * scale;
-        int64_t lo = int64_t(centre - support + 0.5);
+// PIL's window of output i on an axis of n_in inputs: [lo, hi).
+struct AxisMap {
+    int64_t n_in, n_out;
+    double scale, widen, support;
+    AxisMap(int64_t in, int64_t out) : n_in(in), n_out(out) {
+        scale = double(n_in) / double(n_out);
+        widen = scale < 1.0 ? 1.0 : scale;
+        support = 2.0 * widen;
+    }
+    void window(int64_t i, int64_t &lo, int64_t &hi, double &centre) const {
+        centre = (double(i) + 0.5) * scale;
+        lo = int64_t(centre - support + 0.5);
         if (lo < 0) lo = 0;
-        int64_t hi = int64_t(centre + support + 0.5);
+        hi = int64_t(centre + support + 0.5);
         if (hi > n_in) hi = n_in;
+    }
+};
+
+// An axis table is first[n_out], count[n_out], weights[n_out][k].  Every
+// output gets the same k taps, the most any output of the axis has: its
+// window [first, first + k) is moved left where it would run past the last
+// input (its own taps then sit further right in the row), and the weights
+// it does not use are zero.  The kernel then runs one tap count for every
+// output and never reads outside the image; the sums are those of the
+// outputs' own taps, since the extra terms are zero.
+
+// k of an axis (at least 1, at most n_in).
+int axis_tap_count(int64_t n_in, int64_t n_out) {
+    const AxisMap m(n_in, n_out);
+    int64_t k = 1;
+    for (int64_t i = 0; i < n_out; ++i) {
+        int64_t lo, hi;
+        double centre;
+        m.window(i, lo, hi, centre);
+        k = std::max(k, hi - lo);
+    }
+    return int(k);
+}
+
+// first and count of an axis table at tab (the cheap part: what the host's
+// band and staging sizes need).
+void fill_axis_heads(int64_t n_in, int64_t n_out, int k, int32_t *tab) {
+    const AxisMap m(n_in, n_out);
+    for (int64_t i = 0; i < n_out; ++i) {
+        int64_t lo, hi;
+        double centre;
+        m.window(i, lo, hi, centre);
+        tab[i] = int32_t(std::min<int64_t>(lo, n_in - k));
+        tab[n_out + i] = k;
+    }
+}
+
+// The weights of an axis table at tab (zeroed by the caller), in float64
+// as PIL computes them, rounded half away from zero to kWeightBits.
+void fill_axis_weights(int64_t n_in, int64_t n_out, int k, int32_t *tab) {
+    const AxisMap m(n_in, n_out);
+    int32_t *weight = tab + 2 * n_out;
+    std::vector<double> w(size_t(k) + 1);
+    for (int64_t i = 0; i < n_out; ++i) {
+        int64_t lo, hi;
+        double centre;
+        m.window(i, lo, hi, centre);
         const int64_t cnt = hi - lo;
         double sum = 0.0;
         for (int64_t j = 0; j < cnt; ++j) {
-            w[j] = keys_bicubic((double(j + lo) - centre + 0.5) / widen);
+            w[j] = keys_bicubic((double(j + lo) - centre + 0.5) / m.widen);
             sum += w[j];
         }
+        const int64_t shift = lo - tab[i];
         for (int64_t j = 0; j < cnt; ++j) {
             const double v = sum != 0.0 ? w[j] / sum : w[j];
             const double fixed = v * double(1 << kWeightBits);
-            wts[size_t(i) * k_max + j] = int32_t(v < 0.0 ? fixed - 0.5 : fixed + 0.5);
+            weight[i * k + shift + j] = int32_t(v < 0.0 ? fixed - 0.5 : fixed + 0.5);
         }
-        lo_of[i] = int32_t(lo);
-        cnt_of[i] = int32_t(cnt);
-        k = std::max<int>(k, int(cnt));
     }
-    const size_t base = tab.size();
-    tab.resize(base + size_t(n_out) * (2 + k), 0);
-    int32_t *first = tab.data() + base;
-    int32_t *count = first + n_out;
-    int32_t *weight = count + n_out;
-    for (int64_t i = 0; i < n_out; ++i) {
-        // k <= n_in, since no output has more taps than there are inputs
-        const int32_t lo = std::min<int32_t>(lo_of[i], int32_t(n_in - k));
-        const int32_t shift = lo_of[i] - lo;
-        for (int32_t j = 0; j < cnt_of[i]; ++j) weight[i * k + shift + j] = wts[size_t(i) * k_max + j];
-        first[i] = lo;
-        count[i] = k;
-    }
-    return k;
 }
 
 struct HfTables {
@@ -472,7 +498,9 @@ int build_hf_tables(int32_t n, const mimo_image_desc *desc, const float *mean01,
         }
     int64_t tiles = 0, rows = 0;
     // One tap table per (input length, output length) pair in the batch:
-    // items of the same size share it (built and uploaded once).
+    // items of the same size share it (built and uploaded once).  Its first
+    // and count entries are filled here; the weights, the costly part, after
+    // the loop, several tables at a time.
     std::map<std::pair<int32_t, int32_t>, std::pair<int64_t, int32_t>> tables;
     auto axis_table = [&](int32_t n_in, int32_t n_out, int64_t &tab, int32_t &k) {
         const auto key = std::make_pair(n_in, n_out);
@@ -482,8 +510,10 @@ int build_hf_tables(int32_t n, const mimo_image_desc *desc, const float *mean01,
             k = it->second.second;
             return;
         }
+        k = axis_tap_count(n_in, n_out);
         tab = int64_t(out.taps.size());
-        k = append_axis_taps(n_in, n_out, out.taps);
+        out.taps.resize(out.taps.size() + size_t(n_out) * (2 + k), 0);
+        fill_axis_heads(n_in, n_out, k, out.taps.data() + tab);
         tables.emplace(key, std::make_pair(tab, k));
     };
     for (int32_t i = 0; i < n; ++i) {
@@ -559,6 +589,32 @@ int build_hf_tables(int32_t n, const mimo_image_desc *desc, const float *mean01,
     out.rows = rows;
     if (out.taps.size() > size_t(0x7FFFFFFF))
         return set_error(MIMO_E_TOO_LARGE, "preprocess_hf: tap tables above 2^31 entries");
+    // the weights: tables are independent, so large batches of them are
+    // shared out over up to 16 host threads
+    struct Job {
+        int32_t n_in, n_out, k;
+        int64_t tab;
+    };
+    std::vector<Job> jobs;
+    int64_t work = 0;
+    for (const auto &t : tables) {
+        jobs.push_back({t.first.first, t.first.second, t.second.second, t.second.first});
+        work += int64_t(t.first.second) * t.second.second;
+    }
+    auto run = [&](size_t from, size_t step) {
+        for (size_t j = from; j < jobs.size(); j += step)
+            fill_axis_weights(jobs[j].n_in, jobs[j].n_out, jobs[j].k, out.taps.data() + jobs[j].tab);
+    };
+    const size_t threads =
+        std::min<size_t>({size_t(16), jobs.size(), size_t(std::max(1u, std::thread::hardware_concurrency()))});
+    if (threads < 2 || work < kParallelTapWork) {
+        run(0, 1);
+    } else {
+        std::vector<std::thread> pool;
+        for (size_t t = 1; t < threads; ++t) pool.emplace_back(run, t, threads);
+        run(0, threads);
+        for (auto &th : pool) th.join();
+    }
     return MIMO_OK;
 }
 
