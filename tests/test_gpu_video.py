@@ -145,6 +145,17 @@ def test_mixed_clips_and_stills_full(V, out_dtype):
     assert torch.equal(gathered, out["pixel_values_col"])
 
 
+def test_clip_strong_downscale_reads_taps_directly(V):
+    """Distinct frames whose band exceeds the LDS budget (a 7-10x downscale
+    under a small per-frame ceiling) take the direct-read route, frame
+    after frame; same bar."""
+    _say("clip strong downscale")
+    b = W.media_batch([(2, 3000, 2600, 3), (3, 2048, 4000, 4)], seed=68, video_budget=[1 << 17, 1 << 17])
+    plan, out = _run(V, b, "f32", merge=True, column=True)
+    assert plan.desc["dst_h"][0] * 7 <= 3000  # band far beyond the LDS budget
+    _check(V, b, plan, out, "f32", column=True)
+
+
 def test_column_order_only(V):
     _say("column order only")
     b = W.media_batch(MIXED[:7], seed=62)
