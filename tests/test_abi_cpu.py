@@ -110,6 +110,28 @@ def test_smart_resize_per_call_bounds_match_oracle():
             assert e.value.code == st
 
 
+def test_get_number_of_image_patches_matches_oracle():
+    """The processor's get_number_of_image_patches through the planner: the
+    oracle's row count on random sizes and the pages' sub-factor cases, the
+    per-call bounds honoured, and a rejected size raising."""
+    import oracle
+    import vision_image_preprocessing_amd as V
+
+    assert V.get_number_of_image_patches(16, 192) == 48     # 32x384 -> 2 x 24 patches
+    assert V.get_number_of_image_patches(8, 500) == 248     # 32x1984 -> 2 x 124 (a tie, to even)
+    rng = np.random.default_rng(12)
+    for _ in range(300):
+        h, w = (int(np.exp(rng.uniform(0.0, np.log(5000.0)))) for _ in range(2))
+        st, _, _ = oracle.smart_resize_status(h, w)
+        if st != 0:
+            continue
+        assert V.get_number_of_image_patches(h, w) == oracle.image_grid(h, w)[1], (h, w)
+    assert V.get_number_of_image_patches(1000, 1000, max_pixels=65536) == \
+        oracle.image_grid(1000, 1000, max_pixels=65536)[1]
+    with pytest.raises(V.MimoError):
+        V.get_number_of_image_patches(32, 6401)               # beyond the 200:1 aspect guard
+
+
 def test_plan_reports_per_image_status():
     shapes = [(64, 64, 3), (32, 6401, 3), (0, 5, 3), (40, 40, 5), (1, 8193, 4), (50, 60, 4)]
     desc, total_rows, total_src, code = V.plan_geometry(shapes, check=False)

@@ -16,7 +16,8 @@ from ._abi import (  # noqa: F401
     IMAGE_DESC_DTYPE, MIMO_BF16, MIMO_E_ASPECT, MIMO_E_CAPACITY, MIMO_E_DEGENERATE,
     MIMO_E_HIP, MIMO_E_INVALID, MIMO_E_TOO_LARGE, MIMO_E_UNSUPPORTED, MIMO_F32, MIMO_OK,
     ROW_LEN, LibraryNotBuilt, MimoError, MimoParams, column_permutation, column_permute,
-    chunk_seqlens, default_params, dispatch_count, fold_patch_weights, hf_smart_resize,
+    chunk_seqlens, default_params, dispatch_count, fold_patch_weights, get_number_of_image_patches,
+    hf_smart_resize,
     hf_workspace_bytes, last_error, load, make_params, patch_embed, plan_frames, plan_geometry,
     plan_hf,
     preprocess_hf_batch, preprocess_batch, rope_inv_freq, rotary_tables, sample_frames,

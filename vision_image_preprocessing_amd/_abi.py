@@ -210,6 +210,15 @@ def plan_geometry(hwc, params: MimoParams | None = None, check: bool = True):
     return desc, total_rows.value, total_src.value, code
 
 
+def get_number_of_image_patches(height: int, width: int, min_pixels=None, max_pixels=None) -> int:
+    """The processor's get_number_of_image_patches (NeMo Automodel
+    "mimo_v2_flash.processing"): patches (= rows, grid_h * grid_w) of one
+    image of that size, from mimo_plan_geometry; raises MimoError for a size
+    the geometry rejects."""
+    desc, _, _, _ = plan_geometry([(int(height), int(width), 3)], make_params(min_pixels, max_pixels))
+    return int(desc["rows"][0])
+
+
 def plan_frames(fhwc, max_pixels=None, params: MimoParams | None = None, check: bool = True):
     """mimo_plan_frames over an [n, 4] (frames, height, width, channels)
     table; max_pixels: optional per-item resized-area ceilings ([n] int64,
