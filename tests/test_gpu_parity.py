@@ -201,8 +201,24 @@ def test_empty_batch(V):
     assert plan.total_rows == 0 and len(plan) == 0
     src = torch.zeros(16, dtype=torch.uint8, device="cuda")
     out = V.preprocess(src, plan)
-    assert out["pixel_values"].shape == (1, 1536)
+    assert out["pixel_values"].shape == (0, 1536)  # [sum of rows, 1536]
+    out = V.ImageProcessor()([])
+    assert out["pixel_values"].shape == (0, 1536) and out["image_grid_thw"].shape == (0, 3)
     del b
+
+
+def test_image_processor_call(V):
+    """The processor's call shape: decoded images in, rows and grids out,
+    equal to the planned path's rows (and so to the oracle's)."""
+    _say("ImageProcessor")
+    b = W.uniform_images([(200, 300, 3), (45, 77, 4), (96, 128, 3)], seed=9)
+    images = [b.image(i) for i in range(len(b))]
+    out = V.ImageProcessor(image_mean=b.mean, image_std=b.std)(images, column_order=True)
+    plan, ref = _run(V, b, "f32", merge=True, column=True)
+    assert torch.equal(out["pixel_values"], ref["pixel_values"][:plan.total_rows])
+    assert torch.equal(out["pixel_values_col"], ref["pixel_values_col"][:plan.total_rows])
+    assert np.array_equal(out["image_grid_thw"].numpy(), plan.image_grid_thw)
+    _check_full(V, b, plan, out, "f32", column=True)
 
 
 def test_argument_errors(V):

@@ -110,9 +110,10 @@ def preprocess(src_dev, plan: BatchPlan, mean=IMAGENET_MEAN, std=IMAGENET_STD,
     dev = src_dev.device
     tdtype = {"f32": torch.float32, "bf16": torch.bfloat16}[out_dtype]
     n_rows = max(plan.total_rows, 1)
-    if merge_order and rows is None:
+    own_rows, own_col = merge_order and rows is None, column_order and rows_col is None
+    if own_rows:
         rows = torch.empty((n_rows, _abi.ROW_LEN), dtype=tdtype, device=dev)
-    if column_order and rows_col is None:
+    if own_col:
         rows_col = torch.empty((n_rows, _abi.ROW_LEN), dtype=tdtype, device=dev)
     if workspace is None:
         workspace = torch.empty(max(_abi.workspace_bytes(len(plan)), 16), dtype=torch.uint8,
@@ -122,11 +123,50 @@ def preprocess(src_dev, plan: BatchPlan, mean=IMAGENET_MEAN, std=IMAGENET_STD,
                           rows=rows if merge_order else None,
                           rows_col=rows_col if column_order else None,
                           workspace=workspace, stream=stream)
+    # outputs allocated here hold at least one row (the library takes no null
+    # output); hand back exactly the plan's rows
+    if own_rows:
+        rows = rows[:plan.total_rows]
+    if own_col:
+        rows_col = rows_col[:plan.total_rows]
     return {
         "pixel_values": rows if merge_order else None,
         "pixel_values_col": rows_col if column_order else None,
         "image_grid_thw": torch.from_numpy(plan.image_grid_thw),
     }
+
+
+class ImageProcessor:
+    """MimoV2ImageProcessor's call shape (NeMo Automodel
+    "mimo_v2_flash.processing"): decoded images in, ``pixel_values`` and
+    ``image_grid_thw`` out, in one kernel launch.
+
+    Images are uint8 arrays [height, width, 3 or 4] (RGB, or RGBA flattened
+    onto white); decoding them is the caller's.  Defaults are the
+    processor's: patch 16, temporal 2, merge 2, 8192..8388608 pixels,
+    ImageNet statistics.  A size the geometry rejects raises MimoError.
+    """
+
+    def __init__(self, image_mean=IMAGENET_MEAN, image_std=IMAGENET_STD, min_pixels=None,
+                 max_pixels=None, out_dtype: str = "f32", device="cuda"):
+        self.image_mean, self.image_std = tuple(image_mean), tuple(image_std)
+        self.min_pixels, self.max_pixels = min_pixels, max_pixels
+        self.out_dtype, self.device = out_dtype, device
+
+    def __call__(self, images, min_pixels=None, max_pixels=None, column_order: bool = False):
+        images = [np.asarray(im) for im in images]
+        for im in images:
+            if im.dtype != np.uint8 or im.ndim != 3 or im.shape[2] not in (3, 4):
+                raise _abi.MimoError(_abi.MIMO_E_INVALID,
+                                     "ImageProcessor: images must be uint8 [height, width, 3 or 4]")
+        plan = plan_batch([im.shape for im in images],
+                          self.min_pixels if min_pixels is None else min_pixels,
+                          self.max_pixels if max_pixels is None else max_pixels)
+        packed = (np.concatenate([np.ascontiguousarray(im).reshape(-1) for im in images])
+                  if images else np.zeros(0, dtype=np.uint8))
+        src = upload_sources(packed, plan, self.device)
+        return preprocess(src, plan, mean=self.image_mean, std=self.image_std, out_dtype=self.out_dtype,
+                          column_order=column_order)
 
 
 def vit_tables(plan: BatchPlan, device="cuda", column: bool = False, rope_dim: int = 32,
@@ -182,9 +222,10 @@ def preprocess_hf(src_dev, plan: BatchPlan, mean=IMAGENET_MEAN, std=IMAGENET_STD
     dev = src_dev.device
     tdtype = {"f32": torch.float32, "bf16": torch.bfloat16}[out_dtype]
     n_rows = max(plan.total_rows, 1)
-    if merge_order and rows is None:
+    own_rows, own_col = merge_order and rows is None, column_order and rows_col is None
+    if own_rows:
         rows = torch.empty((n_rows, _abi.ROW_LEN), dtype=tdtype, device=dev)
-    if column_order and rows_col is None:
+    if own_col:
         rows_col = torch.empty((n_rows, _abi.ROW_LEN), dtype=tdtype, device=dev)
     if workspace is None:
         workspace = torch.empty(max(_abi.hf_workspace_bytes(plan.desc), 16), dtype=torch.uint8,
@@ -192,6 +233,12 @@ def preprocess_hf(src_dev, plan: BatchPlan, mean=IMAGENET_MEAN, std=IMAGENET_STD
     _abi.preprocess_hf_batch(plan.desc, src_dev, mean, std, rows=rows if merge_order else None,
                              rows_col=rows_col if column_order else None, workspace=workspace,
                              stream=stream)
+    # outputs allocated here hold at least one row (the library takes no null
+    # output); hand back exactly the plan's rows
+    if own_rows:
+        rows = rows[:plan.total_rows]
+    if own_col:
+        rows_col = rows_col[:plan.total_rows]
     return {
         "pixel_values": rows if merge_order else None,
         "pixel_values_col": rows_col if column_order else None,
