@@ -132,6 +132,21 @@ def test_get_number_of_image_patches_matches_oracle():
         V.get_number_of_image_patches(32, 6401)               # beyond the 200:1 aspect guard
 
 
+def test_image_processor_arguments_without_gpu():
+    """The processor's constructor arguments; patch sizes other than the
+    kernels' and non-image inputs are refused before any GPU work."""
+    import vision_image_preprocessing_amd as V
+
+    p = V.ImageProcessor(16, 2, 2, 8192, 8388608, (0.5, 0.5, 0.5), (0.5, 0.5, 0.5))
+    assert p.image_mean == (0.5, 0.5, 0.5) and p.min_pixels == 8192
+    with pytest.raises(V.MimoError):
+        V.ImageProcessor(patch_size=14)
+    with pytest.raises(V.MimoError):
+        p([np.zeros((10, 10), np.uint8)])
+    with pytest.raises(V.MimoError):
+        p([np.zeros((10, 10, 3), np.float32)])
+
+
 def test_plan_reports_per_image_status():
     shapes = [(64, 64, 3), (32, 6401, 3), (0, 5, 3), (40, 40, 5), (1, 8193, 4), (50, 60, 4)]
     desc, total_rows, total_src, code = V.plan_geometry(shapes, check=False)

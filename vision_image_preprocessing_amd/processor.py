@@ -141,14 +141,20 @@ class ImageProcessor:
     "mimo_v2_flash.processing"): decoded images in, ``pixel_values`` and
     ``image_grid_thw`` out, in one kernel launch.
 
-    Images are uint8 arrays [height, width, 3 or 4] (RGB, or RGBA flattened
-    onto white); decoding them is the caller's.  Defaults are the
-    processor's: patch 16, temporal 2, merge 2, 8192..8388608 pixels,
-    ImageNet statistics.  A size the geometry rejects raises MimoError.
+    The constructor takes the processor's arguments, in its order.  Images
+    are uint8 arrays [height, width, 3 or 4] (RGB, or RGBA flattened onto
+    white); decoding them is the caller's.  Defaults are the processor's:
+    patch 16, temporal 2, merge 2, 8192..8388608 pixels, ImageNet
+    statistics; other patch sizes raise MimoError (MIMO_E_UNSUPPORTED), as
+    does a size the geometry rejects (its own code).
     """
 
-    def __init__(self, image_mean=IMAGENET_MEAN, image_std=IMAGENET_STD, min_pixels=None,
-                 max_pixels=None, out_dtype: str = "f32", device="cuda"):
+    def __init__(self, patch_size: int = 16, temporal_patch_size: int = 2, merge_size: int = 2,
+                 min_pixels=None, max_pixels=None, image_mean=IMAGENET_MEAN, image_std=IMAGENET_STD,
+                 out_dtype: str = "f32", device="cuda"):
+        if (patch_size, temporal_patch_size, merge_size) != (16, 2, 2):
+            raise _abi.MimoError(_abi.MIMO_E_UNSUPPORTED,
+                                 "ImageProcessor: the kernels are built for patch 16, temporal 2, merge 2")
         self.image_mean, self.image_std = tuple(image_mean), tuple(image_std)
         self.min_pixels, self.max_pixels = min_pixels, max_pixels
         self.out_dtype, self.device = out_dtype, device
