@@ -145,6 +145,28 @@ def test_mixed_clips_and_stills_full(V, out_dtype):
     assert torch.equal(gathered, out["pixel_values_col"])
 
 
+@pytest.mark.parametrize("seed", [71, 72])
+def test_random_clips_full(V, seed):
+    """40 random items: 1 to 7 frames (odd counts repeat their last frame),
+    sides log-uniform in [1, 400], RGB and RGBA, a quarter of them under a
+    clip pixel budget; both orders, every row against the oracle."""
+    rng = np.random.default_rng(seed)
+    items, budget = [], []
+    for _ in range(40):
+        h, w = (int(np.exp(rng.uniform(0.0, np.log(400.0)))) for _ in range(2))
+        items.append((int(rng.integers(1, 8)), max(h, 1), max(w, 1), int(rng.choice([3, 4]))))
+        budget.append(int(1 << 16) if rng.random() < 0.25 else 0)
+    # keep the items the geometry accepts (sub-factor shapes whose upscale
+    # exceeds the pixel ceiling are refused)
+    pre = V.plan_media(items, video_budget=budget, check=False)
+    keep = [i for i in range(len(items)) if pre.desc["status"][i] == 0]
+    items, budget = [items[i] for i in keep], [budget[i] for i in keep]
+    _say("random clips", seed, len(items))
+    b = W.media_batch(items, seed=seed, video_budget=budget)
+    plan, out = _run(V, b, "f32", merge=True, column=True)
+    _check(V, b, plan, out, "f32", column=True)
+
+
 def test_clip_strong_downscale_reads_taps_directly(V):
     """Distinct frames whose band exceeds the LDS budget (a 7-10x downscale
     under a small per-frame ceiling) take the direct-read route, frame
