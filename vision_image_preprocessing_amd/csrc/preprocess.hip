@@ -505,9 +505,10 @@ __device__ __forceinline__ void tile_pass(const PreArgs &a, const DevImage &d, c
     }
 }
 
-// Two distinct frames of a clip tile whose band fits the LDS (and is at
-// most one row of groups per thread pass): frame 1's first batch of band
-// loads goes out before frame 0 is resampled, so its latency is spent there.
+// Two distinct frames of a clip tile whose band fits the LDS and whose band
+// row has no more 4-pixel groups than the workgroup has threads: frame 1's
+// first batch of band loads goes out before frame 0 is resampled, so that
+// its latency is spent there.
 template <typename OutT, int C>
 __device__ __forceinline__ void clip_pair_pass(const PreArgs &a, const DevImage &d, const TileGeom &g,
                                                const Band &b, int64_t off0, int64_t off1, OutT *out,
@@ -561,9 +562,10 @@ __device__ __forceinline__ void clip_pair_pass(const PreArgs &a, const DevImage 
 
 // kClips: the batch holds at least one clip (an item with two or more
 // frames); batches of still images compile without the temporal decode.
-// At least 6 waves per SIMD: the register budget of a clip tile's LDS
-// occupancy (its band holds a CU to 6 workgroups), which the clip pair path
-// would exceed; batches of stills stay within it anyway.
+// Built for at least 6 waves per SIMD: a clip tile's band typically holds a
+// CU to 6 workgroups (25 KB for 1280x720 frames at 960x512), and the clip
+// pair path would otherwise take more registers than that occupancy leaves;
+// batches of stills stay within the budget anyway.
 template <typename OutT, bool kClips>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) void preprocess_kernel(PreArgs a) {
     extern __shared__ uint32_t band[];
