@@ -96,8 +96,8 @@ def test_ragged_batch_bitwise(V, out_dtype):
     _check(V, b, plan, out, out_dtype)
 
 
-@pytest.mark.parametrize("seed", [93, 94])
-def test_random_shapes_bitwise(V, seed):
+@pytest.mark.parametrize("seed,out_dtype", [(93, "f32"), (94, "f32"), (95, "bf16")])
+def test_random_shapes_bitwise(V, seed, out_dtype):
     """60 random images: sides log-uniform in [1, 700] on each axis, so
     upscales of sides shorter than the tap count, mild and strong
     downscales and sizes the stock geometry leaves alone all occur; RGB and
@@ -107,10 +107,10 @@ def test_random_shapes_bitwise(V, seed):
     for _ in range(60):
         h, w = (int(np.exp(rng.uniform(0.0, np.log(700.0)))) for _ in range(2))
         shapes.append((max(h, 1), max(w, 1), int(rng.choice([3, 4]))))
-    _say("random shapes", seed)
+    _say("random shapes", seed, out_dtype)
     b = W.uniform_images(shapes, seed=seed)
-    plan, out = _run(V, b, "f32", merge=True, column=True)
-    _check(V, b, plan, out, "f32")
+    plan, out = _run(V, b, out_dtype, merge=True, column=True)
+    _check(V, b, plan, out, out_dtype)
 
 
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])

@@ -145,8 +145,8 @@ def test_mixed_clips_and_stills_full(V, out_dtype):
     assert torch.equal(gathered, out["pixel_values_col"])
 
 
-@pytest.mark.parametrize("seed", [71, 72])
-def test_random_clips_full(V, seed):
+@pytest.mark.parametrize("seed,out_dtype", [(71, "f32"), (72, "f32"), (73, "bf16")])
+def test_random_clips_full(V, seed, out_dtype):
     """40 random items: 1 to 7 frames (odd counts repeat their last frame),
     sides log-uniform in [1, 400], RGB and RGBA, a quarter of them under a
     clip pixel budget; both orders, every row against the oracle."""
@@ -161,10 +161,10 @@ def test_random_clips_full(V, seed):
     pre = V.plan_media(items, video_budget=budget, check=False)
     keep = [i for i in range(len(items)) if pre.desc["status"][i] == 0]
     items, budget = [items[i] for i in keep], [budget[i] for i in keep]
-    _say("random clips", seed, len(items))
+    _say("random clips", seed, out_dtype, len(items))
     b = W.media_batch(items, seed=seed, video_budget=budget)
-    plan, out = _run(V, b, "f32", merge=True, column=True)
-    _check(V, b, plan, out, "f32", column=True)
+    plan, out = _run(V, b, out_dtype, merge=True, column=True)
+    _check(V, b, plan, out, out_dtype, column=True)
 
 
 def test_clip_strong_downscale_reads_taps_directly(V):
