@@ -8,6 +8,8 @@ uint8 HWC arrays (RGB or RGBA).
 """
 from __future__ import annotations
 
+import threading
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 
 import numpy as np
@@ -86,13 +88,62 @@ def plan_media(items, max_pixels=None, min_pixels=None, video_budget=None,
     return BatchPlan(desc=desc, total_rows=rows, total_src_bytes=src)
 
 
+_STAGE_BYTES = 64 << 20          # one pinned staging chunk
+_DIRECT_BYTES = 8 << 20          # smaller uploads copy straight from pageable memory
+_stage_lock = threading.Lock()
+_stages = {}                     # device index -> two pinned uint8 tensors of _STAGE_BYTES
+
+
+def _pinned_stages(torch, index):
+    """The device's two staging chunks (callers hold _stage_lock)."""
+    if index not in _stages:
+        _stages[index] = [torch.empty(_STAGE_BYTES, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
+    return _stages[index]
+
+
 def upload_sources(packed: np.ndarray, plan: BatchPlan, device="cuda"):
     """Copies packed uint8 images (back to back, batch order) into a padded
-    device buffer."""
+    device buffer; returns when the copy is done.
+
+    Large batches go through two reusable pinned chunks: host threads fill
+    one while the other's DMA copy runs, instead of one copy from pageable
+    memory (which the runtime stages through a small buffer of its own).
+    """
     import torch
-    buf = torch.zeros(plan.src_capacity, dtype=torch.uint8, device=device)
-    flat = torch.from_numpy(np.ascontiguousarray(packed).reshape(-1))
-    buf[:flat.numel()].copy_(flat)
+    dev = torch.device(device)
+    if dev.type == "cuda" and dev.index is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
+    flat = np.ascontiguousarray(packed).reshape(-1)
+    n = int(flat.size)
+    buf = torch.empty(plan.src_capacity, dtype=torch.uint8, device=dev)
+    if plan.src_capacity > n:
+        buf[n:].zero_()
+    if n == 0:
+        return buf
+    if n <= _DIRECT_BYTES:
+        buf[:n].copy_(torch.from_numpy(flat))
+        return buf
+    stream = torch.cuda.current_stream(dev)
+    done = [None, None]
+    parts = 8
+    # one chunked upload at a time: concurrent callers would share the chunks
+    with _stage_lock, ThreadPoolExecutor(max_workers=parts) as pool:
+        stages = _pinned_stages(torch, dev.index)
+        for i, off in enumerate(range(0, n, _STAGE_BYTES)):
+            k = i & 1
+            if done[k] is not None:
+                done[k].synchronize()      # this chunk's previous copy has run
+            m = min(_STAGE_BYTES, n - off)
+            host = stages[k].numpy()
+            step = (m + parts - 1) // parts
+            list(pool.map(lambda j: np.copyto(host[j:min(j + step, m)], flat[off + j:off + min(j + step, m)]),
+                          range(0, m, step)))
+            buf[off:off + m].copy_(stages[k][:m], non_blocking=True)
+            done[k] = torch.cuda.Event()
+            done[k].record(stream)
+        for ev in done:
+            if ev is not None:
+                ev.synchronize()
     return buf
 
 
