@@ -167,6 +167,22 @@ def test_random_clips_full(V, seed, out_dtype):
     _check(V, b, plan, out, out_dtype, column=True)
 
 
+def test_video_processor_call(V):
+    """Clips and a still through VideoProcessor equal the planned path's
+    rows (and so the oracle's)."""
+    _say("VideoProcessor")
+    items = [(4, 64, 96, 3), (3, 45, 77, 4), (1, 200, 300, 3)]
+    b = W.media_batch(items, seed=69, video_budget=[1 << 16, 0, 0])
+    arrays = [b.clip(i) for i in range(len(b))]
+    out = V.VideoProcessor(image_mean=b.mean, image_std=b.std)(arrays, video_budget=[1 << 16, 0, 0],
+                                                              column_order=True)
+    plan, ref = _run(V, b, "f32", merge=True, column=True)
+    assert torch.equal(out["pixel_values"], ref["pixel_values"][:plan.total_rows])
+    assert torch.equal(out["pixel_values_col"], ref["pixel_values_col"][:plan.total_rows])
+    assert np.array_equal(out["video_grid_thw"].numpy(), plan.grid_thw)
+    _check(V, b, plan, out, "f32", column=True)
+
+
 def test_clip_strong_downscale_reads_taps_directly(V):
     """Distinct frames whose band exceeds the LDS budget (a 7-10x downscale
     under a small per-frame ceiling) take the direct-read route, frame

@@ -25,6 +25,6 @@ from ._abi import (  # noqa: F401
     window_index, workspace_bytes,
 )
 from .processor import (  # noqa: F401
-    BatchPlan, ImageProcessor, plan_batch, plan_batch_hf, plan_media, preprocess, preprocess_hf, stats255,
-    vit_tables,
+    BatchPlan, ImageProcessor, VideoProcessor, plan_batch, plan_batch_hf, plan_media, preprocess, preprocess_hf,
+    stats255, vit_tables,
 )

@@ -226,6 +226,47 @@ class ImageProcessor:
                           column_order=column_order)
 
 
+class VideoProcessor:
+    """The frames path of docs.rs "cortiq_engine::mimo_vision"
+    (prepare_video_frames) on the GPU: already-sampled clips, and still
+    images among them, in; ``pixel_values`` and ``video_grid_thw`` out, in
+    one kernel launch.
+
+    Each item is a uint8 array [frames, height, width, 3 or 4], or an image
+    [height, width, 3 or 4] (one frame).  Frames 2t and 2t + 1 form
+    temporal patch t; an odd count repeats its last frame.  ``video_budget``
+    (a clip's total pixels, per call or per item; 0 for none) sets each
+    clip's per-frame ceiling as mimo_video_max_pixels does.  Sampling frames
+    out of a longer video is the caller's (smart_nframes, sample_frames).
+    """
+
+    def __init__(self, min_pixels=None, max_pixels=None, image_mean=IMAGENET_MEAN, image_std=IMAGENET_STD,
+                 out_dtype: str = "f32", device="cuda"):
+        self.image_mean, self.image_std = tuple(image_mean), tuple(image_std)
+        self.min_pixels, self.max_pixels = min_pixels, max_pixels
+        self.out_dtype, self.device = out_dtype, device
+
+    def __call__(self, items, video_budget=None, column_order: bool = False):
+        arrays = []
+        for it in items:
+            a = np.asarray(it)
+            if a.ndim == 3:
+                a = a[None]
+            if a.dtype != np.uint8 or a.ndim != 4 or a.shape[0] < 1 or a.shape[3] not in (3, 4):
+                raise _abi.MimoError(_abi.MIMO_E_INVALID, "VideoProcessor: items must be uint8 "
+                                                          "[frames, height, width, 3 or 4] or [height, width, 3 or 4]")
+            arrays.append(a)
+        plan = plan_media([a.shape for a in arrays], max_pixels=self.max_pixels, min_pixels=self.min_pixels,
+                          video_budget=video_budget)
+        packed = (np.concatenate([np.ascontiguousarray(a).reshape(-1) for a in arrays])
+                  if arrays else np.zeros(0, dtype=np.uint8))
+        src = upload_sources(packed, plan, self.device)
+        out = preprocess(src, plan, mean=self.image_mean, std=self.image_std, out_dtype=self.out_dtype,
+                         column_order=column_order)
+        out["video_grid_thw"] = out.pop("image_grid_thw")
+        return out
+
+
 def vit_tables(plan: BatchPlan, device="cuda", column: bool = False, rope_dim: int = 32,
                theta: float = _abi.ROPE_THETA, stream=None, workspace=None):
     """The ViT index tables of a planned batch (vision page,
