@@ -147,6 +147,22 @@ def test_image_processor_arguments_without_gpu():
         p([np.zeros((10, 10, 3), np.float32)])
 
 
+def test_video_processor_arguments_without_gpu():
+    """Items that are not uint8 clips or images are refused before any GPU
+    work; a clip beyond the geometry raises the planner's error."""
+    import vision_image_preprocessing_amd as V
+
+    p = V.VideoProcessor()
+    with pytest.raises(V.MimoError):
+        p([np.zeros((2, 10, 10), np.uint8)])           # no channel axis
+    with pytest.raises(V.MimoError):
+        p([np.zeros((2, 10, 10, 3), np.float32)])      # not uint8
+    with pytest.raises(V.MimoError):
+        p([np.zeros((0, 10, 10, 3), np.uint8)])        # no frames
+    with pytest.raises(V.MimoError):
+        p([np.zeros((2, 32, 6401, 3), np.uint8)])      # beyond the 200:1 aspect guard
+
+
 def test_plan_reports_per_image_status():
     shapes = [(64, 64, 3), (32, 6401, 3), (0, 5, 3), (40, 40, 5), (1, 8193, 4), (50, 60, 4)]
     desc, total_rows, total_src, code = V.plan_geometry(shapes, check=False)
