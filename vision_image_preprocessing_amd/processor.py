@@ -108,6 +108,9 @@ def upload_sources(packed: np.ndarray, plan: BatchPlan, device="cuda"):
     Large batches go through two reusable pinned chunks: host threads fill
     one while the other's DMA copy runs, instead of one copy from pageable
     memory (which the runtime stages through a small buffer of its own).
+    The chunks (128 MB of pinned host memory per device) are allocated on
+    the first large upload and kept for the life of the process; large
+    uploads from several threads take turns.
     """
     import torch
     dev = torch.device(device)
