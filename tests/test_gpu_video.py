@@ -76,6 +76,11 @@ def _assert_close(got, ref, out_dtype, what=""):
     if out_dtype == "f32":
         err = np.abs(got.astype(np.float64) - ref.astype(np.float64))
         assert err.max() <= F32_TOL, (what, float(err.max()), np.unravel_index(err.argmax(), err.shape))
+        # tighter: the resize is the oracle's float32 arithmetic in the same
+        # order; only the standardisation differs (a product with the rounded
+        # 1/S against a quotient by S), by at most 3 float32 ulps of the value
+        bound = 4.0 * 2.0 ** -24 * np.maximum(np.abs(ref.astype(np.float64)), 1.0)
+        assert (err <= bound).all(), (what, "beyond 4 ulps", float((err / bound).max()))
     else:
         want = oracle.to_bf16_bits(ref).astype(np.int64)
         have = (got.astype(np.float32).view(np.uint32) >> 16).astype(np.int64)
