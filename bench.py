@@ -63,6 +63,28 @@ def measured_traffic(workload: str):
     return rec.get("traffic_bytes_per_launch")
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (as lscpu reports it)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def host_threads() -> int:
+    """Threads for the CPU baseline: the CPUs this process may run on, at
+    most 16 -- one GPU's share of the host on the GPU machines, whatever larger
+    count os.cpu_count() shows there."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    return max(1, min(16, avail))
+
+
 def cpu_baseline(batch, plan, sample: int, threads: int, out_bytes_per_value: int = 4) -> dict:
     """The oracle, as it is, on the first `sample` items (images, or clips
     for a video batch), one item per thread at a time.  "GB/s" counts the
@@ -97,8 +119,8 @@ def cpu_baseline(batch, plan, sample: int, threads: int, out_bytes_per_value: in
             "sample": f"first {len(idx)} of {len(batch)} {what} of the same batch"
                       + (f" ({units} frames)" if batch.is_media else "")
                       + f", one item per thread, {threads} threads, {dt:.2f} s wall",
-            "seconds": dt, "GB/s": nbytes / dt / 1e9,
-            "cpu_model": platform.processor() or platform.machine()}
+            "seconds": dt, "GB/s": nbytes / dt / 1e9, "cpu_model": cpu_model(),
+            "host_cpus_visible": os.cpu_count()}
 
 
 def time_launches(V, fn, reps: int, stream):
@@ -208,8 +230,7 @@ def patch_embed_rates(V, batch, plan, src, ws, reps: int, embed_dim: int = 1280)
     for name, wt, k in forms:
         ms = time_launches(V, lambda: V.patch_embed(rows, wt, bias, out=out), reps, stream)
         tflops = 2.0 * plan.total_rows * embed_dim * k / (ms * 1e-3) / 1e12
-        res[name] = {"k": k, "ms": ms, "TFLOP/s": tflops, "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
-                     "conv_equivalent_TFLOP/s": 2.0 * plan.total_rows * embed_dim * 1536 / (ms * 1e-3) / 1e12}
+        res[name] = {"k": k, "ms": ms, "TFLOP/s": tflops, "frac": tflops / MFMA_BF16_PEAK_TFLOPS}
     # the same product through torch's bf16 matmul (vendor GEMM), for context
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.matmul(rows, w.t(), out=out)
@@ -222,6 +243,100 @@ def patch_embed_rates(V, batch, plan, src, ws, reps: int, embed_dim: int = 1280)
     res["torch_matmul_full"] = {"ms": ms, "TFLOP/s": 2.0 * plan.total_rows * embed_dim * 1536 / (ms * 1e-3) / 1e12}
     del rows, out
     torch.cuda.empty_cache()
+    return res
+
+
+def pixel_rates(V, batch, plan, src, out_dtype: str, merge: bool, column: bool, reps: int,
+                rows=None, ws=None) -> dict:
+    """Kernel time of mimo_preprocess_batch on a resident batch (launch
+    events around each launch), against the algorithmic bytes: sources read
+    once, every row written once per requested order."""
+    import torch
+
+    tdtype = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    bpv = 4 if out_dtype == "f32" else 2
+    if merge and rows is None:
+        rows = torch.empty((plan.total_rows, 1536), dtype=tdtype, device="cuda")
+    rows_col = torch.empty((plan.total_rows, 1536), dtype=tdtype, device="cuda") if column else None
+    if ws is None:
+        ws = torch.empty(V.workspace_bytes(len(plan)), dtype=torch.uint8, device="cuda")
+    call = lambda: V.preprocess(src, plan, mean=batch.mean, std=batch.std, out_dtype=out_dtype,
+                                merge_order=merge, column_order=column, rows=rows,
+                                rows_col=rows_col, workspace=ws)
+    ms = time_launches(V, call, reps, torch.cuda.current_stream())
+    alg = algorithmic_bytes(plan, bpv, int(merge) + int(column))
+    gbs = alg["total"] / (ms * 1e-3) / 1e9
+    res = {"kernel": "preprocess_kernel", "dtype": out_dtype,
+           "orders": "+".join(o for o, on in (("merge", merge), ("column", column)) if on),
+           "rows": int(plan.total_rows), "ms": ms, "algorithmic_bytes": alg["total"],
+           "GB/s": gbs, "frac": gbs / HBM_PEAK_GBPS,
+           "images/s": sum(batch.frame_counts) / (ms * 1e-3)}
+    return res, (rows if merge else rows_col)
+
+
+def merge_only_leg(V, batch, plan, src, rows, ws, reps: int) -> dict:
+    """The throughput batch in float32, merge-block order only: the
+    configuration the 60%-of-HBM target is stated on (3.02 ms)."""
+    res, _ = pixel_rates(V, batch, plan, src, "f32", True, False, reps, rows=rows, ws=ws)
+    res["target_ms_at_60pct_of_peak"] = res["algorithmic_bytes"] / (0.6 * HBM_PEAK_GBPS * 1e9) * 1e3
+    return res
+
+
+def large_batch_leg(V, workloads, reps: int) -> dict:
+    """16 RGB 6000x4000 images downscaled to 3520x2336, bf16, merge order:
+    the bilinear path at size.  Beside it, the stock-HF contrast path on the
+    same resized batch: its kernel rate and the pixel shift between the two
+    paths' rows, in standard deviations."""
+    import torch
+
+    log("large batch: generating 16 x 6000x4000")
+    batch = workloads.large_16_6000x4000()
+    plan = V.plan_batch(batch.shapes)
+    src = V.processor.upload_sources(batch.packed, plan)
+    batch.packed = None
+    res, rows = pixel_rates(V, batch, plan, src, "bf16", True, False, reps)
+    res = {"workload": "large_16_6000x4000", **res}
+    log("large batch: stock-HF contrast path")
+    res["hf_contrast"] = hf_contrast_rates(V, batch, plan, src, rows, reps)
+    del rows, src
+    torch.cuda.empty_cache()
+    return res
+
+
+def single_image_leg(V, workloads, calls: int) -> dict:
+    """One 300x200 RGB image (resized to 288x192, float32): latency bound.
+    us_per_call is the host clock over `calls` back-to-back preprocess calls
+    with the outputs and workspace kept (synchronised once at the end);
+    us_per_call_allocating lets preprocess allocate them each call; kernel_us
+    is the launch-event time of the kernel alone.  The stock path's shift on
+    this uniform-noise image is beside it."""
+    import numpy as np
+    import torch
+
+    batch = workloads.single_rgb_300x200()
+    plan = V.plan_batch(batch.shapes)
+    src = V.processor.upload_sources(batch.packed, plan)
+    rows = torch.empty((plan.total_rows, 1536), dtype=torch.float32, device="cuda")
+    ws = torch.empty(V.workspace_bytes(1), dtype=torch.uint8, device="cuda")
+    call = lambda: V.preprocess(src, plan, mean=batch.mean, std=batch.std, rows=rows, workspace=ws)
+    for _ in range(50):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        call()
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) / calls * 1e6
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        V.preprocess(src, plan, mean=batch.mean, std=batch.std)
+    torch.cuda.synchronize()
+    us_alloc = (time.perf_counter() - t0) / calls * 1e6
+    kernel_ms = time_launches(V, call, 200, torch.cuda.current_stream())
+    res = {"workload": "single_rgb_300x200", "rows": int(plan.total_rows), "us_per_call": us,
+           "us_per_call_allocating": us_alloc, "kernel_us": kernel_ms * 1e3, "calls": calls,
+           "images/s": 1e6 / us}
+    res["hf_contrast"] = hf_contrast_rates(V, batch, plan, src, rows, 20)
     return res
 
 
@@ -263,6 +378,9 @@ def main():
                     help="skip timing the patch embedding on the same batch's rows")
     ap.add_argument("--no-hf", action="store_true",
                     help="skip timing the stock-HF contrast path on the same batch")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="skip the other configurations (float32 merge order only, the "
+                         "6000x4000 batch, the single image)")
     ap.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GIB",
                     help="only run a plain copy kernel of this size (counter calibration)")
     args = ap.parse_args()
@@ -364,7 +482,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": out_dtype,
         "data": "synthetic",
         "config": {
             "workload": args.workload,
@@ -417,6 +535,10 @@ def main():
         result["column_permute_gather"] = {"ms": ms, "GB/s": gb, "frac": gb / HBM_PEAK_GBPS}
         del gathered
 
+    if not args.no_legs and args.workload == "throughput_512_1024":
+        log("float32, merge-block order only")
+        result["merge_order_f32"] = merge_only_leg(V, batch, plan, src, rows, ws, reps=10)
+
     if not args.no_vit_tables:
         log("vit tables")
         result["vit_tables"] = vit_tables_rates(V, plan, ws, reps=10)
@@ -429,8 +551,15 @@ def main():
         log("patch embed")
         result["patch_embed"] = patch_embed_rates(V, batch, plan, src, ws, reps=5)
 
+    if not args.no_legs and args.workload == "throughput_512_1024":
+        del rows, rows_col, src
+        torch.cuda.empty_cache()
+        result["large_16_6000x4000"] = large_batch_leg(V, workloads, reps=10)
+        log("single image")
+        result["single_rgb_300x200"] = single_image_leg(V, workloads, calls=2000)
+
     if not args.no_cpu_baseline:
-        threads = max(1, min(16, os.cpu_count() or 1))
+        threads = host_threads()
         log("cpu baseline (oracle)", args.cpu_sample, "images,", threads, "threads")
         result["cpu_baseline"] = cpu_baseline(batch, plan, args.cpu_sample, threads, bpv)
         log("cpu baseline (oracle), one thread")

@@ -175,6 +175,19 @@ int64_t mimo_smart_nframes(int64_t total, double fps_src, double fps, int64_t mi
  */
 int64_t mimo_sample_frames(int64_t total, int64_t n, double fps_src, int64_t *idx, float *ts);
 
+/*
+ * Statistics in 0-255 units (processing page, MimoV2ImageProcessor: the
+ * image_mean / image_std it is given are 0-1 values, and standardisation
+ * runs on 0-255 floats with mean and std scaled by 255).
+ *   mean01, std01    host double[3]: the processor's per-channel statistics.
+ *   mean255, std255  host float[3]: float32(255 * v), the product formed in
+ *                    float64 and rounded once -- what mimo_preprocess_batch
+ *                    takes.
+ * Host only.  Returns MIMO_OK, or MIMO_E_INVALID for a null pointer, a
+ * non-finite value or std <= 0 (outputs untouched).
+ */
+int mimo_stats255(const double *mean01, const double *std01, float *mean255, float *std255);
+
 /* Bytes of device workspace mimo_preprocess_batch / mimo_column_permute need
  * for n images (descriptor tables copied from the host on each call). */
 size_t mimo_workspace_bytes(int32_t n);

@@ -367,3 +367,77 @@ def test_hf_extreme_vertical_downscale_is_refused_before_launch():
                                       None, 1 << 20, dummy, V.hf_workspace_bytes(desc), None)
     assert st == V.MIMO_E_UNSUPPORTED
     assert "downscale" in V.last_error()
+
+
+def test_stats255_matches_oracle():
+    for mean, std in (((0.485, 0.456, 0.406), (0.229, 0.224, 0.225)),
+                      (W.CLIP_MEAN, W.CLIP_STD), ((0.0, 0.5, 1.0), (1e-3, 1.0, 3.5))):
+        m, s = V._abi.stats255(mean, std)
+        om, os_ = oracle.stats255(mean, std)
+        assert np.array_equal(np.asarray(m, np.float32), om)
+        assert np.array_equal(np.asarray(s, np.float32), os_)
+    for bad in (((0.5, 0.5, 0.5), (0.2, 0.0, 0.2)), ((0.5, float("nan"), 0.5), (0.2, 0.2, 0.2)),
+                ((0.5, 0.5, 0.5), (0.2, -1.0, 0.2)), ((0.5, 0.5, 0.5), (0.2, 0.2, float("inf")))):
+        with pytest.raises(V.MimoError) as e:
+            V._abi.stats255(*bad)
+        assert e.value.code == V.MIMO_E_INVALID
+
+
+def test_binding_refuses_misshaped_tensors_before_any_launch():
+    """Every entry point that takes device tensors checks their shape, dtype
+    and contiguity (then their device) in the binding: a flat or narrow
+    output would otherwise make the library believe it holds far more rows
+    than it does.  Host tensors stand in here: the shape checks come first,
+    and a well-shaped host tensor fails the device check."""
+    torch = pytest.importorskip("torch")
+    desc, _, _, _ = V.plan_geometry([(64, 64, 3)])
+    f32, bf16 = torch.float32, torch.bfloat16
+    rows = torch.zeros((4, 1536), dtype=f32)
+    ws = torch.zeros(V.workspace_bytes(1), dtype=torch.uint8)
+    src = torch.zeros(64 * 64 * 3, dtype=torch.uint8)
+    m, s = (1.0, 1.0, 1.0), (1.0, 1.0, 1.0)
+
+    def refused(fn, *a, **k):
+        with pytest.raises(V.MimoError) as e:
+            fn(*a, **k)
+        assert e.value.code == V.MIMO_E_INVALID
+        return str(e.value)
+
+    # preprocess_batch
+    refused(V.preprocess_batch, desc, src, m, s, rows=torch.zeros(4 * 1536, dtype=f32), workspace=ws)
+    refused(V.preprocess_batch, desc, src, m, s, rows=torch.zeros((4, 768), dtype=f32), workspace=ws)
+    refused(V.preprocess_batch, desc, src, m, s, rows=torch.zeros((1536, 4), dtype=f32).t(), workspace=ws)
+    refused(V.preprocess_batch, desc, src, m, s, rows=torch.zeros((4, 1536), dtype=torch.float16),
+            workspace=ws)
+    refused(V.preprocess_batch, desc, src, m, s, rows=rows, rows_col=torch.zeros((4, 1536), dtype=bf16),
+            workspace=ws)
+    refused(V.preprocess_batch, desc, src.float(), m, s, rows=rows, workspace=ws)
+    refused(V.preprocess_batch, desc, src, m, s, rows=rows, workspace=None)
+    assert "GPU" in refused(V.preprocess_batch, desc, src, m, s, rows=rows, workspace=ws)
+    # column_permute
+    refused(V.column_permute, desc, rows, torch.zeros(4 * 1536, dtype=f32), ws)
+    refused(V.column_permute, desc, rows, torch.zeros((4, 1536), dtype=bf16), ws)
+    refused(V.column_permute, desc, rows.view(8, 768), rows.clone().view(8, 768), ws)
+    assert "GPU" in refused(V.column_permute, desc, rows, rows.clone(), ws)
+    # patch_embed
+    w = torch.zeros((256, 1536), dtype=bf16)
+    refused(V.patch_embed, rows, w)                                      # float32 rows
+    refused(V.patch_embed, rows.to(bf16), torch.zeros((256, 1000), dtype=bf16))
+    refused(V.patch_embed, rows.to(bf16), w.float())
+    refused(V.patch_embed, rows.to(bf16), w, bias=torch.zeros(255))
+    refused(V.patch_embed, rows.to(bf16), w, out=torch.zeros((4, 128), dtype=f32))
+    refused(V.patch_embed, rows.to(bf16), w, out=torch.zeros((3, 256), dtype=f32))
+    assert "GPU" in refused(V.patch_embed, rows.to(bf16), w, out=torch.zeros((4, 256), dtype=f32))
+    # fold_patch_weights
+    refused(V.fold_patch_weights, torch.zeros((256, 768), dtype=bf16))
+    refused(V.fold_patch_weights, w, torch.zeros((128, 768), dtype=bf16))
+    # preprocess_hf_batch
+    hdesc, _, _, _ = V.plan_hf([(64, 64, 3)])
+    refused(V.preprocess_hf_batch, hdesc, src, m, s, rows=torch.zeros(4 * 1536, dtype=f32), workspace=ws)
+    refused(V.preprocess_hf_batch, hdesc, src, m, s, rows=None, workspace=ws)
+    assert "GPU" in refused(V.preprocess_hf_batch, hdesc, src, m, s, rows=rows, workspace=ws)
+    # rotary tables and window index
+    refused(V.rotary_tables, desc, ws, pos=torch.zeros((4, 2), dtype=torch.int64))
+    refused(V.rotary_tables, desc, ws, cos=torch.zeros((4, 16), dtype=f32), rope_dim=32)
+    refused(V.window_index, desc, ws, index=torch.zeros((1, 1), dtype=torch.int64))
+    refused(V.window_index, desc, ws, index=torch.zeros(1, dtype=torch.int32))

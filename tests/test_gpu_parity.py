@@ -365,3 +365,29 @@ def test_workload_throughput_512_1024(V):
     V.column_permute(plan.desc, out["pixel_values"], gathered, ws)
     torch.cuda.synchronize()
     assert torch.equal(gathered, out["pixel_values_col"])
+
+
+def test_side_stream_back_to_back_allocations(V):
+    """preprocess on a non-default stream: the outputs and workspace it
+    allocates belong to that stream, so allocations made right after on the
+    current stream (and overwritten there) cannot take their memory while the
+    side stream's table copy and kernel still use it."""
+    _say("side stream")
+    batch = W.uniform_images([(200, 300, 3), (45, 77, 3), (130, 64, 3)], seed=91)
+    plan = V.plan_batch(batch.shapes)
+    src = V.processor.upload_sources(batch.packed, plan)
+    side = torch.cuda.Stream()
+    outs = []
+    for rep in range(4):
+        out = V.preprocess(src, plan, mean=batch.mean, std=batch.std, column_order=True, stream=side)
+        outs.append(out)
+        # busy the current stream with fresh allocations of the same sizes,
+        # filled with garbage, while the side stream may still be working
+        junk = [torch.full((max(plan.total_rows, 1), 1536), 7.0, device="cuda") for _ in range(2)]
+        junk.append(torch.full((V.workspace_bytes(len(plan)) + 64,), 255, dtype=torch.uint8, device="cuda"))
+        del junk
+    side.synchronize()
+    torch.cuda.synchronize()
+    for out in outs:
+        _check_properties(out)
+        _check_full(V, batch, plan, out, "f32", column=True)

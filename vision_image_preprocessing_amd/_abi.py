@@ -79,6 +79,7 @@ SIGNATURES = {
     "mimo_smart_nframes": ([_I64, ctypes.c_double, ctypes.c_double, _I64, _I64], _I64),
     "mimo_sample_frames": ([_I64, _I64, ctypes.c_double, _P, _P], _I64),
     "mimo_workspace_bytes": ([_I32], _SZ),
+    "mimo_stats255": ([_P, _P, _P, _P], ctypes.c_int),
     "mimo_preprocess_batch": ([_I32, _P, _P, _I64, _P, _P, _I32, _P, _P, _I64, _P, _SZ, _P],
                               ctypes.c_int),
     "mimo_column_permutation": ([_I64, _I64, _I64, _I64, _P], ctypes.c_int),
@@ -272,6 +273,16 @@ def workspace_bytes(n: int) -> int:
     return int(load().mimo_workspace_bytes(int(n)))
 
 
+def stats255(mean, std):
+    """mimo_stats255: the processor's 0-1 statistics in 0-255 units, as the
+    float32 lists (mean255, std255) that preprocess_batch takes."""
+    m01 = (ctypes.c_double * 3)(*[float(v) for v in mean])
+    s01 = (ctypes.c_double * 3)(*[float(v) for v in std])
+    m255, s255 = (ctypes.c_float * 3)(), (ctypes.c_float * 3)()
+    _check(load().mimo_stats255(m01, s01, m255, s255), "stats255")
+    return list(m255), list(s255)
+
+
 def column_permutation(grid_t: int, grid_h: int, grid_w: int, merge: int = 2) -> np.ndarray:
     """mimo_column_permutation: perm[dst] = src (int64)."""
     perm = np.empty(int(grid_t) * int(grid_h) * int(grid_w), dtype=np.int64)
@@ -296,6 +307,47 @@ def _dtype_code(t) -> int:
     raise MimoError(MIMO_E_INVALID, f"output dtype {t.dtype} is not float32 or bfloat16")
 
 
+def _require(ok: bool, what: str):
+    if not ok:
+        raise MimoError(MIMO_E_INVALID, what)
+
+
+def _check_matrix(t, what: str, width: int, dtypes):
+    """t must be a contiguous 2-D tensor [capacity, width] of one of dtypes."""
+    _require(t.dim() == 2 and t.shape[1] == width and t.is_contiguous() and t.dtype in dtypes,
+             f"{what}: need a contiguous [capacity, {width}] tensor of "
+             f"{' or '.join(str(d) for d in dtypes)}, got {tuple(t.shape)} {t.dtype}"
+             + ("" if t.is_contiguous() else " (not contiguous)"))
+
+
+def _check_bytes(t, what: str):
+    """t must be a contiguous uint8 tensor (its numel is its size in bytes)."""
+    import torch
+    _require(t.dtype == torch.uint8 and t.is_contiguous() and t.dim() == 1,
+             f"{what}: need a contiguous 1-D uint8 tensor, got {tuple(t.shape)} {t.dtype}")
+
+
+def _check_device(tensors, what: str):
+    """Every tensor lives on one GPU (checked after shapes and dtypes, so
+    mis-shaped host tensors are reported as such)."""
+    devs = {(t.device.type, t.device.index) for t in tensors if t is not None}
+    _require(len(devs) == 1 and next(iter(devs))[0] == "cuda",
+             f"{what}: every tensor must be on one GPU, got {sorted(map(str, devs))}")
+
+
+def _out_tensors(rows, rows_col, what: str):
+    """Checks the pixel-path outputs: one or two contiguous [capacity, 1536]
+    tensors of one dtype (float32 or bfloat16); returns (dtype code,
+    capacity)."""
+    import torch
+    outs = [t for t in (rows, rows_col) if t is not None]
+    _require(bool(outs), f"{what}: both outputs are None")
+    for t in outs:
+        _check_matrix(t, what + " output", ROW_LEN, (torch.float32, torch.bfloat16))
+    _require(len({t.dtype for t in outs}) == 1, f"{what}: the two outputs differ in dtype")
+    return _dtype_code(outs[0]), min(t.shape[0] for t in outs)
+
+
 def preprocess_batch(desc: np.ndarray, src, mean255, std255, rows=None, rows_col=None,
                      workspace=None, stream=None):
     """mimo_preprocess_batch.  src: uint8 device tensor (packed images,
@@ -305,37 +357,33 @@ def preprocess_batch(desc: np.ndarray, src, mean255, std255, rows=None, rows_col
     Enqueues on `stream` (default: torch's current stream)."""
     desc = np.ascontiguousarray(desc, dtype=IMAGE_DESC_DTYPE)
     n = desc.shape[0]
+    code_dtype, cap = _out_tensors(rows, rows_col, "preprocess_batch")
     out = rows if rows is not None else rows_col
-    if out is None:
-        raise MimoError(MIMO_E_INVALID, "preprocess_batch: both outputs are None")
-    code_dtype = _dtype_code(out)
-    cap = None
-    for t in (rows, rows_col):
-        if t is None:
-            continue
-        if _dtype_code(t) != code_dtype or t.dim() != 2 or t.shape[1] != ROW_LEN or not t.is_contiguous():
-            raise MimoError(MIMO_E_INVALID, "preprocess_batch: outputs must be contiguous "
-                                            "[capacity, 1536] tensors of one dtype")
-        cap = t.shape[0] if cap is None else min(cap, t.shape[0])
+    _check_bytes(src, "preprocess_batch: src")
+    _require(workspace is not None, "preprocess_batch: workspace is None")
+    _check_bytes(workspace, "preprocess_batch: workspace")
+    _check_device([src, rows, rows_col, workspace], "preprocess_batch")
     m = (ctypes.c_float * 3)(*[float(v) for v in mean255])
     s = (ctypes.c_float * 3)(*[float(v) for v in std255])
     code = load().mimo_preprocess_batch(
         n, desc.ctypes.data, src.data_ptr(), src.numel(), m, s, code_dtype,
         rows.data_ptr() if rows is not None else None,
         rows_col.data_ptr() if rows_col is not None else None,
-        cap, workspace.data_ptr() if workspace is not None else None,
-        workspace.numel() if workspace is not None else 0,
-        _stream_handle(stream, out.device))
+        cap, workspace.data_ptr(), workspace.numel(), _stream_handle(stream, out.device))
     _check(code, "preprocess_batch")
 
 
 def column_permute(desc: np.ndarray, rows_in, rows_out, workspace, stream=None):
     """mimo_column_permute: merge-order rows -> column-order rows (gather)."""
+    import torch
     desc = np.ascontiguousarray(desc, dtype=IMAGE_DESC_DTYPE)
     n = desc.shape[0]
+    for t, name in ((rows_in, "rows_in"), (rows_out, "rows_out")):
+        _check_matrix(t, "column_permute: " + name, ROW_LEN, (torch.float32, torch.bfloat16))
+    _require(rows_in.dtype == rows_out.dtype, "column_permute: rows_in and rows_out differ in dtype")
     code_dtype = _dtype_code(rows_in)
-    if _dtype_code(rows_out) != code_dtype:
-        raise MimoError(MIMO_E_INVALID, "column_permute: dtype mismatch")
+    _check_bytes(workspace, "column_permute: workspace")
+    _check_device([rows_in, rows_out, workspace], "column_permute")
     cap = min(rows_in.shape[0], rows_out.shape[0])
     code = load().mimo_column_permute(n, desc.ctypes.data, rows_in.data_ptr(), rows_out.data_ptr(),
                                       code_dtype, cap, workspace.data_ptr(), workspace.numel(),
@@ -355,10 +403,19 @@ def rotary_tables(desc: np.ndarray, workspace, pos=None, cos=None, sin=None, col
     """mimo_rotary_tables: fills the given device tensors (pos int32 [rows, 2],
     cos / sin float32 [rows, rope_dim]) for the rows in merge-block order, or
     column order with column=True."""
+    import torch
     desc = np.ascontiguousarray(desc, dtype=IMAGE_DESC_DTYPE)
     outs = [t for t in (pos, cos, sin) if t is not None]
-    cap = min(t.shape[0] for t in outs) if outs else 0
-    dev = outs[0].device if outs else workspace.device
+    _require(bool(outs), "rotary_tables: no output given")
+    if pos is not None:
+        _check_matrix(pos, "rotary_tables: pos", 2, (torch.int32,))
+    for t, name in ((cos, "cos"), (sin, "sin")):
+        if t is not None:
+            _check_matrix(t, "rotary_tables: " + name, int(rope_dim), (torch.float32,))
+    _check_bytes(workspace, "rotary_tables: workspace")
+    _check_device(outs + [workspace], "rotary_tables")
+    cap = min(t.shape[0] for t in outs)
+    dev = outs[0].device
     code = load().mimo_rotary_tables(
         desc.shape[0], desc.ctypes.data, MIMO_ORDER_COLUMN if column else MIMO_ORDER_MERGE,
         int(rope_dim), float(theta),
@@ -373,10 +430,17 @@ def window_index(desc: np.ndarray, workspace, index=None, inverse=None, column_m
                  stream=None):
     """mimo_window_index: fills int64 device tensors [units] (index[dst] = src,
     inverse[src] = dst)."""
+    import torch
     desc = np.ascontiguousarray(desc, dtype=IMAGE_DESC_DTYPE)
     outs = [t for t in (index, inverse) if t is not None]
-    cap = min(t.shape[0] for t in outs) if outs else 0
-    dev = outs[0].device if outs else workspace.device
+    _require(bool(outs), "window_index: no output given")
+    for t in outs:
+        _require(t.dim() == 1 and t.dtype == torch.int64 and t.is_contiguous(),
+                 f"window_index: need contiguous 1-D int64 outputs, got {tuple(t.shape)} {t.dtype}")
+    _check_bytes(workspace, "window_index: workspace")
+    _check_device(outs + [workspace], "window_index")
+    cap = min(t.shape[0] for t in outs)
+    dev = outs[0].device
     code = load().mimo_window_index(
         desc.shape[0], desc.ctypes.data, int(bool(column_major)),
         index.data_ptr() if index is not None else None,
@@ -399,9 +463,13 @@ def chunk_seqlens(desc: np.ndarray) -> np.ndarray:
 def fold_patch_weights(w, w_folded=None, stream=None):
     """mimo_fold_patch_weights: bf16 [E, 1536] -> bf16 [E, 768] (device tensors)."""
     import torch
+    _check_matrix(w, "fold_patch_weights: w", ROW_LEN, (torch.bfloat16,))
     e = w.shape[0]
     if w_folded is None:
         w_folded = torch.empty((e, ROW_LEN // 2), dtype=torch.bfloat16, device=w.device)
+    _check_matrix(w_folded, "fold_patch_weights: w_folded", ROW_LEN // 2, (torch.bfloat16,))
+    _require(w_folded.shape[0] == e, "fold_patch_weights: w_folded must have w's row count")
+    _check_device([w, w_folded], "fold_patch_weights")
     _check(load().mimo_fold_patch_weights(e, w.data_ptr(), w_folded.data_ptr(),
                                           _stream_handle(stream, w.device)), "fold_patch_weights")
     return w_folded
@@ -411,11 +479,22 @@ def patch_embed(rows, w, bias=None, out=None, out_dtype: str = "bf16", stream=No
     """mimo_patch_embed: rows bf16 [n, 1536] x w bf16 [E, 1536] (or folded
     [E, 768]) -> out [n, E] (+ bias float32 [E])."""
     import torch
+    _check_matrix(rows, "patch_embed: rows", ROW_LEN, (torch.bfloat16,))
+    _require(w.dim() == 2 and w.shape[1] in (ROW_LEN, ROW_LEN // 2),
+             f"patch_embed: w must be [E, 1536] or folded [E, 768], got {tuple(w.shape)}")
+    _check_matrix(w, "patch_embed: w", int(w.shape[1]), (torch.bfloat16,))
     n, e = rows.shape[0], w.shape[0]
     folded = int(w.shape[1] == ROW_LEN // 2)
-    tdtype = {"f32": torch.float32, "bf16": torch.bfloat16}[out_dtype]
+    if bias is not None:
+        _require(bias.dim() == 1 and bias.shape[0] == e and bias.dtype == torch.float32
+                 and bias.is_contiguous(), f"patch_embed: bias must be contiguous float32 [{e}]")
     if out is None:
+        _require(out_dtype in ("f32", "bf16"), f"patch_embed: out_dtype {out_dtype!r} is not f32 or bf16")
+        tdtype = {"f32": torch.float32, "bf16": torch.bfloat16}[out_dtype]
         out = torch.empty((n, e), dtype=tdtype, device=rows.device)
+    _check_matrix(out, "patch_embed: out", e, (torch.float32, torch.bfloat16))
+    _require(out.shape[0] == n, f"patch_embed: out must be [{n}, {e}], got {tuple(out.shape)}")
+    _check_device([rows, w, bias, out], "patch_embed")
     code = load().mimo_patch_embed(n, rows.data_ptr(), e, w.data_ptr(), folded,
                                    bias.data_ptr() if bias is not None else None,
                                    _dtype_code(out), out.data_ptr(),
@@ -456,15 +535,17 @@ def preprocess_hf_batch(desc: np.ndarray, src, mean01, std01, rows=None, rows_co
     float32 or bf16 [capacity, 1536], workspace uint8)."""
     desc = np.ascontiguousarray(desc, dtype=IMAGE_DESC_DTYPE)
     n = desc.shape[0]
+    code_dtype, cap = _out_tensors(rows, rows_col, "preprocess_hf_batch")
     out = rows if rows is not None else rows_col
-    code_dtype = _dtype_code(out)
+    _check_bytes(src, "preprocess_hf_batch: src")
+    _require(workspace is not None, "preprocess_hf_batch: workspace is None")
+    _check_bytes(workspace, "preprocess_hf_batch: workspace")
+    _check_device([src, rows, rows_col, workspace], "preprocess_hf_batch")
     m = (ctypes.c_float * 3)(*[float(v) for v in mean01])
     s = (ctypes.c_float * 3)(*[float(v) for v in std01])
-    cap = min(t.shape[0] for t in (rows, rows_col) if t is not None)
     code = load().mimo_preprocess_hf_batch(
         n, desc.ctypes.data, src.data_ptr(), src.numel(), m, s, code_dtype,
         rows.data_ptr() if rows is not None else None,
         rows_col.data_ptr() if rows_col is not None else None,
-        cap, workspace.data_ptr() if workspace is not None else None,
-        workspace.numel() if workspace is not None else 0, _stream_handle(stream, out.device))
+        cap, workspace.data_ptr(), workspace.numel(), _stream_handle(stream, out.device))
     _check(code, "preprocess_hf_batch")

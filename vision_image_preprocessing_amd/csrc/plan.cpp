@@ -357,6 +357,22 @@ int64_t mimo_sample_frames(int64_t total, int64_t n, double fps_src, int64_t *id
 
 size_t mimo_workspace_bytes(int32_t n) { return n < 0 ? 0 : ws_total_bytes(n); }
 
+int mimo_stats255(const double *mean01, const double *std01, float *mean255, float *std255) {
+    clear_error();
+    if (!mean01 || !std01 || !mean255 || !std255)
+        return set_error(MIMO_E_INVALID, "stats255: null pointer");
+    for (int c = 0; c < 3; ++c)
+        if (!std::isfinite(mean01[c]) || !std::isfinite(std01[c]) || !(std01[c] > 0.0))
+            return set_error(MIMO_E_INVALID, "stats255: statistics must be finite with std > 0");
+    // the processor's statistics scaled to 0-255 units: the product formed in
+    // float64, then rounded once to float32
+    for (int c = 0; c < 3; ++c) {
+        mean255[c] = float(255.0 * mean01[c]);
+        std255[c] = float(255.0 * std01[c]);
+    }
+    return MIMO_OK;
+}
+
 int mimo_column_permutation(int64_t grid_t, int64_t grid_h, int64_t grid_w, int64_t merge,
                             int64_t *perm) {
     clear_error();

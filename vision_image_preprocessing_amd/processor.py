@@ -8,6 +8,8 @@ uint8 HWC arrays (RGB or RGBA).
 """
 from __future__ import annotations
 
+import contextlib
+import functools
 import threading
 from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
@@ -21,11 +23,29 @@ IMAGENET_MEAN = (0.485, 0.456, 0.406)
 IMAGENET_STD = (0.229, 0.224, 0.225)
 
 
+@functools.lru_cache(maxsize=64)
+def _stats255_cached(mean: tuple, std: tuple):
+    m, s = _abi.stats255(mean, std)
+    return tuple(m), tuple(s)
+
+
 def stats255(mean, std):
-    """Statistics in 0-255 units as float32 (products formed in float64)."""
-    m = [float(np.float32(255.0 * float(v))) for v in mean]
-    s = [float(np.float32(255.0 * float(v))) for v in std]
-    return m, s
+    """Statistics in 0-255 units (mimo_stats255): float32(255 * v), the
+    product formed in float64.  Cached per (mean, std)."""
+    return _stats255_cached(tuple(float(v) for v in mean), tuple(float(v) for v in std))
+
+
+def _on_stream(torch, stream, tensors):
+    """The context a call runs in: with a caller's stream, that stream is
+    made current, so the outputs and workspace allocated here belong to it in
+    torch's caching allocator, and the caller's tensors are marked as used on
+    it (their memory is not handed out again before its work has run)."""
+    if stream is None:
+        return contextlib.nullcontext()
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+    return torch.cuda.stream(stream)
 
 
 @dataclass
@@ -33,6 +53,7 @@ class BatchPlan:
     desc: np.ndarray          # IMAGE_DESC_DTYPE [n]
     total_rows: int
     total_src_bytes: int
+    _grid: np.ndarray = None  # image_grid_thw, formed on first use
 
     @property
     def src_capacity(self) -> int:
@@ -47,8 +68,10 @@ class BatchPlan:
 
     @property
     def image_grid_thw(self) -> np.ndarray:
-        return np.stack([self.desc["grid_t"], self.desc["grid_h"], self.desc["grid_w"]],
-                        axis=1).astype(np.int64)
+        if self._grid is None:
+            self._grid = np.stack([self.desc["grid_t"], self.desc["grid_h"], self.desc["grid_w"]],
+                                  axis=1).astype(np.int64)
+        return self._grid
 
     def __len__(self):
         return int(self.desc.shape[0])
@@ -165,18 +188,19 @@ def preprocess(src_dev, plan: BatchPlan, mean=IMAGENET_MEAN, std=IMAGENET_STD,
     tdtype = {"f32": torch.float32, "bf16": torch.bfloat16}[out_dtype]
     n_rows = max(plan.total_rows, 1)
     own_rows, own_col = merge_order and rows is None, column_order and rows_col is None
-    if own_rows:
-        rows = torch.empty((n_rows, _abi.ROW_LEN), dtype=tdtype, device=dev)
-    if own_col:
-        rows_col = torch.empty((n_rows, _abi.ROW_LEN), dtype=tdtype, device=dev)
-    if workspace is None:
-        workspace = torch.empty(max(_abi.workspace_bytes(len(plan)), 16), dtype=torch.uint8,
-                                device=dev)
-    m255, s255 = stats255(mean, std)
-    _abi.preprocess_batch(plan.desc, src_dev, m255, s255,
-                          rows=rows if merge_order else None,
-                          rows_col=rows_col if column_order else None,
-                          workspace=workspace, stream=stream)
+    with _on_stream(torch, stream, (src_dev, rows, rows_col, workspace)):
+        if own_rows:
+            rows = torch.empty((n_rows, _abi.ROW_LEN), dtype=tdtype, device=dev)
+        if own_col:
+            rows_col = torch.empty((n_rows, _abi.ROW_LEN), dtype=tdtype, device=dev)
+        if workspace is None:
+            workspace = torch.empty(max(_abi.workspace_bytes(len(plan)), 16), dtype=torch.uint8,
+                                    device=dev)
+        m255, s255 = stats255(mean, std)
+        _abi.preprocess_batch(plan.desc, src_dev, m255, s255,
+                              rows=rows if merge_order else None,
+                              rows_col=rows_col if column_order else None,
+                              workspace=workspace, stream=stream)
     # outputs allocated here hold at least one row (the library takes no null
     # output); hand back exactly the plan's rows
     if own_rows:
@@ -285,18 +309,19 @@ def vit_tables(plan: BatchPlan, device="cuda", column: bool = False, rope_dim: i
     import torch
     n_rows = max(plan.total_rows, 1)
     units = max(plan.total_rows // 4, 1)
-    if workspace is None:
-        workspace = torch.empty(max(_abi.workspace_bytes(len(plan)), 16), dtype=torch.uint8,
-                                device=device)
-    pos = torch.empty((n_rows, 2), dtype=torch.int32, device=device)
-    cos = torch.empty((n_rows, rope_dim), dtype=torch.float32, device=device)
-    sin = torch.empty((n_rows, rope_dim), dtype=torch.float32, device=device)
-    index = torch.empty(units, dtype=torch.int64, device=device)
-    inverse = torch.empty(units, dtype=torch.int64, device=device)
-    _abi.rotary_tables(plan.desc, workspace, pos=pos, cos=cos, sin=sin, column=column,
-                       rope_dim=rope_dim, theta=theta, stream=stream)
-    _abi.window_index(plan.desc, workspace, index=index, inverse=inverse, column_major=column,
-                      stream=stream)
+    with _on_stream(torch, stream, (workspace,)):
+        if workspace is None:
+            workspace = torch.empty(max(_abi.workspace_bytes(len(plan)), 16), dtype=torch.uint8,
+                                    device=device)
+        pos = torch.empty((n_rows, 2), dtype=torch.int32, device=device)
+        cos = torch.empty((n_rows, rope_dim), dtype=torch.float32, device=device)
+        sin = torch.empty((n_rows, rope_dim), dtype=torch.float32, device=device)
+        index = torch.empty(units, dtype=torch.int64, device=device)
+        inverse = torch.empty(units, dtype=torch.int64, device=device)
+        _abi.rotary_tables(plan.desc, workspace, pos=pos, cos=cos, sin=sin, column=column,
+                           rope_dim=rope_dim, theta=theta, stream=stream)
+        _abi.window_index(plan.desc, workspace, index=index, inverse=inverse, column_major=column,
+                          stream=stream)
     rows = plan.total_rows
     return {
         "rotary_pos": pos[:rows], "rope_cos": cos[:rows], "rope_sin": sin[:rows],
@@ -324,16 +349,17 @@ def preprocess_hf(src_dev, plan: BatchPlan, mean=IMAGENET_MEAN, std=IMAGENET_STD
     tdtype = {"f32": torch.float32, "bf16": torch.bfloat16}[out_dtype]
     n_rows = max(plan.total_rows, 1)
     own_rows, own_col = merge_order and rows is None, column_order and rows_col is None
-    if own_rows:
-        rows = torch.empty((n_rows, _abi.ROW_LEN), dtype=tdtype, device=dev)
-    if own_col:
-        rows_col = torch.empty((n_rows, _abi.ROW_LEN), dtype=tdtype, device=dev)
-    if workspace is None:
-        workspace = torch.empty(max(_abi.hf_workspace_bytes(plan.desc), 16), dtype=torch.uint8,
-                                device=dev)
-    _abi.preprocess_hf_batch(plan.desc, src_dev, mean, std, rows=rows if merge_order else None,
-                             rows_col=rows_col if column_order else None, workspace=workspace,
-                             stream=stream)
+    with _on_stream(torch, stream, (src_dev, rows, rows_col, workspace)):
+        if own_rows:
+            rows = torch.empty((n_rows, _abi.ROW_LEN), dtype=tdtype, device=dev)
+        if own_col:
+            rows_col = torch.empty((n_rows, _abi.ROW_LEN), dtype=tdtype, device=dev)
+        if workspace is None:
+            workspace = torch.empty(max(_abi.hf_workspace_bytes(plan.desc), 16), dtype=torch.uint8,
+                                    device=dev)
+        _abi.preprocess_hf_batch(plan.desc, src_dev, mean, std, rows=rows if merge_order else None,
+                                 rows_col=rows_col if column_order else None, workspace=workspace,
+                                 stream=stream)
     # outputs allocated here hold at least one row (the library takes no null
     # output); hand back exactly the plan's rows
     if own_rows:
