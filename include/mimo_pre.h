@@ -223,6 +223,30 @@ int mimo_preprocess_batch(int32_t n, const mimo_image_desc *desc, const uint8_t 
                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * mimo_preprocess_batch for callers that cannot allocate memory -- code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc:
+ * the same kernel, with the descriptor tables kept in a device scratch array
+ * inside the library instead of a caller's workspace.  Neither this call nor
+ * anything it calls allocates: the scratch is static device memory of
+ * MIMO_NOALLOC_SCRATCH_BYTES (640.5 KiB) per GPU, held until the process
+ * ends, and the host hands the tables over in the arguments of small copy
+ * kernels (one per 3 KB of table, on `stream`, before the main kernel).
+ *   n   at most MIMO_NOALLOC_MAX_IMAGES images; more returns
+ *       MIMO_E_CAPACITY before anything is enqueued.
+ * Other arguments, results and errors as for mimo_preprocess_batch.
+ * Every call on one GPU shares that GPU's scratch, which keeps the last
+ * call's tables: calls on one stream are ordered and safe, but calls that
+ * overlap on one GPU (several streams, or host threads on different
+ * streams) race on the scratch and must be serialised by the caller.
+ */
+#define MIMO_NOALLOC_MAX_IMAGES 8192
+#define MIMO_NOALLOC_SCRATCH_BYTES 655872 /* mimo_workspace_bytes(MIMO_NOALLOC_MAX_IMAGES) */
+int mimo_preprocess_batch_noalloc(int32_t n, const mimo_image_desc *desc, const uint8_t *src,
+                                  int64_t src_capacity, const float *mean255, const float *std255,
+                                  int32_t out_dtype, void *rows, void *rows_col, int64_t capacity_rows,
+                                  void *stream);
+
+/*
  * column_permutation (cortiq mimo_vision): for one image with grid
  * (grid_t, grid_h, grid_w) and merge size m, perm[dst] = src lists the merge
  * units by (t, block col, block row), each unit's m*m rows kept together.

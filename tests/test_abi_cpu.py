@@ -441,3 +441,18 @@ def test_binding_refuses_misshaped_tensors_before_any_launch():
     refused(V.rotary_tables, desc, ws, cos=torch.zeros((4, 16), dtype=f32), rope_dim=32)
     refused(V.window_index, desc, ws, index=torch.zeros((1, 1), dtype=torch.int64))
     refused(V.window_index, desc, ws, index=torch.zeros(1, dtype=torch.int32))
+
+
+def test_noalloc_refuses_too_many_images_before_any_device_work():
+    """mimo_preprocess_batch_noalloc checks the image count against its
+    static scratch first: the pointers are never touched (these are not
+    device addresses) and nothing is enqueued."""
+    lib = V.load()
+    n = V._abi.NOALLOC_MAX_IMAGES + 1
+    m = (ctypes.c_float * 3)(0.0, 0.0, 0.0)
+    s = (ctypes.c_float * 3)(1.0, 1.0, 1.0)
+    before = V.dispatch_count()
+    code = lib.mimo_preprocess_batch_noalloc(n, 0x1000, 0x2000, 1 << 20, m, s, V.MIMO_F32, 0x3000,
+                                             None, 1 << 20, None)
+    assert code == V.MIMO_E_CAPACITY and V.dispatch_count() == before
+    assert "8192" in V.last_error()

@@ -82,6 +82,8 @@ SIGNATURES = {
     "mimo_stats255": ([_P, _P, _P, _P], ctypes.c_int),
     "mimo_preprocess_batch": ([_I32, _P, _P, _I64, _P, _P, _I32, _P, _P, _I64, _P, _SZ, _P],
                               ctypes.c_int),
+    "mimo_preprocess_batch_noalloc": ([_I32, _P, _P, _I64, _P, _P, _I32, _P, _P, _I64, _P],
+                                      ctypes.c_int),
     "mimo_column_permutation": ([_I64, _I64, _I64, _I64, _P], ctypes.c_int),
     "mimo_column_permute": ([_I32, _P, _P, _P, _I32, _I64, _P, _SZ, _P], ctypes.c_int),
     "mimo_status_string": ([ctypes.c_int], ctypes.c_char_p),
@@ -371,6 +373,31 @@ def preprocess_batch(desc: np.ndarray, src, mean255, std255, rows=None, rows_col
         rows_col.data_ptr() if rows_col is not None else None,
         cap, workspace.data_ptr(), workspace.numel(), _stream_handle(stream, out.device))
     _check(code, "preprocess_batch")
+
+
+NOALLOC_MAX_IMAGES = 8192  # MIMO_NOALLOC_MAX_IMAGES
+
+
+def preprocess_batch_noalloc(desc: np.ndarray, src, mean255, std255, rows=None, rows_col=None,
+                             stream=None):
+    """mimo_preprocess_batch_noalloc: preprocess_batch with the descriptor
+    tables in the library's static device scratch (no workspace, nothing
+    allocated); at most NOALLOC_MAX_IMAGES images.  Calls that overlap on
+    one GPU race on the scratch."""
+    desc = np.ascontiguousarray(desc, dtype=IMAGE_DESC_DTYPE)
+    n = desc.shape[0]
+    code_dtype, cap = _out_tensors(rows, rows_col, "preprocess_batch_noalloc")
+    out = rows if rows is not None else rows_col
+    _check_bytes(src, "preprocess_batch_noalloc: src")
+    _check_device([src, rows, rows_col], "preprocess_batch_noalloc")
+    m = (ctypes.c_float * 3)(*[float(v) for v in mean255])
+    s = (ctypes.c_float * 3)(*[float(v) for v in std255])
+    code = load().mimo_preprocess_batch_noalloc(
+        n, desc.ctypes.data, src.data_ptr(), src.numel(), m, s, code_dtype,
+        rows.data_ptr() if rows is not None else None,
+        rows_col.data_ptr() if rows_col is not None else None,
+        cap, _stream_handle(stream, out.device))
+    _check(code, "preprocess_batch_noalloc")
 
 
 def column_permute(desc: np.ndarray, rows_in, rows_out, workspace, stream=None):

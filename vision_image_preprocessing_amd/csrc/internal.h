@@ -49,10 +49,11 @@ constexpr int32_t kFlagIdentity = 1;  // dst == src on both axes
 
 // Workspace layout: [DevImage x n][int64 tile_begin x (n+1)][int64 row_begin x (n+1)],
 // each part 256-byte aligned.
-inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
-inline size_t ws_images_bytes(int32_t n) { return align256(sizeof(DevImage) * size_t(n)); }
-inline size_t ws_prefix_bytes(int32_t n) { return align256(sizeof(int64_t) * (size_t(n) + 1)); }
-inline size_t ws_total_bytes(int32_t n) { return ws_images_bytes(n) + 2 * ws_prefix_bytes(n); }
+constexpr size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+constexpr size_t ws_images_bytes(int32_t n) { return align256(sizeof(DevImage) * size_t(n)); }
+constexpr size_t ws_prefix_bytes(int32_t n) { return align256(sizeof(int64_t) * (size_t(n) + 1)); }
+constexpr size_t ws_total_bytes(int32_t n) { return ws_images_bytes(n) + 2 * ws_prefix_bytes(n); }
+constexpr size_t ws_total_bytes_const(int32_t n) { return ws_total_bytes(n); }
 
 // Thread-local error reporting.
 int set_error(int code, const std::string &msg);

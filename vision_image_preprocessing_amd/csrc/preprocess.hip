@@ -739,20 +739,20 @@ int64_t band_estimate(const DevImage &d, int R) {
 }
 
 struct BuiltTables {
-    std::vector<uint8_t> bytes;  // workspace image
+    std::vector<uint8_t> bytes;  // workspace image (build_tables)
     int64_t total_tiles = 0;
     int64_t total_rows = 0;
     int32_t band_capacity = 0;  // dwords
     bool clips = false;         // some item has two or more frames
 };
 
-// Builds the workspace image: DevImage records, tile prefix, row prefix.
-int build_tables(int32_t n, const mimo_image_desc *desc, const Tiling &tiling, BuiltTables &out) {
-    out.bytes.assign(ws_total_bytes(n), 0);
-    DevImage *img = reinterpret_cast<DevImage *>(out.bytes.data());
-    int64_t *tile_begin = reinterpret_cast<int64_t *>(out.bytes.data() + ws_images_bytes(n));
-    int64_t *row_begin =
-        reinterpret_cast<int64_t *>(out.bytes.data() + ws_images_bytes(n) + ws_prefix_bytes(n));
+// Builds the workspace image -- DevImage records, tile prefix, row prefix --
+// into `bytes` (ws_total_bytes(n) bytes, zeroed by the caller).
+int build_tables_into(int32_t n, const mimo_image_desc *desc, const Tiling &tiling, uint8_t *bytes,
+                      BuiltTables &out) {
+    DevImage *img = reinterpret_cast<DevImage *>(bytes);
+    int64_t *tile_begin = reinterpret_cast<int64_t *>(bytes + ws_images_bytes(n));
+    int64_t *row_begin = reinterpret_cast<int64_t *>(bytes + ws_images_bytes(n) + ws_prefix_bytes(n));
     const int R = tiling.rows_per_tile;
     int64_t tiles = 0, rows = 0, band = 0;
     for (int32_t i = 0; i < n; ++i) {
@@ -806,45 +806,136 @@ int build_tables(int32_t n, const mimo_image_desc *desc, const Tiling &tiling, B
     return MIMO_OK;
 }
 
-}  // namespace mimo
+// The same, into out.bytes.
+int build_tables(int32_t n, const mimo_image_desc *desc, const Tiling &tiling, BuiltTables &out) {
+    out.bytes.assign(ws_total_bytes(n), 0);
+    return build_tables_into(n, desc, tiling, out.bytes.data(), out);
+}
 
-using namespace mimo;
+// ------------------------------------------- allocation-free entry point
 
-extern "C" {
+// Device scratch of mimo_preprocess_batch_noalloc: the descriptor tables of
+// one call (at most MIMO_NOALLOC_MAX_IMAGES images), one copy per GPU, held
+// until the process ends.  Host code never uses this name as an address
+// (on the host it is only a stand-in for the symbol): each device's copy is
+// reached through the pointer hipGetSymbolAddress returns for it.
+constexpr size_t kNoAllocScratchBytes = ws_total_bytes_const(MIMO_NOALLOC_MAX_IMAGES);
+static_assert(kNoAllocScratchBytes == MIMO_NOALLOC_SCRATCH_BYTES, "scratch size as declared");
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
 
-int mimo_preprocess_batch(int32_t n, const mimo_image_desc *desc, const uint8_t *src,
-                          int64_t src_capacity, const float *mean255, const float *std255,
-                          int32_t out_dtype, void *rows, void *rows_col, int64_t capacity_rows,
-                          void *workspace, size_t workspace_bytes, void *stream) {
-    clear_error();
+// One piece of a descriptor table carried in a kernel's arguments: the host
+// hands the tables over with no staging buffer of its own.
+constexpr int kChunkWords = 768;  // 3 KB per launch
+struct TableChunk {
+    uint32_t *dst;
+    uint32_t words;  // <= kChunkWords
+    uint32_t pad;
+    uint32_t data[kChunkWords];
+};
+
+__global__ __launch_bounds__(256) void table_fill_kernel(TableChunk c) {
+    for (uint32_t i = threadIdx.x; i < c.words; i += blockDim.x) c.dst[i] = c.data[i];
+}
+
+// The device address of this device's scratch, looked up once per device
+// (with that device current) and kept.
+hipError_t scratch_address(uint8_t **out) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *out = static_cast<uint8_t *>(addr[dev]);
+    return hipSuccess;
+}
+
+// Copies `bytes` (a multiple of 4) from host memory to device memory on
+// `stream` through the arguments of table_fill_kernel launches.
+hipError_t fill_by_arguments(const uint8_t *host, size_t bytes, uint8_t *dev, hipStream_t stream) {
+    TableChunk c;
+    c.pad = 0;
+    for (size_t off = 0; off < bytes; off += 4 * size_t(kChunkWords)) {
+        c.words = uint32_t(std::min<size_t>(kChunkWords, (bytes - off) / 4));
+        c.dst = reinterpret_cast<uint32_t *>(dev + off);
+        std::memcpy(c.data, host + off, 4 * size_t(c.words));
+        hipLaunchKernelGGL(table_fill_kernel, dim3(1), dim3(256), 0, stream, c);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+namespace {
+
+// Where a call's descriptor tables go: the caller's workspace, uploaded
+// through the pinned staging ring, or this device's scratch, filled through
+// kernel arguments.
+enum class TableHome { kWorkspace, kScratch };
+
+int preprocess_common(const char *who, int32_t n, const mimo_image_desc *desc, const uint8_t *src,
+                      int64_t src_capacity, const float *mean255, const float *std255,
+                      int32_t out_dtype, void *rows, void *rows_col, int64_t capacity_rows,
+                      void *workspace, size_t workspace_bytes, void *stream, TableHome home) {
+    const std::string w(who);
     if (n < 0 || (n > 0 && !desc) || !mean255 || !std255)
-        return set_error(MIMO_E_INVALID, "preprocess_batch: bad n or null pointer");
+        return set_error(MIMO_E_INVALID, w + ": bad n or null pointer");
+    if (home == TableHome::kScratch && n > MIMO_NOALLOC_MAX_IMAGES)
+        return set_error(MIMO_E_CAPACITY, w + ": " + std::to_string(n) + " images, above the scratch's " +
+                                              std::to_string(MIMO_NOALLOC_MAX_IMAGES));
     if (out_dtype != MIMO_F32 && out_dtype != MIMO_BF16)
-        return set_error(MIMO_E_INVALID, "preprocess_batch: out_dtype must be MIMO_F32 or MIMO_BF16");
+        return set_error(MIMO_E_INVALID, w + ": out_dtype must be MIMO_F32 or MIMO_BF16");
     if (!rows && !rows_col)
-        return set_error(MIMO_E_INVALID, "preprocess_batch: both outputs are null");
+        return set_error(MIMO_E_INVALID, w + ": both outputs are null");
     if ((rows && !check_ptr_align(rows, 16)) || (rows_col && !check_ptr_align(rows_col, 16)))
-        return set_error(MIMO_E_INVALID, "preprocess_batch: outputs must be 16-byte aligned");
+        return set_error(MIMO_E_INVALID, w + ": outputs must be 16-byte aligned");
     if (n == 0) return MIMO_OK;
     if (!src || !check_ptr_align(src, 4))
-        return set_error(MIMO_E_INVALID, "preprocess_batch: src must be non-null and 4-byte aligned");
-    if (!workspace || !check_ptr_align(workspace, 16))
-        return set_error(MIMO_E_INVALID, "preprocess_batch: workspace must be non-null and 16-byte aligned");
-    if (workspace_bytes < ws_total_bytes(n))
-        return set_error(MIMO_E_CAPACITY, "preprocess_batch: workspace smaller than mimo_workspace_bytes(n)");
+        return set_error(MIMO_E_INVALID, w + ": src must be non-null and 4-byte aligned");
+    if (home == TableHome::kWorkspace) {
+        if (!workspace || !check_ptr_align(workspace, 16))
+            return set_error(MIMO_E_INVALID, w + ": workspace must be non-null and 16-byte aligned");
+        if (workspace_bytes < ws_total_bytes(n))
+            return set_error(MIMO_E_CAPACITY, w + ": workspace smaller than mimo_workspace_bytes(n)");
+    }
     PreArgs a;
     std::memset(&a, 0, sizeof(a));
     for (int c = 0; c < 3; ++c) {
         if (!(std255[c] > 0.0f) || !std::isfinite(std255[c]) || !std::isfinite(mean255[c]))
-            return set_error(MIMO_E_INVALID, "preprocess_batch: std255 must be > 0 and finite");
+            return set_error(MIMO_E_INVALID, w + ": std255 must be > 0 and finite");
         a.inv_std[c] = float(1.0 / double(std255[c]));
         a.mean[c] = mean255[c];
     }
     bool clips = false;
     for (int32_t i = 0; i < n; ++i) clips = clips || (desc[i].status == MIMO_OK && desc[i].frames > 1);
     const Tiling tiling = Tiling::choose(rows != nullptr, rows_col != nullptr, clips);
+    // The tables are built on the host: into a vector for the workspace
+    // path; for the scratch path into a static host buffer (held under its
+    // lock until the launches that carry it have been issued), so that the
+    // call allocates nothing.
+    static std::mutex host_mu;
+    static uint8_t host_tables[kNoAllocScratchBytes];
+    std::unique_lock<std::mutex> host_lock(host_mu, std::defer_lock);
     BuiltTables t;
-    int st = build_tables(n, desc, tiling, t);
+    const uint8_t *table = nullptr;
+    int st;
+    if (home == TableHome::kScratch) {
+        host_lock.lock();
+        std::memset(host_tables, 0, ws_total_bytes(n));
+        st = build_tables_into(n, desc, tiling, host_tables, t);
+        table = host_tables;
+    } else {
+        st = build_tables(n, desc, tiling, t);
+        table = t.bytes.data();
+    }
     if (st != MIMO_OK) return st;
     int64_t src_needed = 0;
     for (int32_t i = 0; i < n; ++i)
@@ -853,19 +944,27 @@ int mimo_preprocess_batch(int32_t n, const mimo_image_desc *desc, const uint8_t 
                                                            int64_t(desc[i].frames) * desc[i].src_h *
                                                                desc[i].src_w * desc[i].channels);
     if (src_capacity < ((src_needed + 15) & ~int64_t(15)))
-        return set_error(MIMO_E_CAPACITY, "preprocess_batch: src_capacity below the packed size rounded up to 16");
+        return set_error(MIMO_E_CAPACITY, w + ": src_capacity below the packed size rounded up to 16");
     if (t.total_rows > capacity_rows)
-        return set_error(MIMO_E_CAPACITY, "preprocess_batch: capacity_rows " + std::to_string(capacity_rows) +
+        return set_error(MIMO_E_CAPACITY, w + ": capacity_rows " + std::to_string(capacity_rows) +
                                               " < " + std::to_string(t.total_rows) + " rows");
     if (t.total_tiles == 0) return MIMO_OK;
     if (t.total_tiles * tiling.passes > 0x7FFFFFFFll)
-        return set_error(MIMO_E_TOO_LARGE, "preprocess_batch: more than 2^31-1 tiles");
+        return set_error(MIMO_E_TOO_LARGE, w + ": more than 2^31-1 tiles");
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = upload_table(t.bytes.data(), t.bytes.size(), workspace, s);
-    if (e != hipSuccess) return hip_error(e, "preprocess_batch: table upload");
+    uint8_t *ws = nullptr;
+    hipError_t e;
+    if (home == TableHome::kScratch) {
+        e = scratch_address(&ws);
+        if (e != hipSuccess) return hip_error(e, (w + ": scratch address").c_str());
+        e = fill_by_arguments(table, ws_total_bytes(n), ws, s);
+    } else {
+        ws = static_cast<uint8_t *>(workspace);
+        e = upload_table(table, ws_total_bytes(n), ws, s);
+    }
+    if (e != hipSuccess) return hip_error(e, (w + ": table upload").c_str());
 
-    uint8_t *ws = static_cast<uint8_t *>(workspace);
     a.src = src;
     a.src_end = src_capacity;
     a.images = reinterpret_cast<const DevImage *>(ws);
@@ -893,9 +992,36 @@ int mimo_preprocess_batch(int32_t n, const mimo_image_desc *desc, const uint8_t 
                 hipLaunchKernelGGL((preprocess_kernel<uint16_t, false>), grid, block, lds, s, a);
         }
     });
-    if (e != hipSuccess) return hip_error(e, "preprocess_batch: kernel launch");
+    if (e != hipSuccess) return hip_error(e, (w + ": kernel launch").c_str());
     g_dispatches.fetch_add(1);
     return MIMO_OK;
+}
+
+}  // namespace
+}  // namespace mimo
+
+using namespace mimo;
+
+extern "C" {
+
+int mimo_preprocess_batch(int32_t n, const mimo_image_desc *desc, const uint8_t *src,
+                          int64_t src_capacity, const float *mean255, const float *std255,
+                          int32_t out_dtype, void *rows, void *rows_col, int64_t capacity_rows,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+    clear_error();
+    return preprocess_common("preprocess_batch", n, desc, src, src_capacity, mean255, std255, out_dtype,
+                             rows, rows_col, capacity_rows, workspace, workspace_bytes, stream,
+                             TableHome::kWorkspace);
+}
+
+int mimo_preprocess_batch_noalloc(int32_t n, const mimo_image_desc *desc, const uint8_t *src,
+                                  int64_t src_capacity, const float *mean255, const float *std255,
+                                  int32_t out_dtype, void *rows, void *rows_col, int64_t capacity_rows,
+                                  void *stream) {
+    clear_error();
+    return preprocess_common("preprocess_batch_noalloc", n, desc, src, src_capacity, mean255, std255,
+                             out_dtype, rows, rows_col, capacity_rows, nullptr, 0, stream,
+                             TableHome::kScratch);
 }
 
 int mimo_column_permute(int32_t n, const mimo_image_desc *desc, const void *rows_in,
