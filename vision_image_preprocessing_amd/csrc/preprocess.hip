@@ -49,6 +49,7 @@
 #include "device_util.h"
 #include "internal.h"
 #include "runtime.h"
+#include "tables.h"
 
 namespace mimo {
 
@@ -56,12 +57,22 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 // LDS budget for one tile's source band, in dwords (one dword per pixel).
 constexpr int kBandBudgetDwords = 12288;  // 48 KB
+// Most output columns of one tile (three merge units side by side): the size
+// of each of the three x-tap arrays that follow the band in LDS.
+constexpr int kMaxTileCols = 3 * kUnitPx;
+static_assert(MIMO_ROWS_PER_TILE <= 3 * kRowsPerUnit && MIMO_ROWS_PER_TILE_CLIPS <= 3 * kRowsPerUnit &&
+                  MIMO_ROWS_PER_TILE_DUAL <= kRowsPerUnit,
+              "a tile spans at most three merge units of output columns");
 // Buffer resource word 3 for raw (untyped) buffer loads on gfx9-family parts.
 constexpr int kBufferWord3 = 0x00020000;
 
+// Batches of at most this many images carry their descriptor tables in the
+// kernel arguments (296 bytes), so a call makes no table upload.
+constexpr int kInlineImages = 4;
+
 struct PreArgs {
     const uint8_t *src;
-    const DevImage *images;
+    const DevImage *images;     // null: the tables are inline (below)
     const int64_t *tile_begin;  // [n + 1]
     void *rows;                 // merge-block order, nullable
     void *rows_col;             // column order, nullable
@@ -73,7 +84,43 @@ struct PreArgs {
     int32_t xcd_order;          // map workgroups to XCD-contiguous tile runs
     float inv_std[3];           // 1 / std255, rounded once
     float mean[3];              // mean255
+    DevImage inl_images[kInlineImages];
+    int64_t inl_tile_begin[kInlineImages + 1];
 };
+
+// The image that holds `tile` (largest i with tile_begin[i] <= tile), from
+// the inline tables (kInline) or the workspace; wave-uniform.
+template <bool kInline>
+__device__ __forceinline__ int tile_image(const PreArgs &a, int64_t tile) {
+    if (!kInline) return find_segment(a.tile_begin, a.n, tile);
+    int img = 0;
+#pragma unroll
+    for (int i = 1; i < kInlineImages; ++i)
+        if (i < a.n && a.inl_tile_begin[i] <= tile) img = i;
+    return img;
+}
+
+// Entry `img` of the tables.  The inline arrays are read with constant
+// indices only (scalar loads from the kernel arguments).
+template <bool kInline>
+__device__ __forceinline__ DevImage image_at(const PreArgs &a, int img) {
+    if (!kInline) return a.images[img];
+    DevImage d = a.inl_images[0];
+#pragma unroll
+    for (int i = 1; i < kInlineImages; ++i)
+        if (img == i) d = a.inl_images[i];
+    return d;
+}
+
+template <bool kInline>
+__device__ __forceinline__ int64_t tile_begin_at(const PreArgs &a, int img) {
+    if (!kInline) return a.tile_begin[img];
+    int64_t b = a.inl_tile_begin[0];
+#pragma unroll
+    for (int i = 1; i <= kInlineImages; ++i)
+        if (img == i) b = a.inl_tile_begin[i];
+    return b;
+}
 
 struct PermArgs {
     const DevImage *images;
@@ -252,9 +299,11 @@ __device__ __forceinline__ void identity_patch(const PreArgs &a, const DevImage 
 struct BandPixels {  // staged in LDS, edge already replicated
     const uint32_t *band;
     int pitch, r_lo, c_lo;
-    __device__ __forceinline__ uint32_t at(int y, int x) const {
-        return band[(y - r_lo) * pitch + (x - c_lo)];
-    }
+    // the x taps of the tile's output columns (from column ox_first), made
+    // once per tile: first tap relative to c_lo, and its two weights
+    const int32_t *xi;
+    const float *xl0, *xl1;
+    int ox_first;
 };
 
 struct GlobalPixels {  // straight from memory, clamped
@@ -294,6 +343,42 @@ __device__ __forceinline__ void bilinear_patch(const Pixels &px, const DevImage 
         for (int c = 0; c < 3; ++c) {
             const float top = __builtin_fmaf(tx.l0, chan(p00, c), tx.l1 * chan(p01, c));
             const float bot = __builtin_fmaf(tx.l0, chan(p10, c), tx.l1 * chan(p11, c));
+            const float val = __builtin_fmaf(ty.l0, top, ty.l1 * bot);
+            v[c][j] = (val - a.mean[c]) * a.inv_std[c];
+        }
+    }
+    OutT *dst = row_dest(out, d, t, br, bc, mh, mw, column);
+#pragma unroll
+    for (int c = 0; c < 3; ++c) store_frames<TT>(dst, c, v[c]);
+}
+
+// The same for a tile staged in LDS: the row tap per lane, the column taps
+// from the tile's table (three 16-byte LDS reads for the lane's 4 pixels),
+// the second taps always one row / column on (the band repeats the image's
+// last row and column).  Bitwise the same values as bilinear_patch.
+template <typename OutT, int TT>
+__device__ __forceinline__ void bilinear_patch_band(const BandPixels &px, const DevImage &d, const PreArgs &a,
+                                                    int t, int br, int bc, int mh, int mw, OutT *out,
+                                                    bool column) {
+    const int lane = threadIdx.x & 63;
+    const int py = lane >> 2, q = lane & 3;
+    const int oy = (br * kMerge + mh) * kPatch + py;
+    const int xc = (bc * kMerge + mw) * kPatch + 4 * q - px.ox_first;
+    const Tap ty = make_tap(d.scale_y, oy, d.src_h);
+    const uint32_t *r0 = px.band + (ty.i0 - px.r_lo) * px.pitch;
+    const uint32_t *r1 = r0 + px.pitch;
+    const i32x4 xi = *reinterpret_cast<const i32x4 *>(px.xi + xc);
+    const f32x4 l0 = *reinterpret_cast<const f32x4 *>(px.xl0 + xc);
+    const f32x4 l1 = *reinterpret_cast<const f32x4 *>(px.xl1 + xc);
+    float v[3][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t p00 = r0[xi[j]], p01 = r0[xi[j] + 1];
+        const uint32_t p10 = r1[xi[j]], p11 = r1[xi[j] + 1];
+#pragma unroll
+        for (int c = 0; c < 3; ++c) {
+            const float top = __builtin_fmaf(l0[j], chan(p00, c), l1[j] * chan(p01, c));
+            const float bot = __builtin_fmaf(l0[j], chan(p10, c), l1[j] * chan(p11, c));
             const float val = __builtin_fmaf(ty.l0, top, ty.l1 * bot);
             v[c][j] = (val - a.mean[c]) * a.inv_std[c];
         }
@@ -460,6 +545,32 @@ __device__ __forceinline__ void replicate_right_edge(uint32_t *band, const DevIm
         band[r * b.pitch + xl + 1] = band[r * b.pitch + xl];
 }
 
+// The x taps of the tile's output columns into the table that follows the
+// band in LDS (the band's first column c_lo as origin); made before the
+// band's barrier.
+__device__ __forceinline__ BandPixels band_pixels(uint32_t *band, const PreArgs &a, const DevImage &d,
+                                                  const TileGeom &g, const Band &b) {
+    BandPixels px;
+    px.band = band;
+    px.pitch = b.pitch;
+    px.r_lo = b.r_lo;
+    px.c_lo = b.c_lo;
+    int32_t *xi = reinterpret_cast<int32_t *>(band + a.band_capacity);
+    float *xl0 = reinterpret_cast<float *>(xi + kMaxTileCols);
+    float *xl1 = xl0 + kMaxTileCols;
+    for (int i = threadIdx.x; i <= g.ox_last - g.ox_first; i += blockDim.x) {
+        const Tap tx = make_tap(d.scale_x, g.ox_first + i, d.src_w);
+        xi[i] = tx.i0 - b.c_lo;
+        xl0[i] = tx.l0;
+        xl1[i] = tx.l1;
+    }
+    px.xi = xi;
+    px.xl0 = xl0;
+    px.xl1 = xl1;
+    px.ox_first = g.ox_first;
+    return px;
+}
+
 // Resamples one source frame (at frame_offset) of the tile into temporal
 // slot TT of its rows (both slots when TT < 0).
 template <typename OutT, int TT>
@@ -484,16 +595,16 @@ __device__ __forceinline__ void tile_pass(const PreArgs &a, const DevImage &d, c
 
     const Band b = tile_band(a, d, g);
     if (b.fits) {
+        const BandPixels px = band_pixels(band, a, d, g, b);
         stage_band(band, a, d, frame_offset, b.r_lo, b.c_lo, b.rows, b.groups, b.pitch);
         __syncthreads();
         if (b.c_end == d.src_w) {
             replicate_right_edge(band, d, b);
             __syncthreads();
         }
-        const BandPixels px{band, b.pitch, b.r_lo, b.c_lo};
         for (int p = wave; p < g.count; p += waves) {
             const int qr = g.first + p;
-            bilinear_patch<OutT, TT>(px, d, a, g.t, g.br, qr >> 2, (qr >> 1) & 1, qr & 1, out, column);
+            bilinear_patch_band<OutT, TT>(px, d, a, g.t, g.br, qr >> 2, (qr >> 1) & 1, qr & 1, out, column);
         }
     } else {
         const GlobalPixels px{a.src + frame_offset, int64_t(d.src_w) * d.channels, d.channels,
@@ -524,7 +635,7 @@ __device__ __forceinline__ void clip_pair_pass(const PreArgs &a, const DevImage 
     const int gi = threadIdx.x - r0 * b.groups;
     const bool active = r0 < step;
     const int wave = threadIdx.x >> 6, waves = blockDim.x >> 6;
-    const BandPixels px{band, b.pitch, b.r_lo, b.c_lo};
+    const BandPixels px = band_pixels(band, a, d, g, b);
     RowBatch next;
     if (active) {
         stage_rows<C>(band, w0, row_bytes, r0, step, b.rows, last_row, gi, b.pitch);
@@ -537,7 +648,7 @@ __device__ __forceinline__ void clip_pair_pass(const PreArgs &a, const DevImage 
     }
     for (int p = wave; p < g.count; p += waves) {
         const int qr = g.first + p;
-        bilinear_patch<OutT, 0>(px, d, a, g.t, g.br, qr >> 2, (qr >> 1) & 1, qr & 1, out, column);
+        bilinear_patch_band<OutT, 0>(px, d, a, g.t, g.br, qr >> 2, (qr >> 1) & 1, qr & 1, out, column);
     }
     __syncthreads();  // the first frame's band is no longer read
     if (active) {
@@ -556,29 +667,33 @@ __device__ __forceinline__ void clip_pair_pass(const PreArgs &a, const DevImage 
     }
     for (int p = wave; p < g.count; p += waves) {
         const int qr = g.first + p;
-        bilinear_patch<OutT, 1>(px, d, a, g.t, g.br, qr >> 2, (qr >> 1) & 1, qr & 1, out, column);
+        bilinear_patch_band<OutT, 1>(px, d, a, g.t, g.br, qr >> 2, (qr >> 1) & 1, qr & 1, out, column);
     }
 }
 
 // kClips: the batch holds at least one clip (an item with two or more
 // frames); batches of still images compile without the temporal decode.
-// Built for at least 6 waves per SIMD: a clip tile's band typically holds a
-// CU to 6 workgroups (25 KB for 1280x720 frames at 960x512), and the clip
-// pair path would otherwise take more registers than that occupancy leaves;
-// batches of stills stay within the budget anyway.
-template <typename OutT, bool kClips>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) void preprocess_kernel(PreArgs a) {
+// The clip instance is built for at least 6 waves per SIMD: a clip tile's
+// band typically holds a CU to 6 workgroups (25 KB for 1280x720 frames at
+// 960x512), and its pair path would otherwise take more registers than that
+// occupancy leaves.  The stills instance is built for the full 8, which it
+// reaches with no spill and no added instruction in its resample loop.
+// kInline: the descriptor tables are in the kernel arguments (batches of at
+// most kInlineImages images); a separate instance, since code that could
+// take either source keeps the record in vector registers and spills.
+template <typename OutT, bool kClips, bool kInline>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kClips ? 6 : 8))) void preprocess_kernel(PreArgs a) {
     extern __shared__ uint32_t band[];
-    int64_t tile = a.xcd_order ? xcd_contiguous_tile(blockIdx.x, gridDim.x) : int64_t(blockIdx.x);
+    const int64_t u = a.xcd_order ? xcd_contiguous_tile(blockIdx.x, gridDim.x) : int64_t(blockIdx.x);
     // Pass 0 writes merge-block order (if requested), pass 1 column order:
     // each workgroup writes one output, in that output's own order.
-    const bool second = tile >= a.tiles_per_pass;
-    if (second) tile -= a.tiles_per_pass;
+    const bool second = u >= a.tiles_per_pass;
+    const int64_t tile = second ? u - a.tiles_per_pass : u;
+    const int img = tile_image<kInline>(a, tile);
+    int local = int(tile - tile_begin_at<kInline>(a, img));  // the tile's index within its image and pass
     const bool column = second || a.rows == nullptr;
     OutT *const out = static_cast<OutT *>(column ? a.rows_col : a.rows);
-    const int img = find_segment(a.tile_begin, a.n, tile);
-    const DevImage d = a.images[img];
-    int local = int(tile - a.tile_begin[img]);
+    const DevImage d = image_at<kInline>(a, img);
     TileGeom g;
     // temporal patch t of a clip: tiles are listed slice by slice
     g.t = 0;
@@ -689,45 +804,6 @@ __global__ __launch_bounds__(kThreads) void column_permute_kernel(PermArgs a) {
 
 // ------------------------------------------------------------- host side
 
-// Tiling policy: rows per tile (1, 2 or a multiple of 4) and whether
-// workgroups are mapped to XCD-contiguous runs of tiles.  Small tiles keep
-// the output each workgroup writes small, which the HBM write path favours.
-// With both outputs requested the grid holds two passes of tiles (merge
-// order, then column order), so each output is written as a dense stream.
-#ifndef MIMO_ROWS_PER_TILE
-#define MIMO_ROWS_PER_TILE 4
-#endif
-#ifndef MIMO_ROWS_PER_TILE_DUAL
-#define MIMO_ROWS_PER_TILE_DUAL 1
-#endif
-#ifndef MIMO_ROWS_PER_TILE_CLIPS
-#define MIMO_ROWS_PER_TILE_CLIPS 12
-#endif
-#ifndef MIMO_XCD_ORDER
-#define MIMO_XCD_ORDER 1
-#endif
-struct Tiling {
-    int rows_per_tile = MIMO_ROWS_PER_TILE;
-    int xcd_order = MIMO_XCD_ORDER;
-    int passes = 1;
-    // clips: the batch holds an item with two or more frames.  A clip tile
-    // stages and resamples its two frames one after the other; three merge
-    // units per tile amortise the two band loads and barriers better than
-    // one (measured on 64-frame 1280x720 clips, bf16: 0.62 vs 0.70 ms).
-    static Tiling choose(bool merge, bool column, bool clips) {
-        Tiling t;
-        if (clips) t.rows_per_tile = MIMO_ROWS_PER_TILE_CLIPS;
-        if (merge && column) {
-            t.passes = 2;
-            t.rows_per_tile = std::min(MIMO_ROWS_PER_TILE_DUAL, kRowsPerUnit);
-        } else if (column) {
-            t.rows_per_tile = std::min(t.rows_per_tile, kRowsPerUnit);
-        }
-        return t;
-    }
-    int threads() const { return 64 * std::min(rows_per_tile, kRowsPerUnit); }
-};
-
 // Conservative size of the LDS band one tile of R rows needs, in dwords.
 int64_t band_estimate(const DevImage &d, int R) {
     const int out_rows = R >= kRowsPerUnit ? kUnitPx : kPatch;
@@ -737,14 +813,6 @@ int64_t band_estimate(const DevImage &d, int R) {
     const double cols = std::min<double>(d.src_w, std::ceil((out_cols - 1.0) * d.scale_x) + 4.0);
     return int64_t(rows) * (4 * ((int64_t(cols) + 3) / 4 + 1));
 }
-
-struct BuiltTables {
-    std::vector<uint8_t> bytes;  // workspace image (build_tables)
-    int64_t total_tiles = 0;
-    int64_t total_rows = 0;
-    int32_t band_capacity = 0;  // dwords
-    bool clips = false;         // some item has two or more frames
-};
 
 // Builds the workspace image -- DevImage records, tile prefix, row prefix --
 // into `bytes` (ws_total_bytes(n) bytes, zeroed by the caller).
@@ -802,7 +870,7 @@ int build_tables_into(int32_t n, const mimo_image_desc *desc, const Tiling &tili
     row_begin[n] = rows;
     out.total_tiles = tiles;
     out.total_rows = rows;
-    out.band_capacity = int32_t(std::max<int64_t>(band, 4));
+    out.band_capacity = int32_t((std::max<int64_t>(band, 4) + 3) & ~int64_t(3));  // the x-tap table follows, 16-byte aligned
     return MIMO_OK;
 }
 
@@ -953,22 +1021,30 @@ int preprocess_common(const char *who, int32_t n, const mimo_image_desc *desc, c
         return set_error(MIMO_E_TOO_LARGE, w + ": more than 2^31-1 tiles");
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    uint8_t *ws = nullptr;
     hipError_t e;
-    if (home == TableHome::kScratch) {
-        e = scratch_address(&ws);
-        if (e != hipSuccess) return hip_error(e, (w + ": scratch address").c_str());
-        e = fill_by_arguments(table, ws_total_bytes(n), ws, s);
+    if (n <= kInlineImages) {
+        // small batch: the tables travel in the kernel arguments
+        std::memcpy(a.inl_images, table, sizeof(DevImage) * size_t(n));
+        std::memcpy(a.inl_tile_begin, table + ws_images_bytes(n), sizeof(int64_t) * (size_t(n) + 1));
+        a.images = nullptr;
+        a.tile_begin = nullptr;
     } else {
-        ws = static_cast<uint8_t *>(workspace);
-        e = upload_table(table, ws_total_bytes(n), ws, s);
+        uint8_t *ws = nullptr;
+        if (home == TableHome::kScratch) {
+            e = scratch_address(&ws);
+            if (e != hipSuccess) return hip_error(e, (w + ": scratch address").c_str());
+            e = fill_by_arguments(table, ws_total_bytes(n), ws, s);
+        } else {
+            ws = static_cast<uint8_t *>(workspace);
+            e = upload_table(table, ws_total_bytes(n), ws, s);
+        }
+        if (e != hipSuccess) return hip_error(e, (w + ": table upload").c_str());
+        a.images = reinterpret_cast<const DevImage *>(ws);
+        a.tile_begin = reinterpret_cast<const int64_t *>(ws + ws_images_bytes(n));
     }
-    if (e != hipSuccess) return hip_error(e, (w + ": table upload").c_str());
 
     a.src = src;
     a.src_end = src_capacity;
-    a.images = reinterpret_cast<const DevImage *>(ws);
-    a.tile_begin = reinterpret_cast<const int64_t *>(ws + ws_images_bytes(n));
     a.rows = rows;
     a.rows_col = rows_col;
     a.n = n;
@@ -976,21 +1052,30 @@ int preprocess_common(const char *who, int32_t n, const mimo_image_desc *desc, c
     a.rows_per_tile = tiling.rows_per_tile;
     a.xcd_order = tiling.xcd_order;
     a.tiles_per_pass = rows ? t.total_tiles : int64_t(1) << 62;
-    const size_t lds = size_t(t.band_capacity) * 4;
+    const size_t lds = (size_t(t.band_capacity) + 3 * kMaxTileCols) * 4;  // band, then the x-tap table
     const dim3 grid{unsigned(t.total_tiles * tiling.passes), 1, 1},
         block{unsigned(tiling.threads()), 1, 1};
+    const bool inl = n <= kInlineImages;
     e = timed_launch(s, [&] {
+#define MIMO_LAUNCH(T, C)                                                                   \
+    do {                                                                                    \
+        if (inl)                                                                            \
+            hipLaunchKernelGGL((preprocess_kernel<T, C, true>), grid, block, lds, s, a);    \
+        else                                                                                \
+            hipLaunchKernelGGL((preprocess_kernel<T, C, false>), grid, block, lds, s, a);   \
+    } while (0)
         if (out_dtype == MIMO_F32) {
             if (t.clips)
-                hipLaunchKernelGGL((preprocess_kernel<float, true>), grid, block, lds, s, a);
+                MIMO_LAUNCH(float, true);
             else
-                hipLaunchKernelGGL((preprocess_kernel<float, false>), grid, block, lds, s, a);
+                MIMO_LAUNCH(float, false);
         } else {
             if (t.clips)
-                hipLaunchKernelGGL((preprocess_kernel<uint16_t, true>), grid, block, lds, s, a);
+                MIMO_LAUNCH(uint16_t, true);
             else
-                hipLaunchKernelGGL((preprocess_kernel<uint16_t, false>), grid, block, lds, s, a);
+                MIMO_LAUNCH(uint16_t, false);
         }
+#undef MIMO_LAUNCH
     });
     if (e != hipSuccess) return hip_error(e, (w + ": kernel launch").c_str());
     g_dispatches.fetch_add(1);
