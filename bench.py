@@ -231,6 +231,21 @@ def patch_embed_rates(V, batch, plan, src, ws, reps: int, embed_dim: int = 1280)
         ms = time_launches(V, lambda: V.patch_embed(rows, wt, bias, out=out), reps, stream)
         tflops = 2.0 * plan.total_rows * embed_dim * k / (ms * 1e-3) / 1e12
         res[name] = {"k": k, "ms": ms, "TFLOP/s": tflops, "frac": tflops / MFMA_BF16_PEAK_TFLOPS}
+    if not batch.is_media:
+        # pixels -> embeddings, stills: the pair (bf16 rows, then the folded
+        # GEMM over them) against the fused kernel, which never writes the rows
+        ms_rows = time_launches(V, lambda: V.preprocess(src, plan, mean=batch.mean, std=batch.std,
+                                                         out_dtype="bf16", rows=rows, workspace=ws),
+                                reps, stream)
+        wp, bp = V.prepare_pixel_embed_weights(w, bias, batch.mean, batch.std)
+        ms_fused = time_launches(V, lambda: V.embed_pixels(src, plan, wp, bp, out=out, workspace=ws),
+                                 reps, stream)
+        tflops = 2.0 * plan.total_rows * embed_dim * 768 / (ms_fused * 1e-3) / 1e12
+        pair = ms_rows + res["folded"]["ms"]
+        res["pixels_to_embed"] = {"kernel": "pixel_embed_kernel", "rows_then_folded_gemm_ms": pair,
+                                  "rows_kernel_ms": ms_rows, "fused_ms": ms_fused,
+                                  "fused_TFLOP/s": tflops, "fused_frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+                                  "speedup_vs_pair": pair / ms_fused}
     # the same product through torch's bf16 matmul (vendor GEMM), for context
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.matmul(rows, w.t(), out=out)

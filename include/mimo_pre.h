@@ -436,6 +436,65 @@ int mimo_patch_embed(int64_t n_rows, const void *rows, int32_t embed_dim, const 
                      int32_t folded, const float *bias, int32_t out_dtype, void *out,
                      void *stream);
 
+/* ------------------------------------------------------------------------
+ * The pixel path and the patch embedding in one kernel, for still images:
+ * NeMo Automodel "mimo_v2_flash.vision", MiMoVisionPatchEmbed, applied to the
+ * rows of NeMo Automodel "mimo_v2_flash.processing", MimoV2ImageProcessor,
+ * without writing the rows.  A still image's two frames are equal, so the
+ * weight's two temporal halves are summed (K = 768); the standardisation is
+ * affine, so it moves into the weight and bias:
+ *   sum_k a_k W'_k = sum_k x_k (s_c W'_k) - sum_k mean255[c] (s_c W'_k),
+ * a = (x - mean255[c]) * s_c, s_c = 1 / std255[c], x the resized 0-255 value.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Prepares the weight and bias for mimo_pixel_embed (one kernel launch):
+ *   w_pixels[e][(py*16 + px)*3 + c] = bf16(s_c * (W[e][c][0][py][px] + W[e][c][1][py][px]))
+ *     (sum and product in float32, s_c = float32(1 / std255[c]), one rounding
+ *     to nearest even) -- the (py, px, c) order of the source bytes;
+ *   bias_pixels[e] = bias[e] - sum_k mean255[c(k)] * w_pixels[e][k]
+ *     (float64, rounded once to float32; bias NULL counts as zeros).
+ *   w           device bf16 [embed_dim][1536] (the Conv3d weight flattened as
+ *               (c, tt, py, px)), 16-byte aligned.
+ *   bias        device float32 [embed_dim], or NULL.
+ *   mean255, std255  host float[3], 0-255 units (mimo_stats255); std255 > 0.
+ *   w_pixels    device bf16 [embed_dim][768], 16-byte aligned, not w.
+ *   bias_pixels device float32 [embed_dim].
+ * Returns MIMO_OK, MIMO_E_INVALID or MIMO_E_HIP.
+ */
+int mimo_prepare_pixel_embed(int32_t embed_dim, const void *w, const float *bias, const float *mean255,
+                             const float *std255, void *w_pixels, float *bias_pixels, void *stream);
+
+/*
+ * Patch embeddings of a planned batch of still images straight from their
+ * packed uint8 sources: out[r][e] = bias_pixels[e] + sum_k bf16(x_r[k]) *
+ * w_pixels[e][k] over the 768 resized 0-255 values x_r of row r's patch in
+ * (py, px, c) order (RGBA flattened onto white, the bilinear resize of
+ * mimo_preprocess_batch in float32, then one rounding to bf16 -- exact for an
+ * image whose smart_resize target is its own size), float32 accumulation on
+ * the matrix cores.  Rows in merge-block order, as mimo_preprocess_batch
+ * lists them.  One kernel launch after one table upload; no pixel row is
+ * written.
+ *   n, desc      host plan (mimo_plan_geometry); items must be still images
+ *                (frames = 1), else MIMO_E_UNSUPPORTED.
+ *   src, src_capacity  as for mimo_preprocess_batch.
+ *   embed_dim    E: a multiple of 256 in [256, 65536].
+ *   w_pixels, bias_pixels  from mimo_prepare_pixel_embed (16-byte aligned).
+ *   out          device [capacity_rows][E] of out_dtype (MIMO_F32 or
+ *                MIMO_BF16, rounded to nearest even), 16-byte aligned.
+ *   workspace    device, >= mimo_workspace_bytes(n), 16-byte aligned.
+ * A batch whose every item is RGB and not resampled runs the fast producer
+ * (source bytes straight into the matrix-core tiles); any other batch runs
+ * a producer that evaluates each value from global memory (correct, slower).
+ * Returns MIMO_OK, MIMO_E_INVALID, MIMO_E_UNSUPPORTED, MIMO_E_CAPACITY,
+ * MIMO_E_TOO_LARGE (more than 2^31 - 1 tiles, or one tile's images spanning
+ * more than 2^31 source bytes) or MIMO_E_HIP.
+ */
+int mimo_pixel_embed(int32_t n, const mimo_image_desc *desc, const uint8_t *src, int64_t src_capacity,
+                     int32_t embed_dim, const void *w_pixels, const float *bias_pixels, int32_t out_dtype,
+                     void *out, int64_t capacity_rows, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
 /*
  * Instrumentation.  When start and stop are non-null hipEvent_t handles
  * (passed as void*), every later kernel launch that the library makes on the

@@ -20,11 +20,12 @@ from ._abi import (  # noqa: F401
     hf_smart_resize,
     hf_workspace_bytes, last_error, load, make_params, patch_embed, plan_frames, plan_geometry,
     plan_hf,
+    pixel_embed, prepare_pixel_embed, preprocess_batch_noalloc,
     preprocess_hf_batch, preprocess_batch, rope_inv_freq, rotary_tables, sample_frames,
     set_launch_events, smart_nframes, smart_resize, status_string, video_max_pixels,
     window_index, workspace_bytes,
 )
 from .processor import (  # noqa: F401
-    BatchPlan, ImageProcessor, VideoProcessor, plan_batch, plan_batch_hf, plan_media, preprocess, preprocess_hf,
-    stats255, vit_tables,
+    BatchPlan, ImageProcessor, VideoProcessor, embed_pixels, plan_batch, plan_batch_hf, plan_media,
+    prepare_pixel_embed_weights, preprocess, preprocess_hf, stats255, vit_tables,
 )

@@ -102,6 +102,8 @@ SIGNATURES = {
     "mimo_preprocess_hf_batch": ([_I32, _P, _P, _I64, _P, _P, _I32, _P, _P, _I64, _P, _SZ, _P],
                                  ctypes.c_int),
     "mimo_patch_embed": ([_I64, _P, _I32, _P, _I32, _P, _I32, _P, _P], ctypes.c_int),
+    "mimo_prepare_pixel_embed": ([_I32, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "mimo_pixel_embed": ([_I32, _P, _P, _I64, _I32, _P, _P, _I32, _P, _I64, _P, _SZ, _P], ctypes.c_int),
 }
 
 _lock = threading.Lock()
@@ -309,45 +311,71 @@ def _dtype_code(t) -> int:
     raise MimoError(MIMO_E_INVALID, f"output dtype {t.dtype} is not float32 or bfloat16")
 
 
-def _require(ok: bool, what: str):
+def _require(ok: bool, what):
+    """Raises MimoError(MIMO_E_INVALID) unless ok; `what` is the message or a
+    callable that makes it (formatted only on failure)."""
     if not ok:
-        raise MimoError(MIMO_E_INVALID, what)
+        raise MimoError(MIMO_E_INVALID, what() if callable(what) else what)
 
 
 def _check_matrix(t, what: str, width: int, dtypes):
     """t must be a contiguous 2-D tensor [capacity, width] of one of dtypes."""
-    _require(t.dim() == 2 and t.shape[1] == width and t.is_contiguous() and t.dtype in dtypes,
-             f"{what}: need a contiguous [capacity, {width}] tensor of "
-             f"{' or '.join(str(d) for d in dtypes)}, got {tuple(t.shape)} {t.dtype}"
-             + ("" if t.is_contiguous() else " (not contiguous)"))
+    if t.dim() == 2 and t.shape[1] == width and t.dtype in dtypes and t.is_contiguous():
+        return
+    raise MimoError(MIMO_E_INVALID,
+                    f"{what}: need a contiguous [capacity, {width}] tensor of "
+                    f"{' or '.join(str(d) for d in dtypes)}, got {tuple(t.shape)} {t.dtype}"
+                    + ("" if t.is_contiguous() else " (not contiguous)"))
 
 
 def _check_bytes(t, what: str):
     """t must be a contiguous uint8 tensor (its numel is its size in bytes)."""
     import torch
-    _require(t.dtype == torch.uint8 and t.is_contiguous() and t.dim() == 1,
-             f"{what}: need a contiguous 1-D uint8 tensor, got {tuple(t.shape)} {t.dtype}")
+    if t.dtype == torch.uint8 and t.dim() == 1 and t.is_contiguous():
+        return
+    raise MimoError(MIMO_E_INVALID, f"{what}: need a contiguous 1-D uint8 tensor, got {tuple(t.shape)} {t.dtype}")
 
 
 def _check_device(tensors, what: str):
     """Every tensor lives on one GPU (checked after shapes and dtypes, so
     mis-shaped host tensors are reported as such)."""
-    devs = {(t.device.type, t.device.index) for t in tensors if t is not None}
-    _require(len(devs) == 1 and next(iter(devs))[0] == "cuda",
-             f"{what}: every tensor must be on one GPU, got {sorted(map(str, devs))}")
+    dev = None
+    for t in tensors:
+        if t is None:
+            continue
+        d = t.device
+        if d.type != "cuda" or (dev is not None and d != dev):
+            devs = sorted({str(x.device) for x in tensors if x is not None})
+            raise MimoError(MIMO_E_INVALID, f"{what}: every tensor must be on one GPU, got {devs}")
+        dev = d
+
+
+_ROW_DTYPES = None  # (torch.float32, torch.bfloat16), set on first use
+
+
+def _row_dtypes():
+    global _ROW_DTYPES
+    if _ROW_DTYPES is None:
+        import torch
+        _ROW_DTYPES = (torch.float32, torch.bfloat16)
+    return _ROW_DTYPES
 
 
 def _out_tensors(rows, rows_col, what: str):
     """Checks the pixel-path outputs: one or two contiguous [capacity, 1536]
     tensors of one dtype (float32 or bfloat16); returns (dtype code,
     capacity)."""
-    import torch
-    outs = [t for t in (rows, rows_col) if t is not None]
-    _require(bool(outs), f"{what}: both outputs are None")
-    for t in outs:
-        _check_matrix(t, what + " output", ROW_LEN, (torch.float32, torch.bfloat16))
-    _require(len({t.dtype for t in outs}) == 1, f"{what}: the two outputs differ in dtype")
-    return _dtype_code(outs[0]), min(t.shape[0] for t in outs)
+    dts = _row_dtypes()
+    if rows is None and rows_col is None:
+        raise MimoError(MIMO_E_INVALID, f"{what}: both outputs are None")
+    first = rows if rows is not None else rows_col
+    _check_matrix(first, what + " output", ROW_LEN, dts)
+    cap = first.shape[0]
+    if rows is not None and rows_col is not None:
+        _check_matrix(rows_col, what + " output", ROW_LEN, dts)
+        _require(rows_col.dtype == first.dtype, lambda: f"{what}: the two outputs differ in dtype")
+        cap = min(cap, rows_col.shape[0])
+    return (MIMO_F32 if first.dtype == dts[0] else MIMO_BF16), cap
 
 
 def preprocess_batch(desc: np.ndarray, src, mean255, std255, rows=None, rows_col=None,
@@ -576,3 +604,53 @@ def preprocess_hf_batch(desc: np.ndarray, src, mean01, std01, rows=None, rows_co
         rows_col.data_ptr() if rows_col is not None else None,
         cap, workspace.data_ptr(), workspace.numel(), _stream_handle(stream, out.device))
     _check(code, "preprocess_hf_batch")
+
+
+def prepare_pixel_embed(w, mean255, std255, bias=None, w_pixels=None, bias_pixels=None, stream=None):
+    """mimo_prepare_pixel_embed: the patch-embedding weight bf16 [E, 1536]
+    (and float32 bias [E], or None) -> (w_pixels bf16 [E, 768] in the
+    source's (py, px, c) order with the two frames' halves summed and the
+    standardisation folded in, bias_pixels float32 [E]) for mimo_pixel_embed
+    with these statistics (0-255 units)."""
+    import torch
+    _check_matrix(w, "prepare_pixel_embed: w", ROW_LEN, (torch.bfloat16,))
+    e = w.shape[0]
+    if bias is not None:
+        _require(bias.dim() == 1 and bias.shape[0] == e and bias.dtype == torch.float32
+                 and bias.is_contiguous(), f"prepare_pixel_embed: bias must be contiguous float32 [{e}]")
+    if w_pixels is None:
+        w_pixels = torch.empty((e, ROW_LEN // 2), dtype=torch.bfloat16, device=w.device)
+    if bias_pixels is None:
+        bias_pixels = torch.empty(e, dtype=torch.float32, device=w.device)
+    _check_matrix(w_pixels, "prepare_pixel_embed: w_pixels", ROW_LEN // 2, (torch.bfloat16,))
+    _require(w_pixels.shape[0] == e and bias_pixels.dim() == 1 and bias_pixels.shape[0] == e
+             and bias_pixels.dtype == torch.float32 and bias_pixels.is_contiguous(),
+             "prepare_pixel_embed: outputs must be bf16 [E, 768] and float32 [E]")
+    _check_device([w, bias, w_pixels, bias_pixels], "prepare_pixel_embed")
+    m = (ctypes.c_float * 3)(*[float(v) for v in mean255])
+    s = (ctypes.c_float * 3)(*[float(v) for v in std255])
+    _check(load().mimo_prepare_pixel_embed(e, w.data_ptr(), bias.data_ptr() if bias is not None else None,
+                                           m, s, w_pixels.data_ptr(), bias_pixels.data_ptr(),
+                                           _stream_handle(stream, w.device)), "prepare_pixel_embed")
+    return w_pixels, bias_pixels
+
+
+def pixel_embed(desc: np.ndarray, src, w_pixels, bias_pixels, out, workspace, stream=None):
+    """mimo_pixel_embed: the still images of a plan straight to their patch
+    embeddings out [rows, E] (merge-block row order), from the packed uint8
+    sources, with weights from prepare_pixel_embed."""
+    import torch
+    desc = np.ascontiguousarray(desc, dtype=IMAGE_DESC_DTYPE)
+    _check_bytes(src, "pixel_embed: src")
+    _check_matrix(w_pixels, "pixel_embed: w_pixels", ROW_LEN // 2, (torch.bfloat16,))
+    e = w_pixels.shape[0]
+    _require(bias_pixels.dim() == 1 and bias_pixels.shape[0] == e and bias_pixels.dtype == torch.float32
+             and bias_pixels.is_contiguous(), f"pixel_embed: bias_pixels must be contiguous float32 [{e}]")
+    _check_matrix(out, "pixel_embed: out", e, (torch.float32, torch.bfloat16))
+    _check_bytes(workspace, "pixel_embed: workspace")
+    _check_device([src, w_pixels, bias_pixels, out, workspace], "pixel_embed")
+    code = load().mimo_pixel_embed(desc.shape[0], desc.ctypes.data, src.data_ptr(), src.numel(), e,
+                                   w_pixels.data_ptr(), bias_pixels.data_ptr(), _dtype_code(out),
+                                   out.data_ptr(), out.shape[0], workspace.data_ptr(), workspace.numel(),
+                                   _stream_handle(stream, out.device))
+    _check(code, "pixel_embed")

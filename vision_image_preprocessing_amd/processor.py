@@ -371,3 +371,32 @@ def preprocess_hf(src_dev, plan: BatchPlan, mean=IMAGENET_MEAN, std=IMAGENET_STD
         "pixel_values_col": rows_col if column_order else None,
         "image_grid_thw": torch.from_numpy(plan.image_grid_thw),
     }
+
+
+def prepare_pixel_embed_weights(w, bias=None, mean=IMAGENET_MEAN, std=IMAGENET_STD, stream=None):
+    """The patch-embedding weight (bf16 [E, 1536], Conv3d (c, tt, py, px)
+    order) and bias, prepared for embed_pixels with these statistics:
+    (w_pixels bf16 [E, 768], bias_pixels float32 [E])."""
+    m255, s255 = stats255(mean, std)
+    return _abi.prepare_pixel_embed(w, m255, s255, bias=bias, stream=stream)
+
+
+def embed_pixels(src_dev, plan: BatchPlan, w_pixels, bias_pixels, out_dtype: str = "bf16", out=None,
+                 workspace=None, stream=None):
+    """Still images straight to their patch embeddings (vision page,
+    MiMoVisionPatchEmbed, over the processing page's pixels) in one kernel
+    launch: out [total_rows, E], rows in merge-block order, as
+    patch_embed(preprocess(...)) would give with the folded weight, but
+    without writing the pixel rows."""
+    import torch
+    dev = src_dev.device
+    e = w_pixels.shape[0]
+    with _on_stream(torch, stream, (src_dev, w_pixels, bias_pixels, out, workspace)):
+        if out is None:
+            tdtype = {"f32": torch.float32, "bf16": torch.bfloat16}[out_dtype]
+            out = torch.empty((max(plan.total_rows, 1), e), dtype=tdtype, device=dev)
+        if workspace is None:
+            workspace = torch.empty(max(_abi.workspace_bytes(len(plan)), 16), dtype=torch.uint8,
+                                    device=dev)
+        _abi.pixel_embed(plan.desc, src_dev, w_pixels, bias_pixels, out, workspace, stream=stream)
+    return out[:plan.total_rows]
