@@ -20,26 +20,39 @@
 // float32); so the kernel is integer up to that lookup and its results are
 // bit-exact.
 //
-// Kernel: one workgroup per merge unit (32 x 32 output pixels).  A unit
-// that neither axis resizes reads its source pixels straight into the
-// output block.  Otherwise it works in groups of output rows sized so that
-// the band of source rows their vertical taps need fits LDS.  Per group:
-// the source block the tile's taps touch is staged into LDS (one dword per
-// pixel, RGB bytes; 4 pixels per load, realigned with v_alignbyte, in row
-// chunks that fit), the horizontal pass reads it from there into the band,
-// the vertical pass turns the band into a 32 x 32 byte block; then the
-// unit's 4 rows (both temporal slots) go out with 16-byte stores, to
-// merge-block and/or column order.  The LDS is dynamic, sized by the host
-// for the batch's widest band, staging and tap tables, so that batches of
-// mild resizes keep several workgroups on each CU.
+// Kernel: one workgroup (256 threads) per merge unit, 32 x 32 output
+// pixels.  A unit that neither axis resizes reads its source pixels straight
+// into an output block.  Otherwise it works in groups of output rows, sized
+// so that the band of source rows their vertical taps read fits LDS; per
+// group, the source block its taps touch is staged into LDS (in row chunks
+// that fit), the horizontal pass turns it into the band, and the vertical
+// pass reads the band and writes the group's output values.
+//
+// Sums of taps, four at a time.  A pass's input is held as signed bytes
+// x' = x - 128 and each output's weights as three planes of signed base-256
+// digits, w = a + 256 b + 65536 c with a, b, c in [-128, 127].  Then
+//     sum x w = sum x' a + 256 sum x' b + 65536 sum x' c + 128 sum w,
+// and each partial sum over four consecutive taps is one v_dot4_i32_i8 (four
+// exact 8 x 8-bit products added to an int32).  The host folds 128 sum w and
+// the rounding term into one constant per output.  It is all int32
+// arithmetic, exact modulo 2^32 like PIL's own int32 sum, so the bytes are
+// PIL's.  For that, consecutive taps must be consecutive bytes: the source
+// block is staged as three channel planes, and the horizontal pass writes
+// the band transposed (one LDS column per output column and channel, source
+// rows consecutive), so the vertical pass finds its taps consecutive too.
+// A window may start at any byte: it is read as aligned dwords and
+// realigned with v_alignbyte.  An axis that is not resized (when the other
+// one is) runs the same code with one tap of weight 1.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <map>
 #include <string>
 #include <thread>
+#include <tuple>
 #include <utility>
 #include <vector>
 
@@ -50,36 +63,38 @@
 namespace mimo {
 namespace {
 
-// Threads per workgroup: 512, or 256 for a batch of at least
-// kNarrowMinTiles tiles whose resized axes have at most kNarrowMaxTaps taps
-// per output (mild resizes), where smaller workgroups keep more units in
-// flight (RGBA 640x480..1920x1080 under the stock geometry: 0.53 against
-// 0.62 ms; a 1.7x downscale would take 1.81 against 1.49 ms).  A small grid
-// keeps the wide workgroups, which finish each tile sooner.
-constexpr int kHfThreadsWide = 512, kHfThreadsNarrow = 256;
-constexpr int kNarrowMaxTaps = 5;
-constexpr int64_t kNarrowMinTiles = 1024;
-constexpr int kWeightBits = 22;           // fractional bits of the resampler's weights
-constexpr int kMidRows = 256;             // most LDS band rows (32 pixels each)
-constexpr int kStageDwords = 4096;        // most LDS source staging (one dword per pixel)
-constexpr int kTapBudget = 2048;          // most LDS weights per axis (else they are read from memory)
+constexpr int kHfThreads = 256;
+constexpr int kWeightBits = 22;              // fractional bits of the resampler's weights
+constexpr int kMaxBandRows = 256;            // most source rows one group's vertical taps read
+constexpr int kMaxStageBytes = 48 * 1024;    // LDS for one staged row chunk (three planes)
+constexpr int kMaxStagePitch = kMaxStageBytes / 12;  // bytes per staged plane row (>= 4 rows a chunk)
+constexpr int kRegDwords = 3;                // windows of up to 12 taps keep their record in registers
+constexpr int kRegRecord = 4 * kRegDwords;   // (the record of such a window: 12 dwords at most)
+constexpr int kStageBatch = 4;                // staging loads a thread issues before using them
+constexpr int kLutBytes = 3 * 256 * 4;
+constexpr int kBlockBytes = kUnitPx * kUnitPx * 4;  // the direct path's unit block (RGB per dword)
 constexpr int64_t kParallelTapWork = 1 << 18;  // weights (outputs x taps) worth several host threads
-constexpr int kFixedDwords = 3 * 256 + kUnitPx * kUnitPx + 2 * kUnitPx;  // lut, block, first x/y
-constexpr int kBufferWord3 = 0x00020000;  // raw buffer resource word 3 (gfx9 family)
+constexpr int kBufferWord3 = 0x00020000;     // raw buffer resource word 3 (gfx9 family)
 
 // Per-item record of the contrast kernel (64 bytes).
 struct HfItem {
     int64_t src_offset;   // bytes into the packed sources
     int64_t row_offset;   // first output row
-    int64_t x_tab;        // int32 offset of the column taps (first, count, weights), or -1
-    int64_t y_tab;        // int32 offset of the row taps, or -1
+    int64_t x_tab;        // int32 offset of the column table, or -1 when neither axis is resized
+    int64_t y_tab;        // int32 offset of the row table, or -1 likewise
     int32_t src_h, src_w;
     int32_t channels;     // 3 or 4 (alpha ignored)
     int32_t blocks_h, blocks_w;
-    int32_t kx, ky;       // weights per output column / row
+    int32_t ndx, ndy;     // dwords (four taps each) of an output column's / row's window
     int32_t group;        // output rows per vertical group (divides 32)
 };
 static_assert(sizeof(HfItem) == 64, "HfItem must stay 64 bytes");
+
+// An axis table is first[n_out] (each output's first input) followed by one
+// record of rec_dwords(nd) int32 per output: the constant 2^21 + 128 sum w,
+// then the digit planes a[nd], b[nd], c[nd], tap t in byte t % 4 of dword
+// t / 4, zero past the output's own taps; padded to whole 16-byte vectors.
+__host__ __device__ constexpr int rec_dwords(int nd) { return (1 + 3 * nd + 3) & ~3; }
 
 struct HfArgs {
     const uint8_t *src;
@@ -91,44 +106,20 @@ struct HfArgs {
     void *rows;                 // merge-block order, nullable
     void *rows_col;             // column order, nullable
     int32_t n;
-    // dynamic LDS, sized for the batch (dwords, each a multiple of 4):
-    // [fixed][x weights][y weights][band mid_rows x 32][stage]
-    int32_t xw_budget, yw_budget, mid_rows, stage_dwords;
+    // dynamic LDS, sized for the batch: [lut][band][stage]; the direct path
+    // uses the bytes after the lut for its block
+    int32_t band_bytes, stage_bytes;
 };
 
 // workspace: [HfItem x n][int64 tile_begin x (n+1)][float lut x 768][int32 taps]
 size_t hf_items_bytes(int32_t n) { return align256(sizeof(HfItem) * size_t(n)); }
 size_t hf_prefix_bytes(int32_t n) { return align256(sizeof(int64_t) * (size_t(n) + 1)); }
-constexpr size_t kLutBytes = 3 * 256 * sizeof(float);
 
-__device__ __forceinline__ uint32_t round_clip_byte(int32_t acc) {
-    const int32_t v = (acc + (1 << (kWeightBits - 1))) >> kWeightBits;
-    return uint32_t(v < 0 ? 0 : (v > 255 ? 255 : v));
-}
-
-typedef const __attribute__((address_space(3))) int32_t *lds_weights;
-
-// One resampled pixel: `taps` taps of px[j * stride] (RGB bytes in a dword,
-// in LDS) weighted by w[j], summed per channel in int32 and rounded back to
-// a byte.  `taps` is the same for every output of an axis (unused taps have
-// zero weight), so the loop is uniform across the wavefront.  The weights
-// have kWeightBits fraction bits and magnitude below 2, so they are 24-bit
-// signed values: said so explicitly, the products run on the full-rate
-// 24-bit multiplier instead of a 64-bit multiply-add.  The weights come from
-// LDS or from memory; the two are separate overloads so that neither goes
-// through flat (generic) addressing.
-template <typename Weights>
-__device__ __forceinline__ uint32_t resample_px(const uint32_t *px, int stride, Weights w, int taps) {
-    int32_t acc0 = 0, acc1 = 0, acc2 = 0;
-    for (int j = 0; j < taps; ++j) {
-        const uint32_t p = px[j * stride];
-        const int32_t wj = __builtin_amdgcn_sbfe(w[j], 0, 24);
-        acc0 += int32_t(p & 255u) * wj;
-        acc1 += int32_t((p >> 8) & 255u) * wj;
-        acc2 += int32_t((p >> 16) & 255u) * wj;
-    }
-    return round_clip_byte(acc0) | (round_clip_byte(acc1) << 8) | (round_clip_byte(acc2) << 16);
-}
+// Dwords per staged source row and per band column: whole dwords with one
+// spare for the realigning read, the band's count made odd so that the
+// horizontal pass's writes of 32 columns fall into distinct LDS banks.
+__host__ __device__ __forceinline__ int stage_pitch(int span) { return ((span + 3) >> 2) + 1; }
+__host__ __device__ __forceinline__ int band_pitch(int rows) { return (((rows + 3) >> 2) + 1) | 1; }
 
 // A raw buffer resource over [base & ~3, src_end): reads past the end
 // return zero.  `lead` is base's offset inside it.
@@ -149,41 +140,204 @@ __device__ __forceinline__ SrcWindow src_window(const HfArgs &a, uint64_t base) 
     return w;
 }
 
-// RGB bytes of the four consecutive pixels at byte offset `off` of the
-// window (any alignment), one pixel per dword; alpha is dropped.  One
-// 12-byte (RGB) or 16-byte (RGBA) load when `off` is dword aligned, else a
-// 16-byte load (plus a dword for RGBA) realigned with v_alignbyte.
-__device__ __forceinline__ void load_quad(const SrcWindow &w, uint32_t off, int channels, u32x4 &p) {
+// The 12 (RGB) or 16 (RGBA) bytes of the four consecutive pixels at byte
+// offset `off` of the window (any alignment), in u[0..3].
+__device__ __forceinline__ void load_quad_bytes(const SrcWindow &w, uint32_t off, int channels, uint32_t (&u)[4]) {
     const uint32_t al = off & ~3u, sh = off & 3u;
+    const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.rsrc, int(al), 0, 0));
+    uint32_t v4 = 0;
+    if (channels == 4) v4 = __builtin_amdgcn_raw_buffer_load_b32(w.rsrc, int(al) + 16, 0, 0);
+    u[0] = __builtin_amdgcn_alignbyte(v.y, v.x, sh);
+    u[1] = __builtin_amdgcn_alignbyte(v.z, v.y, sh);
+    u[2] = __builtin_amdgcn_alignbyte(v.w, v.z, sh);
+    u[3] = __builtin_amdgcn_alignbyte(v4, v.w, sh);
+}
+
+// RGB bytes of four pixels, one pixel per dword (the direct path's block).
+__device__ __forceinline__ u32x4 quad_pixels(const uint32_t (&u)[4], int channels) {
+    if (channels == 3)  // R0 G0 B0 R1 | G1 B1 R2 G2 | B2 R3 G3 B3
+        return u32x4{u[0] & 0x00FFFFFFu, __builtin_amdgcn_perm(u[1], u[0], 0x0C050403u),
+                     __builtin_amdgcn_perm(u[2], u[1], 0x0C040302u), u[2] >> 8};
+    return u32x4{u[0] & 0x00FFFFFFu, u[1] & 0x00FFFFFFu, u[2] & 0x00FFFFFFu, u[3] & 0x00FFFFFFu};
+}
+
+// Four pixels' bytes split into the three channel planes (one channel's
+// four bytes per dword), as signed bytes x - 128.  (v_perm_b32 byte
+// selectors: 0-3 pick a byte of the second operand, 4-7 of the first,
+// 12 gives zero.)
+__device__ __forceinline__ void quad_planes(const uint32_t (&u)[4], int channels, uint32_t (&p)[3]) {
     if (channels == 3) {
-        uint32_t u0, u1, u2;
-        if (sh == 0) {
-            const u32x3 v = __builtin_bit_cast(u32x3, __builtin_amdgcn_raw_buffer_load_b96(w.rsrc, int(al), 0, 0));
-            u0 = v.x; u1 = v.y; u2 = v.z;
-        } else {
-            const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.rsrc, int(al), 0, 0));
-            u0 = __builtin_amdgcn_alignbyte(v.y, v.x, sh);
-            u1 = __builtin_amdgcn_alignbyte(v.z, v.y, sh);
-            u2 = __builtin_amdgcn_alignbyte(v.w, v.z, sh);
-        }
-        // bytes R0 G0 B0 R1 | G1 B1 R2 G2 | B2 R3 G3 B3 -> one pixel per dword
-        p.x = u0 & 0x00FFFFFFu;
-        p.y = __builtin_amdgcn_perm(u1, u0, 0x0C050403u);
-        p.z = __builtin_amdgcn_perm(u2, u1, 0x0C040302u);
-        p.w = u2 >> 8;
+        // R: u0.b0 u0.b3 u1.b2 u2.b1   G: u0.b1 u1.b0 u1.b3 u2.b2   B: u0.b2 u1.b1 u2.b0 u2.b3
+        p[0] = __builtin_amdgcn_perm(u[2], __builtin_amdgcn_perm(u[1], u[0], 0x0C060300u), 0x05020100u);
+        p[1] = __builtin_amdgcn_perm(u[2], __builtin_amdgcn_perm(u[1], u[0], 0x0C070401u), 0x06020100u);
+        p[2] = __builtin_amdgcn_perm(u[2], __builtin_amdgcn_perm(u[1], u[0], 0x0C0C0502u), 0x07040100u);
     } else {
-        u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.rsrc, int(al), 0, 0));
-        if (sh != 0) {
-            const uint32_t v4 = __builtin_amdgcn_raw_buffer_load_b32(w.rsrc, int(al) + 16, 0, 0);
-            v = {__builtin_amdgcn_alignbyte(v.y, v.x, sh), __builtin_amdgcn_alignbyte(v.z, v.y, sh),
-                 __builtin_amdgcn_alignbyte(v.w, v.z, sh), __builtin_amdgcn_alignbyte(v4, v.w, sh)};
-        }
-        p = v & 0x00FFFFFFu;
+        const uint32_t rb0 = __builtin_amdgcn_perm(u[1], u[0], 0x06040200u);  // R0 B0 R1 B1
+        const uint32_t rb1 = __builtin_amdgcn_perm(u[3], u[2], 0x06040200u);  // R2 B2 R3 B3
+        const uint32_t ga0 = __builtin_amdgcn_perm(u[1], u[0], 0x07050301u);  // G0 A0 G1 A1
+        const uint32_t ga1 = __builtin_amdgcn_perm(u[3], u[2], 0x07050301u);  // G2 A2 G3 A3
+        p[0] = __builtin_amdgcn_perm(rb1, rb0, 0x06040200u);
+        p[1] = __builtin_amdgcn_perm(ga1, ga0, 0x06040200u);
+        p[2] = __builtin_amdgcn_perm(rb1, rb0, 0x07050301u);
+    }
+#pragma unroll
+    for (int c = 0; c < 3; ++c) p[c] ^= 0x80808080u;
+}
+
+// A window's record (rec_dwords(nd) <= kRegRecord dwords) into registers.
+__device__ __forceinline__ void load_record(const int32_t *rec, int nd, uint32_t (&r)[kRegRecord]) {
+    const int vecs = rec_dwords(nd) >> 2;
+#pragma unroll
+    for (int v = 0; v < kRegDwords; ++v) {
+        u32x4 q = {0u, 0u, 0u, 0u};
+        if (v < vecs) q = *reinterpret_cast<const u32x4 *>(rec + 4 * v);
+        r[4 * v] = q.x;
+        r[4 * v + 1] = q.y;
+        r[4 * v + 2] = q.z;
+        r[4 * v + 3] = q.w;
     }
 }
 
-// One output value of the tile in the final layout: 4 floats (4 pixels of
-// one patch row, one channel) into both temporal slots.
+// sum over four taps of x * w (signed bytes) plus acc: v_dot4_i32_i8.
+__device__ __forceinline__ int32_t dot4(uint32_t x, uint32_t w, int32_t acc) {
+    return __builtin_amdgcn_sdot4(int32_t(x), int32_t(w), acc, false);
+}
+
+// Two sums s0, s1 shifted right by kWeightBits and saturated to a byte
+// (unsigned, or signed for the _i8 form), in bytes 0 and 1 of the result;
+// the upper half of the result register is left undefined.  The inputs come
+// from v_dot4 instructions, whose results a VALU instruction may read only
+// three wait states later; the compiler keeps that distance for its own
+// instructions but cannot see into this one, hence the s_nop.
+__device__ __forceinline__ uint32_t shift_pack_u8(int32_t s0, int32_t s1) {
+    uint32_t d;
+    asm("s_nop 2\n\tv_ashr_pk_u8_i32 %0, %1, %2, 22" : "=v"(d) : "v"(s0), "v"(s1));
+    return d;
+}
+__device__ __forceinline__ uint32_t shift_pack_i8(int32_t s0, int32_t s1) {
+    uint32_t d;
+    asm("s_nop 2\n\tv_ashr_pk_i8_i32 %0, %1, %2, 22" : "=v"(d) : "v"(s0), "v"(s1));
+    return d;
+}
+static_assert(kWeightBits == 22, "the shift in the packing instructions");
+
+// Four bytes from two packed pairs: bytes 0, 1 of lo, then bytes 0, 1 of hi.
+__device__ __forceinline__ uint32_t join_pairs(uint32_t lo, uint32_t hi) {
+    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
+// Four window sums at once.  Both passes read four windows that start at the
+// same offset in four neighbouring LDS lines (four band rows in the
+// horizontal pass, four output columns in the vertical one), and both store
+// those lines interleaved by dwords: at p, 16-byte group q holds dword q of
+// each of the four.  So one 16-byte read gives dword q of all four windows.
+// Each window starts `sh` bytes into its dword 0 and is realigned with
+// v_alignbyte.  The three digit sums are chained, the higher one shifted
+// into the next one's addend: s = ((sum c << 8) + sum b) << 8) + sum a + K,
+// which saves setting up two of the three accumulators.
+template <int ND>
+__device__ __forceinline__ void quad_sums(const uint8_t *p, uint32_t sh, const uint32_t (&r)[kRegRecord],
+                                          int32_t (&s)[4]) {
+    u32x4 g[ND + 1];
+#pragma unroll
+    for (int q = 0; q <= ND; ++q) g[q] = *reinterpret_cast<const u32x4 *>(p + 16 * q);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        uint32_t x[ND];
+#pragma unroll
+        for (int q = 0; q < ND; ++q) x[q] = __builtin_amdgcn_alignbyte(g[q + 1][j], g[q][j], sh);
+        int32_t sc = 0;
+#pragma unroll
+        for (int q = 0; q < ND; ++q) sc = dot4(x[q], r[1 + 2 * ND + q], sc);
+        int32_t sb = int32_t(uint32_t(sc) << 8);
+#pragma unroll
+        for (int q = 0; q < ND; ++q) sb = dot4(x[q], r[1 + ND + q], sb);
+        int32_t sa = int32_t((uint32_t(sb) << 8) + r[0]);
+#pragma unroll
+        for (int q = 0; q < ND; ++q) sa = dot4(x[q], r[1 + q], sa);
+        s[j] = sa;
+    }
+}
+
+// The same for windows of any length, the record read from memory.
+__device__ __forceinline__ void quad_sums_any(const uint8_t *p, uint32_t sh, const int32_t *rec, int nd,
+                                              int32_t (&s)[4]) {
+    int32_t sa[4], sb[4], sc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sa[j] = sb[j] = sc[j] = 0;
+    u32x4 lo = *reinterpret_cast<const u32x4 *>(p);
+    for (int q = 0; q < nd; ++q) {
+        const u32x4 hi = *reinterpret_cast<const u32x4 *>(p + 16 * (q + 1));
+        const uint32_t wa = uint32_t(rec[1 + q]), wb = uint32_t(rec[1 + nd + q]), wc = uint32_t(rec[1 + 2 * nd + q]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t x = __builtin_amdgcn_alignbyte(hi[j], lo[j], sh);
+            sa[j] = dot4(x, wa, sa[j]);
+            sb[j] = dot4(x, wb, sb[j]);
+            sc[j] = dot4(x, wc, sc[j]);
+        }
+        lo = hi;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        s[j] = int32_t(uint32_t(rec[0]) + uint32_t(sa[j]) + ((uint32_t(sb[j]) + (uint32_t(sc[j]) << 8)) << 8));
+}
+
+template <int ND>
+__device__ __forceinline__ void window_sums(const uint8_t *p, uint32_t sh, const uint32_t (&r)[kRegRecord],
+                                            const int32_t *rec, int nd, int32_t (&s)[4]) {
+    if (ND)
+        quad_sums<ND ? ND : 1>(p, sh, r, s);
+    else
+        quad_sums_any(p, sh, rec, nd, s);
+}
+
+// Horizontal pass of the thread's output column over band row groups
+// rq = tid / 32, + 8, ...: per channel, the window sums of four band rows,
+// saturated to signed bytes (the column records' constants carry the -128
+// that makes them the PIL bytes less 128, the vertical pass's input form),
+// as one dword.
+template <int ND>
+__device__ __forceinline__ void h_pass(const uint8_t *stage, int sgroup, uint8_t *bcol, int bgroup, int groups,
+                                       int x0, const uint32_t (&r)[kRegRecord], const int32_t *rec, int nd,
+                                       int tid) {
+    for (int rq = tid >> 5; rq < groups; rq += kHfThreads / kUnitPx) {
+        const uint8_t *src = stage + rq * 3 * sgroup + (x0 >> 2) * 16;
+#pragma unroll
+        for (int c = 0; c < 3; ++c) {
+            int32_t sum[4];
+            window_sums<ND>(src + c * sgroup, uint32_t(x0) & 3u, r, rec, nd, sum);
+            *reinterpret_cast<uint32_t *>(bcol + c * 8 * bgroup + rq * 16) =
+                join_pairs(shift_pack_i8(sum[0], sum[1]), shift_pack_i8(sum[2], sum[3]));
+        }
+    }
+}
+
+// Vertical pass: items (row, patch column, channel, quad) of the group, the
+// row fixed per thread; four output columns of one channel per item, the
+// bytes through the rescale-and-normalise table, handed to put.
+template <int ND, typename Put>
+__device__ __forceinline__ void v_pass(const uint8_t *band, int bgroup, int y0, const float *lut,
+                                       const uint32_t (&r)[kRegRecord], const int32_t *rec, int nd, int n_items,
+                                       int gsh, int tid, Put &&put) {
+    for (int idx = tid; idx < n_items; idx += kHfThreads) {
+        const int qd = idx & 3;
+        const int mc = idx >> (2 + gsh);
+        const int mw = mc >= 3 ? 1 : 0;
+        const int c = mc - 3 * mw;
+        int32_t sum[4];
+        window_sums<ND>(band + (c * 8 + mw * 4 + qd) * bgroup + (y0 >> 2) * 16, uint32_t(y0) & 3u, r, rec, nd, sum);
+        const uint32_t bytes = join_pairs(shift_pack_u8(sum[0], sum[1]), shift_pack_u8(sum[2], sum[3]));
+        const float *lut_c = lut + c * 256;
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = lut_c[(bytes >> (8 * j)) & 255u];
+        put(mw, c, qd, v);
+    }
+}
+
+// Four output values (4 pixels of one patch row, one channel) into both
+// temporal slots of a row.
 template <typename OutT>
 __device__ __forceinline__ void store_pair(OutT *row_ptr, const float (&v)[4]);
 
@@ -203,19 +357,11 @@ __device__ __forceinline__ void store_pair<uint16_t>(uint16_t *p, const float (&
     __builtin_nontemporal_store(q, reinterpret_cast<u32x2 *>(p + kPlane));
 }
 
-template <typename OutT, int kHfThreads>
+template <typename OutT>
 __global__ __launch_bounds__(kHfThreads) void hf_preprocess_kernel(HfArgs a) {
-    // LDS, sized by the host for the batch (see HfArgs)
     extern __shared__ uint32_t lds[];
-    float *lut = reinterpret_cast<float *>(lds);                     // [3][256]
-    uint32_t *block = lds + 3 * 256;                                  // the unit's output bytes (RGB per dword)
-    int32_t *xfirst_s = reinterpret_cast<int32_t *>(block + kUnitPx * kUnitPx);  // the tile's taps: first
-    int32_t *yfirst_s = xfirst_s + kUnitPx;                           // (relative to the staged block /
-                                                                      // band) and weights
-    int32_t *xw_s = reinterpret_cast<int32_t *>(lds + kFixedDwords);
-    int32_t *yw_s = xw_s + a.xw_budget;
-    uint32_t *mid = reinterpret_cast<uint32_t *>(yw_s + a.yw_budget);  // horizontal-pass band
-    uint32_t *stage = mid + a.mid_rows * kUnitPx;                     // source pixels of a row chunk
+    float *lut = reinterpret_cast<float *>(lds);  // [3][256]
+    uint8_t *region = reinterpret_cast<uint8_t *>(lds) + kLutBytes;
     const int64_t tile = xcd_contiguous_tile(blockIdx.x, gridDim.x);
     const int img = find_segment(a.tile_begin, a.n, tile);
     const HfItem d = a.items[img];
@@ -231,128 +377,136 @@ __global__ __launch_bounds__(kHfThreads) void hf_preprocess_kernel(HfArgs a) {
     const int bc = unit - br * d.blocks_w;
     const int oy0 = br * kUnitPx, ox0 = bc * kUnitPx;
     const int tid = threadIdx.x;
-    for (int i = tid; i < 3 * 256; i += kHfThreads) lut[i] = a.lut[i];
-
     const uint8_t *img_src = a.src + d.src_offset;
-    const int64_t row_bytes = int64_t(d.src_w) * d.channels;
-    if (!d.kx && !d.ky) {
-        // no resize: the unit's 32 x 32 source pixels go straight to the block
+    const int C = d.channels;
+    const uint32_t row_bytes = uint32_t(d.src_w) * uint32_t(C);  // < 2^23 (the host checked)
+
+    // The thread's output row of the group in the vertical pass (and in the
+    // direct path's stores): the same for each of its work items.
+    const int yl = (tid >> 2) & (G - 1);
+    // Output values (yl, mw, c, qd): 4 pixels of one patch row and channel,
+    // into both temporal slots of the unit's row, in the orders asked for.
+    // The thread's pixel row y of the unit fixes its rows' base pointers.
+    const int y_unit = g0 + yl;
+    const int64_t row_m = d.row_offset + int64_t(br * d.blocks_w + bc) * kRowsPerUnit + (y_unit >> 4) * kMerge;
+    const int64_t row_c = d.row_offset + int64_t(bc * d.blocks_h + br) * kRowsPerUnit + (y_unit >> 4) * kMerge;
+    const int py_off = (y_unit & (kPatch - 1)) * kPatch;
+    OutT *out_m = a.rows ? static_cast<OutT *>(a.rows) + row_m * kRowLen + py_off : nullptr;
+    OutT *out_c = a.rows_col ? static_cast<OutT *>(a.rows_col) + row_c * kRowLen + py_off : nullptr;
+    auto put = [&](int mw, int c, int qd, const float (&v)[4]) {
+        const int off = mw * kRowLen + c * (kTemporal * kPlane) + qd * 4;
+        if (out_m) store_pair<OutT>(out_m + off, v);
+        if (out_c) store_pair<OutT>(out_c + off, v);
+    };
+    const int n_items = G * 2 * 3 * 4;  // (row, patch column, channel, quad); a wavefront: 16 rows x 4 quads
+
+    if (d.x_tab < 0) {
+        // no resize: the unit's 32 x 32 source pixels go to the block
+        for (int i = tid; i < 3 * 256; i += kHfThreads) lut[i] = a.lut[i];
+        uint32_t *block = reinterpret_cast<uint32_t *>(region);
         const SrcWindow win = src_window(a, reinterpret_cast<uint64_t>(img_src) +
-                                                uint64_t(int64_t(oy0) * row_bytes + int64_t(ox0) * d.channels));
+                                                uint64_t(int64_t(oy0) * row_bytes + int64_t(ox0) * C));
         for (int idx = tid; idx < kUnitPx * kUnitPx / 4; idx += kHfThreads) {
             const int r = idx >> 3, q = idx & 7;
-            u32x4 px;
-            load_quad(win, win.lead + uint32_t(int64_t(r) * row_bytes + 4 * q * d.channels), d.channels, px);
-            *reinterpret_cast<u32x4 *>(&block[r * kUnitPx + 4 * q]) = px;
+            uint32_t u[4];
+            load_quad_bytes(win, win.lead + __umul24(uint32_t(r), row_bytes) + uint32_t(4 * q * C), C, u);
+            *reinterpret_cast<u32x4 *>(&block[r * kUnitPx + 4 * q]) = quad_pixels(u, C);
         }
         __syncthreads();
-    } else {
-        const int dst_w = d.blocks_w * kUnitPx, dst_h = d.blocks_h * kUnitPx;
-        const int32_t *xf = d.kx ? a.taps + d.x_tab : nullptr;  // first[dst_w], count[dst_w], w[dst_w][kx]
-        const int32_t *yf = d.ky ? a.taps + d.y_tab : nullptr;
-        // source columns the tile's 32 output columns read, and their taps in LDS
-        // (the weights too, when they fit; else they are read from memory)
-        const int xlo = xf ? xf[ox0] : ox0;
-        const int xhi = xf ? xf[ox0 + kUnitPx - 1] + xf[dst_w + ox0 + kUnitPx - 1] : ox0 + kUnitPx;
-        const int quads = (xhi - xlo + 3) >> 2;  // staged 4 pixels at a time
-        const int spitch = 4 * quads;             // <= a.stage_dwords (the host checked)
-        const bool xw_in_lds = xf && kUnitPx * d.kx <= a.xw_budget;
-        if (xf) {
-            for (int i = tid; i < kUnitPx; i += kHfThreads) xfirst_s[i] = xf[ox0 + i] - xlo;
-            if (xw_in_lds)
-                for (int i = tid; i < kUnitPx * d.kx; i += kHfThreads)
-                    xw_s[i] = xf[2 * dst_w + int64_t(ox0) * d.kx + i];
+        for (int idx = tid; idx < n_items; idx += kHfThreads) {
+            const int qd = idx & 3;
+            const int mc = idx >> (2 + gsh);
+            const int mw = mc >= 3 ? 1 : 0;
+            const int c = mc - 3 * mw;
+            const uint32_t *px = &block[(g0 + yl) * kUnitPx + mw * kPatch + qd * 4];
+            float v[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = lut[c * 256 + ((px[j] >> (8 * c)) & 255u)];
+            put(mw, c, qd, v);
         }
-        const bool yw_in_lds = yf && G * d.ky <= a.yw_budget;
-        const int oy_a = oy0 + g0, oy_b = oy_a + G - 1;
-        const int ylo = yf ? yf[oy_a] : oy_a;
-        const int yhi = yf ? yf[oy_b] + yf[dst_h + oy_b] : oy_b + 1;
-        const int nrows = yhi - ylo;  // <= a.mid_rows (the host sized G)
-        if (yf) {
-            for (int i = tid; i < G; i += kHfThreads) yfirst_s[i] = yf[oy_a + i] - ylo;
-            if (yw_in_lds)
-                for (int i = tid; i < G * d.ky; i += kHfThreads)
-                    yw_s[i] = yf[2 * dst_h + int64_t(oy_a) * d.ky + i];
-        }
-        const int chunk = min(nrows, a.stage_dwords / spitch);
-        const float inv_quads = 1.0f / float(quads);
-        for (int r0 = 0; r0 < nrows; r0 += chunk) {
-            const int nr = min(chunk, nrows - r0);
-            // stage source rows [ylo + r0, ylo + r0 + nr) x [xlo, xlo + spitch);
-            // the up to 3 pixels past xhi are never read
-            const SrcWindow win = src_window(a, reinterpret_cast<uint64_t>(img_src) +
-                                                    uint64_t(int64_t(ylo + r0) * row_bytes +
-                                                             int64_t(xlo) * d.channels));
-            for (int idx = tid; idx < nr * quads; idx += kHfThreads) {
-                const int r = div_small(idx, quads, inv_quads);
-                const int q = idx - r * quads;
-                u32x4 px;
-                load_quad(win, win.lead + uint32_t(int64_t(r) * row_bytes + 4 * q * d.channels), d.channels, px);
-                *reinterpret_cast<u32x4 *>(&stage[r * spitch + 4 * q]) = px;
+        return;
+    }
+
+    const int dst_w = d.blocks_w * kUnitPx, dst_h = d.blocks_h * kUnitPx;
+    const int32_t *xt = a.taps + d.x_tab;  // first[dst_w], then the records
+    const int32_t *yt = a.taps + d.y_tab;
+    const int ndx = d.ndx, ndy = d.ndy;
+    const int hx = tid & 31;  // the thread's output column in the horizontal pass
+    const int oy_a = oy0 + g0;
+    const int32_t *xrec = xt + dst_w + int64_t(ox0 + hx) * rec_dwords(ndx);
+    const int32_t *yrec = yt + dst_h + int64_t(oy_a + yl) * rec_dwords(ndy);
+    uint32_t xr[kRegRecord], yr[kRegRecord];
+    if (ndx <= kRegDwords) load_record(xrec, ndx, xr);
+    if (ndy <= kRegDwords) load_record(yrec, ndy, yr);
+    for (int i = tid; i < 3 * 256; i += kHfThreads) lut[i] = a.lut[i];
+    // the tile's source block: columns [xlo, xlo + xspan), rows [ylo, ylo + nrows)
+    // (4 nd inputs past each axis's last first input; bytes past an output's
+    // own taps have zero weight, and reads past the sources return zero)
+    const int xlo = xt[ox0];
+    const int xspan = xt[ox0 + kUnitPx - 1] - xlo + 4 * ndx;
+    const int x0 = xt[ox0 + hx] - xlo;
+    const int ylo = yt[oy_a];
+    const int nrows = yt[oy_a + G - 1] - ylo + 4 * ndy;  // <= kMaxBandRows (the host sized G)
+    const int y0 = yt[oy_a + yl] - ylo;
+    // LDS lines interleaved by dwords in groups of four (see quad_sums):
+    // the staged planes as [row / 4][channel][dword of the row][row % 4],
+    // the band as [channel][column / 4][dword of the column][column % 4]
+    const int sgroup = 16 * stage_pitch(xspan);  // bytes per (row group, channel)
+    const int bgroup = 16 * band_pitch(nrows);   // bytes per (channel, column group)
+    const int quads = (xspan + 3) >> 2;
+    // staged rows per chunk: a multiple of 4, at least 4 (the host checked)
+    const int chunk = min((nrows + 3) & ~3, (a.stage_bytes / (12 * stage_pitch(xspan))) & ~3);
+    uint8_t *band = region;
+    uint8_t *stage = region + a.band_bytes;
+    // staging work items (row, quad) with the quads of a row padded to 2^lq
+    const int lq = quads > 1 ? 32 - __builtin_clz(unsigned(quads - 1)) : 0;
+    for (int r0 = 0; r0 < nrows; r0 += chunk) {
+        const int nr = min(chunk, nrows - r0);
+        const SrcWindow win = src_window(a, reinterpret_cast<uint64_t>(img_src) +
+                                                uint64_t(int64_t(ylo + r0) * row_bytes + int64_t(xlo) * C));
+        const int total = nr << lq;
+        for (int base = tid; base < total; base += kStageBatch * kHfThreads) {
+            // all of a batch's loads first (reads outside the window return
+            // zero, so an item past the end may load too), then their planes
+            uint32_t u[kStageBatch][4];
+#pragma unroll
+            for (int k = 0; k < kStageBatch; ++k) {
+                const int idx = base + k * kHfThreads;
+                const uint32_t r = uint32_t(idx >> lq), q = uint32_t(idx & ((1 << lq) - 1));
+                load_quad_bytes(win, win.lead + __umul24(r, row_bytes) + q * uint32_t(4 * C), C, u[k]);
             }
-            __syncthreads();
-            // horizontal pass (or a copy) into band rows [r0, r0 + nr)
-            for (int idx = tid; idx < nr * kUnitPx; idx += kHfThreads) {
-                const int r = idx >> 5, x = idx & 31;
-                const uint32_t *line = &stage[r * spitch];
-                uint32_t px;
-                if (xf) {
-                    const int first = xfirst_s[x];
-                    if (xw_in_lds)
-                        px = resample_px(line + first, 1, (lds_weights)(&xw_s[x * d.kx]), d.kx);
-                    else
-                        px = resample_px(line + first, 1, xf + 2 * dst_w + int64_t(ox0 + x) * d.kx, d.kx);
-                } else {
-                    px = line[x];
+#pragma unroll
+            for (int k = 0; k < kStageBatch; ++k) {
+                const int idx = base + k * kHfThreads;
+                const int r = idx >> lq, q = idx & ((1 << lq) - 1);
+                if (idx < total && q < quads) {
+                    uint32_t pl[3];
+                    quad_planes(u[k], C, pl);
+                    uint8_t *dst = stage + (r >> 2) * 3 * sgroup + q * 16 + (r & 3) * 4;
+#pragma unroll
+                    for (int c = 0; c < 3; ++c) *reinterpret_cast<uint32_t *>(dst + c * sgroup) = pl[c];
                 }
-                mid[(r0 + r) * kUnitPx + x] = px;
             }
-            __syncthreads();
         }
-        // vertical pass (or a copy) for output rows [oy_a, oy_b]
-        for (int idx = tid; idx < G * kUnitPx; idx += kHfThreads) {
-            const int r = idx >> 5, x = idx & 31;
-            const int oy = oy_a + r;
-            uint32_t px;
-            if (yf) {
-                const uint32_t *col = &mid[yfirst_s[r] * kUnitPx + x];
-                if (yw_in_lds)
-                    px = resample_px(col, kUnitPx, (lds_weights)(&yw_s[r * d.ky]), d.ky);
-                else
-                    px = resample_px(col, kUnitPx, yf + 2 * dst_h + int64_t(oy) * d.ky, d.ky);
-            } else {
-                px = mid[idx];
-            }
-            block[(g0 + r) * kUnitPx + x] = px;
+        __syncthreads();
+        // horizontal pass: band rows r0 + 4 rq .. + 3 of the thread's column
+        // (rows past nr hold bytes of no weight: their source rows lie past
+        // every window)
+        uint8_t *bcol = band + (hx >> 2) * bgroup + (r0 >> 2) * 16 + (hx & 3) * 4;
+        const int groups = (nr + 3) >> 2;
+        switch (ndx) {
+        case 1: h_pass<1>(stage, sgroup, bcol, bgroup, groups, x0, xr, xrec, ndx, tid); break;
+        case 2: h_pass<2>(stage, sgroup, bcol, bgroup, groups, x0, xr, xrec, ndx, tid); break;
+        case 3: h_pass<3>(stage, sgroup, bcol, bgroup, groups, x0, xr, xrec, ndx, tid); break;
+        default: h_pass<0>(stage, sgroup, bcol, bgroup, groups, x0, xr, xrec, ndx, tid); break;
         }
         __syncthreads();
     }
-
-    // The group's G pixel rows x 2 patch columns x 3 channels x 4 quads of 4
-    // pixels; each thread stores one quad into both temporal slots, a wave
-    // one contiguous run of a (c, tt) plane.
-    for (int idx = tid; idx < G * 2 * 3 * 4; idx += kHfThreads) {
-        const int qd = idx & 3;
-        const int yl = (idx >> 2) & (G - 1);
-        const int mc = idx >> (2 + gsh);  // (mw, c): 0 .. 5
-        const int mw = mc >= 3 ? 1 : 0;
-        const int c = mc - 3 * mw;
-        const int y = g0 + yl;            // pixel row in the unit
-        const int mh = y >> 4, py = y & (kPatch - 1);
-        const int q = mh * kMerge + mw;   // row of the unit
-        const uint32_t *src_px = &block[y * kUnitPx + mw * kPatch + qd * 4];
-        float v[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = lut[c * 256 + ((src_px[j] >> (8 * c)) & 255u)];
-        const int64_t elem = int64_t(c) * (kTemporal * kPlane) + py * kPatch + qd * 4;
-        if (a.rows) {
-            const int64_t row = d.row_offset + int64_t(br * d.blocks_w + bc) * kRowsPerUnit + q;
-            store_pair<OutT>(static_cast<OutT *>(a.rows) + row * kRowLen + elem, v);
-        }
-        if (a.rows_col) {
-            const int64_t row = d.row_offset + int64_t(bc * d.blocks_h + br) * kRowsPerUnit + q;
-            store_pair<OutT>(static_cast<OutT *>(a.rows_col) + row * kRowLen + elem, v);
-        }
+    switch (ndy) {
+    case 1: v_pass<1>(band, bgroup, y0, lut, yr, yrec, ndy, n_items, gsh, tid, put); break;
+    case 2: v_pass<2>(band, bgroup, y0, lut, yr, yrec, ndy, n_items, gsh, tid, put); break;
+    case 3: v_pass<3>(band, bgroup, y0, lut, yr, yrec, ndy, n_items, gsh, tid, put); break;
+    default: v_pass<0>(band, bgroup, y0, lut, yr, yrec, ndy, n_items, gsh, tid, put); break;
     }
 }
 
@@ -391,13 +545,12 @@ struct AxisMap {
     }
 };
 
-// An axis table is first[n_out], count[n_out], weights[n_out][k].  Every
-// output gets the same k taps, the most any output of the axis has: its
-// window [first, first + k) is moved left where it would run past the last
-// input (its own taps then sit further right in the row), and the weights
-// it does not use are zero.  The kernel then runs one tap count for every
-// output and never reads outside the image; the sums are those of the
-// outputs' own taps, since the extra terms are zero.
+// Every output of an axis gets the same k taps, the most any output of the
+// axis has: its window [first, first + k) is moved left where it would run
+// past the last input (its own taps then sit further right in the window),
+// and the weights it does not use are zero.  The kernel then runs one window
+// length for every output of an axis and never reads outside the image; the
+// sums are those of the outputs' own taps, since the extra terms are zero.
 
 // k of an axis (at least 1, at most n_in).
 int axis_tap_count(int64_t n_in, int64_t n_out) {
@@ -412,24 +565,66 @@ int axis_tap_count(int64_t n_in, int64_t n_out) {
     return int(k);
 }
 
-// first and count of an axis table at tab (the cheap part: what the host's
-// band and staging sizes need).
+int axis_dwords(int k) { return (k + 3) / 4; }
+size_t axis_table_entries(int64_t n_out, int nd) { return size_t(n_out) * (1 + rec_dwords(nd)); }
+
+// first[] of an axis table at tab (the cheap part: what the host's band and
+// staging sizes need).  An axis of equal lengths is the identity: one tap.
 void fill_axis_heads(int64_t n_in, int64_t n_out, int k, int32_t *tab) {
+    if (n_in == n_out) {
+        for (int64_t i = 0; i < n_out; ++i) tab[i] = int32_t(i);
+        return;
+    }
     const AxisMap m(n_in, n_out);
     for (int64_t i = 0; i < n_out; ++i) {
         int64_t lo, hi;
         double centre;
         m.window(i, lo, hi, centre);
         tab[i] = int32_t(std::min<int64_t>(lo, n_in - k));
-        tab[n_out + i] = k;
     }
 }
 
-// The weights of an axis table at tab (zeroed by the caller), in float64
-// as PIL computes them, rounded half away from zero to kWeightBits.
-void fill_axis_weights(int64_t n_in, int64_t n_out, int k, int32_t *tab) {
+// One output's record from its k integer weights w (see rec_dwords), its
+// constant less `offset`: false if a weight has no three-digit form (|w|
+// beyond about 2^23, which normalised bicubic weights never reach).
+bool fill_record(const int32_t *w, int k, int nd, int32_t offset, int32_t *rec) {
+    int64_t sum = 0;
+    uint32_t planes[3][64] = {};
+    if (nd > 64) return false;
+    for (int t = 0; t < k; ++t) {
+        sum += w[t];
+        int64_t v = w[t];
+        for (int p = 0; p < 3; ++p) {
+            const int64_t digit = ((v + 128) & 255) - 128;  // in [-128, 127]
+            planes[p][t / 4] |= uint32_t(digit & 255) << (8 * (t % 4));
+            v = (v - digit) / 256;
+        }
+        if (v != 0) return false;
+    }
+    rec[0] = int32_t((int64_t(1) << (kWeightBits - 1)) + 128 * sum - offset);
+    for (int p = 0; p < 3; ++p)
+        for (int q = 0; q < nd; ++q) rec[1 + p * nd + q] = int32_t(planes[p][q]);
+    return true;
+}
+
+// The records of an axis table at tab (zeroed by the caller): the weights
+// in float64 as PIL computes them, rounded half away from zero to
+// kWeightBits, then split into digits.  A column table's constants are
+// 128 << kWeightBits lower: the horizontal pass saturates its sums to signed
+// bytes, which then come out as the PIL byte less 128, the vertical pass's
+// input form.
+bool fill_axis_records(int64_t n_in, int64_t n_out, int k, bool columns, int32_t *tab) {
+    const int32_t offset = columns ? int32_t(128) << kWeightBits : 0;
+    const int nd = axis_dwords(k);
+    int32_t *recs = tab + n_out;
+    std::vector<int32_t> wi(size_t(k), 0);
+    if (n_in == n_out) {
+        const int32_t one = 1 << kWeightBits;
+        for (int64_t i = 0; i < n_out; ++i)
+            if (!fill_record(&one, 1, nd, offset, recs + i * rec_dwords(nd))) return false;
+        return true;
+    }
     const AxisMap m(n_in, n_out);
-    int32_t *weight = tab + 2 * n_out;
     std::vector<double> w(size_t(k) + 1);
     for (int64_t i = 0; i < n_out; ++i) {
         int64_t lo, hi;
@@ -441,13 +636,16 @@ void fill_axis_weights(int64_t n_in, int64_t n_out, int k, int32_t *tab) {
             w[j] = keys_bicubic((double(j + lo) - centre + 0.5) / m.widen);
             sum += w[j];
         }
+        std::fill(wi.begin(), wi.end(), 0);
         const int64_t shift = lo - tab[i];
         for (int64_t j = 0; j < cnt; ++j) {
             const double v = sum != 0.0 ? w[j] / sum : w[j];
             const double fixed = v * double(1 << kWeightBits);
-            weight[i * k + shift + j] = int32_t(v < 0.0 ? fixed - 0.5 : fixed + 0.5);
+            wi[shift + j] = int32_t(v < 0.0 ? fixed - 0.5 : fixed + 0.5);
         }
+        if (!fill_record(wi.data(), k, nd, offset, recs + i * rec_dwords(nd))) return false;
     }
+    return true;
 }
 
 struct HfTables {
@@ -455,31 +653,25 @@ struct HfTables {
     std::vector<int32_t> taps;
     int64_t tiles = 0;
     int64_t rows = 0;
-    // dynamic LDS the batch needs (dwords, multiples of 4; see HfArgs)
-    int32_t xw_budget = 0, yw_budget = 0, mid_rows = 0, stage_dwords = 0;
-    int32_t max_taps = 0;  // the most taps per output over the batch's resized axes
+    int32_t band_bytes = 0, stage_bytes = 0;  // dynamic LDS the batch needs (see HfArgs)
     size_t lds_bytes() const {
-        return 4 * (size_t(kFixedDwords) + xw_budget + yw_budget + size_t(mid_rows) * kUnitPx + stage_dwords);
+        return size_t(kLutBytes) + std::max<size_t>(kBlockBytes, size_t(band_bytes) + size_t(stage_bytes));
     }
 };
 
-int32_t round4(int64_t v) { return int32_t((v + 3) & ~int64_t(3)); }
-
-// The most source rows one group of g output rows reads.
-int band_rows(const int32_t *yfirst, const int32_t *ycount, int dst_h, int g) {
+// The most source rows one group of g output rows reads (the band the
+// kernel forms: 4 nd rows past the group's last first row).
+int band_rows(const int32_t *yfirst, int nd, int dst_h, int g) {
     int most = 0;
-    for (int y0 = 0; y0 < dst_h; y0 += g) {
-        const int y1 = y0 + g - 1;
-        most = std::max(most, yfirst[y1] + ycount[y1] - yfirst[y0]);
-    }
+    for (int y0 = 0; y0 < dst_h; y0 += g) most = std::max(most, yfirst[y0 + g - 1] + 4 * nd - yfirst[y0]);
     return most;
 }
 
 // Output rows per vertical group so that the band of source rows one group
-// needs fits kMidRows: the largest of 32, 16, ..., 1 that fits everywhere.
-int choose_group(const int32_t *yfirst, const int32_t *ycount, int dst_h) {
+// needs fits kMaxBandRows: the largest of 32, 16, ..., 1 that fits everywhere.
+int choose_group(const int32_t *yfirst, int nd, int dst_h) {
     for (int g = kUnitPx; g >= 1; g >>= 1)
-        if (band_rows(yfirst, ycount, dst_h, g) <= kMidRows) return g;
+        if (band_rows(yfirst, nd, dst_h, g) <= kMaxBandRows) return g;
     return 0;
 }
 
@@ -497,24 +689,26 @@ int build_hf_tables(int32_t n, const mimo_image_desc *desc, const float *mean01,
             lut[c * 256 + v] = (x - mean01[c]) / std01[c];
         }
     int64_t tiles = 0, rows = 0;
-    // One tap table per (input length, output length) pair in the batch:
+    // One tap table per (input length, output length, axis) in the batch:
     // items of the same size share it (built and uploaded once).  Its first
-    // and count entries are filled here; the weights, the costly part, after
-    // the loop, several tables at a time.
-    std::map<std::pair<int32_t, int32_t>, std::pair<int64_t, int32_t>> tables;
-    auto axis_table = [&](int32_t n_in, int32_t n_out, int64_t &tab, int32_t &k) {
-        const auto key = std::make_pair(n_in, n_out);
+    // entries are filled here; the records, the costly part, after the
+    // loop, several tables at a time.
+    std::map<std::tuple<int32_t, int32_t, bool>, std::pair<int64_t, int32_t>> tables;
+    auto axis_table = [&](int32_t n_in, int32_t n_out, bool columns, int64_t &tab, int32_t &nd) {
+        const auto key = std::make_tuple(n_in, n_out, columns);
         const auto it = tables.find(key);
-        if (it != tables.end()) {
+        if (it == tables.end()) {
+            const int k = n_in == n_out ? 1 : axis_tap_count(n_in, n_out);
+            const int64_t at = int64_t(out.taps.size());
+            out.taps.resize(out.taps.size() + axis_table_entries(n_out, axis_dwords(k)), 0);
+            fill_axis_heads(n_in, n_out, k, out.taps.data() + at);
+            tables.emplace(key, std::make_pair(at, k));
+            tab = at;
+            nd = axis_dwords(k);
+        } else {
             tab = it->second.first;
-            k = it->second.second;
-            return;
+            nd = axis_dwords(it->second.second);
         }
-        k = axis_tap_count(n_in, n_out);
-        tab = int64_t(out.taps.size());
-        out.taps.resize(out.taps.size() + size_t(n_out) * (2 + k), 0);
-        fill_axis_heads(n_in, n_out, k, out.taps.data() + tab);
-        tables.emplace(key, std::make_pair(tab, k));
     };
     for (int32_t i = 0; i < n; ++i) {
         const mimo_image_desc &s = desc[i];
@@ -525,6 +719,7 @@ int build_hf_tables(int32_t n, const mimo_image_desc *desc, const float *mean01,
         d.src_offset = s.src_offset;
         d.row_offset = rows;
         d.blocks_w = 1;
+        d.group = kUnitPx;
         if (s.status != MIMO_OK || s.rows == 0) {
             items[i] = d;
             continue;
@@ -535,52 +730,41 @@ int build_hf_tables(int32_t n, const mimo_image_desc *desc, const float *mean01,
             s.rows != int64_t(s.grid_h) * s.grid_w || s.row_offset != rows || s.src_offset < 0)
             return set_error(MIMO_E_INVALID, "preprocess_hf: descriptor " + std::to_string(i) +
                                                  " is not a still-image plan of the 16/2/2 kernels");
-        // the staging window addresses up to kMidRows source rows with 32-bit offsets
+        // the staging window addresses a band of source rows (and a few past
+        // it) with 32-bit offsets
         if (s.src_h > kMaxSide || s.src_w > kMaxSide || s.dst_h > kMaxSide || s.dst_w > kMaxSide ||
-            int64_t(s.src_w) * s.channels * (kMidRows + 1) >= 0x7FFFFFF0ll)
+            int64_t(s.src_w) * s.channels * (kMaxBandRows + 2) >= 0x7FFFFFF0ll)
             return set_error(MIMO_E_TOO_LARGE, "preprocess_hf: descriptor " + std::to_string(i) + ": side too large");
         d.src_h = s.src_h;
         d.src_w = s.src_w;
         d.channels = s.channels;
         d.blocks_h = s.dst_h / kUnitPx;
         d.blocks_w = s.dst_w / kUnitPx;
-        d.group = kUnitPx;
-        if (s.dst_w != s.src_w) axis_table(s.src_w, s.dst_w, d.x_tab, d.kx);
-        if (s.dst_h != s.src_h) {
-            axis_table(s.src_h, s.dst_h, d.y_tab, d.ky);
+        if (s.dst_w != s.src_w || s.dst_h != s.src_h) {
+            // both axes get a table (an axis that keeps its length: one tap of weight 1)
+            axis_table(s.src_w, s.dst_w, true, d.x_tab, d.ndx);
+            axis_table(s.src_h, s.dst_h, false, d.y_tab, d.ndy);
+            const int32_t *xfirst = out.taps.data() + d.x_tab;
             const int32_t *yfirst = out.taps.data() + d.y_tab;
-            d.group = choose_group(yfirst, yfirst + s.dst_h, s.dst_h);
+            d.group = choose_group(yfirst, d.ndy, s.dst_h);
             if (d.group == 0)
                 return set_error(MIMO_E_UNSUPPORTED, "preprocess_hf: descriptor " + std::to_string(i) +
                                                          ": vertical downscale beyond the kernel's band");
-        }
-        int spitch = kUnitPx;  // staged pixels per source row (whole quads)
-        if (d.kx) {
             // the widest source block one tile's 32 output columns read
-            const int32_t *xfirst = out.taps.data() + d.x_tab;
-            const int32_t *xcount = xfirst + s.dst_w;
-            for (int32_t x0 = 0; x0 < s.dst_w; x0 += kUnitPx) {
-                const int32_t x1 = x0 + kUnitPx - 1;
-                spitch = std::max(spitch, round4(xfirst[x1] + xcount[x1] - xfirst[x0]));
-            }
-            if (spitch > kStageDwords)
+            int spitch = 0;  // bytes per staged row and channel
+            for (int32_t x0 = 0; x0 < s.dst_w; x0 += kUnitPx)
+                spitch = std::max(spitch, 4 * stage_pitch(xfirst[x0 + kUnitPx - 1] + 4 * d.ndx - xfirst[x0]));
+            if (spitch > kMaxStagePitch)
                 return set_error(MIMO_E_UNSUPPORTED, "preprocess_hf: descriptor " + std::to_string(i) +
                                                          ": horizontal downscale beyond the kernel's staging");
-            if (kUnitPx * d.kx <= kTapBudget) out.xw_budget = std::max(out.xw_budget, round4(kUnitPx * d.kx));
-        }
-        if (d.kx || d.ky) {
-            // band rows of one group, and staging for all of them at once when that fits
-            const int nrows = d.ky ? band_rows(out.taps.data() + d.y_tab, out.taps.data() + d.y_tab + s.dst_h,
-                                               s.dst_h, d.group)
-                                   : d.group;
-            out.mid_rows = std::max(out.mid_rows, round4(nrows));
-            out.stage_dwords = std::max<int32_t>(
-                out.stage_dwords, int32_t(std::min<int64_t>(kStageDwords, int64_t(nrows) * spitch)));
-            if (d.ky && d.group * d.ky <= kTapBudget)
-                out.yw_budget = std::max(out.yw_budget, round4(d.group * d.ky));
+            const int nrows = band_rows(yfirst, d.ndy, s.dst_h, d.group);
+            out.band_bytes = std::max(out.band_bytes, 3 * kUnitPx * 4 * band_pitch(nrows));
+            // a chunk of staged rows: all of them when that fits, else whole
+            // quarters of kMaxStageBytes' worth (at least 4 rows)
+            const int chunk = std::min((nrows + 3) & ~3, (kMaxStageBytes / (3 * spitch)) & ~3);
+            out.stage_bytes = std::max(out.stage_bytes, 3 * chunk * spitch);
         }
         items[i] = d;
-        out.max_taps = std::max(out.max_taps, std::max(d.kx, d.ky));
         tiles += int64_t(d.blocks_h) * d.blocks_w * (kUnitPx / d.group);
         rows += s.rows;
     }
@@ -589,21 +773,26 @@ int build_hf_tables(int32_t n, const mimo_image_desc *desc, const float *mean01,
     out.rows = rows;
     if (out.taps.size() > size_t(0x7FFFFFFF))
         return set_error(MIMO_E_TOO_LARGE, "preprocess_hf: tap tables above 2^31 entries");
-    // the weights: tables are independent, so large batches of them are
+    // the records: tables are independent, so large batches of them are
     // shared out over up to 16 host threads
     struct Job {
         int32_t n_in, n_out, k;
+        bool columns;
         int64_t tab;
     };
     std::vector<Job> jobs;
     int64_t work = 0;
     for (const auto &t : tables) {
-        jobs.push_back({t.first.first, t.first.second, t.second.second, t.second.first});
-        work += int64_t(t.first.second) * t.second.second;
+        jobs.push_back({std::get<0>(t.first), std::get<1>(t.first), t.second.second, std::get<2>(t.first),
+                        t.second.first});
+        work += int64_t(std::get<1>(t.first)) * t.second.second;
     }
+    std::atomic<bool> ok{true};
     auto run = [&](size_t from, size_t step) {
         for (size_t j = from; j < jobs.size(); j += step)
-            fill_axis_weights(jobs[j].n_in, jobs[j].n_out, jobs[j].k, out.taps.data() + jobs[j].tab);
+            if (!fill_axis_records(jobs[j].n_in, jobs[j].n_out, jobs[j].k, jobs[j].columns,
+                                   out.taps.data() + jobs[j].tab))
+                ok.store(false);
     };
     const size_t threads =
         std::min<size_t>({size_t(16), jobs.size(), size_t(std::max(1u, std::thread::hardware_concurrency()))});
@@ -615,6 +804,7 @@ int build_hf_tables(int32_t n, const mimo_image_desc *desc, const float *mean01,
         run(0, threads);
         for (auto &th : pool) th.join();
     }
+    if (!ok.load()) return set_error(MIMO_E_UNSUPPORTED, "preprocess_hf: a resampling weight out of range");
     return MIMO_OK;
 }
 
@@ -631,10 +821,11 @@ size_t mimo_hf_workspace_bytes(int32_t n, const mimo_image_desc *desc) {
     for (int32_t i = 0; i < n; ++i) {
         const mimo_image_desc &s = desc[i];
         if (s.status != MIMO_OK || s.rows == 0 || s.dst_w < 1 || s.dst_h < 1) continue;
-        if (s.dst_w != s.src_w)
-            entries += size_t(s.dst_w) * (2 + axis_taps_per_output(s.src_w, s.dst_w));
-        if (s.dst_h != s.src_h)
-            entries += size_t(s.dst_h) * (2 + axis_taps_per_output(s.src_h, s.dst_h));
+        if (s.dst_w == s.src_w && s.dst_h == s.src_h) continue;
+        // at most: each axis its own table, k bounded by the support
+        const int kx = s.dst_w != s.src_w ? axis_taps_per_output(s.src_w, s.dst_w) : 1;
+        const int ky = s.dst_h != s.src_h ? axis_taps_per_output(s.src_h, s.dst_h) : 1;
+        entries += axis_table_entries(s.dst_w, axis_dwords(kx)) + axis_table_entries(s.dst_h, axis_dwords(ky));
     }
     return hf_items_bytes(n) + hf_prefix_bytes(n) + align256(kLutBytes) +
            align256(std::max<size_t>(entries, 1) * sizeof(int32_t));
@@ -695,31 +886,21 @@ int mimo_preprocess_hf_batch(int32_t n, const mimo_image_desc *desc, const uint8
     a.rows = rows;
     a.rows_col = rows_col;
     a.n = n;
-    a.xw_budget = t.xw_budget;
-    a.yw_budget = t.yw_budget;
-    a.mid_rows = t.mid_rows;
-    a.stage_dwords = t.stage_dwords;
+    a.band_bytes = t.band_bytes;
+    a.stage_bytes = t.stage_bytes;
     const size_t lds = t.lds_bytes();
-    const bool narrow = t.max_taps >= 1 && t.max_taps <= kNarrowMaxTaps && t.tiles >= kNarrowMinTiles;
     const bool f32 = out_dtype == MIMO_F32;
-    const void *kernel =
-        narrow ? (f32 ? reinterpret_cast<const void *>(hf_preprocess_kernel<float, kHfThreadsNarrow>)
-                      : reinterpret_cast<const void *>(hf_preprocess_kernel<uint16_t, kHfThreadsNarrow>))
-               : (f32 ? reinterpret_cast<const void *>(hf_preprocess_kernel<float, kHfThreadsWide>)
-                      : reinterpret_cast<const void *>(hf_preprocess_kernel<uint16_t, kHfThreadsWide>));
+    const void *kernel = f32 ? reinterpret_cast<const void *>(hf_preprocess_kernel<float>)
+                             : reinterpret_cast<const void *>(hf_preprocess_kernel<uint16_t>);
     e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return hip_error(e, "preprocess_hf: LDS size");
     const dim3 grid{unsigned(t.tiles), 1, 1};
-    const dim3 block{unsigned(narrow ? kHfThreadsNarrow : kHfThreadsWide), 1, 1};
+    const dim3 block{unsigned(kHfThreads), 1, 1};
     e = timed_launch(s, [&] {
-        if (narrow && f32)
-            hipLaunchKernelGGL((hf_preprocess_kernel<float, kHfThreadsNarrow>), grid, block, lds, s, a);
-        else if (narrow)
-            hipLaunchKernelGGL((hf_preprocess_kernel<uint16_t, kHfThreadsNarrow>), grid, block, lds, s, a);
-        else if (f32)
-            hipLaunchKernelGGL((hf_preprocess_kernel<float, kHfThreadsWide>), grid, block, lds, s, a);
+        if (f32)
+            hipLaunchKernelGGL((hf_preprocess_kernel<float>), grid, block, lds, s, a);
         else
-            hipLaunchKernelGGL((hf_preprocess_kernel<uint16_t, kHfThreadsWide>), grid, block, lds, s, a);
+            hipLaunchKernelGGL((hf_preprocess_kernel<uint16_t>), grid, block, lds, s, a);
     });
     if (e != hipSuccess) return hip_error(e, "preprocess_hf: kernel launch");
     g_dispatches.fetch_add(1);
