@@ -68,8 +68,9 @@ constexpr int kWeightBits = 22;              // fractional bits of the resampler
 constexpr int kMaxBandRows = 256;            // most source rows one group's vertical taps read
 constexpr int kMaxStageBytes = 48 * 1024;    // LDS for one staged row chunk (three planes)
 constexpr int kMaxStagePitch = kMaxStageBytes / 12;  // bytes per staged plane row (>= 4 rows a chunk)
-constexpr int kRegDwords = 3;                // windows of up to 12 taps keep their record in registers
+constexpr int kRegDwords = 3;                // windows of up to 12 taps keep their tile's records in LDS
 constexpr int kRegRecord = 4 * kRegDwords;   // (the record of such a window: 12 dwords at most)
+constexpr int kRecBytes = 2 * kUnitPx * kRegRecord * 4;  // a tile's column and row records
 constexpr int kStageBatch = 4;                // staging loads a thread issues before using them
 constexpr int kLutBytes = 3 * 256 * 4;
 constexpr int kBlockBytes = kUnitPx * kUnitPx * 4;  // the direct path's unit block (RGB per dword)
@@ -184,18 +185,12 @@ __device__ __forceinline__ void quad_planes(const uint32_t (&u)[4], int channels
     for (int c = 0; c < 3; ++c) p[c] ^= 0x80808080u;
 }
 
-// A window's record (rec_dwords(nd) <= kRegRecord dwords) into registers.
-__device__ __forceinline__ void load_record(const int32_t *rec, int nd, uint32_t (&r)[kRegRecord]) {
+// A window's record (rec_dwords(nd) <= kRegRecord dwords) copied to LDS.
+__device__ __forceinline__ void copy_record(const int32_t *rec, int nd, uint32_t *dst) {
     const int vecs = rec_dwords(nd) >> 2;
 #pragma unroll
-    for (int v = 0; v < kRegDwords; ++v) {
-        u32x4 q = {0u, 0u, 0u, 0u};
-        if (v < vecs) q = *reinterpret_cast<const u32x4 *>(rec + 4 * v);
-        r[4 * v] = q.x;
-        r[4 * v + 1] = q.y;
-        r[4 * v + 2] = q.z;
-        r[4 * v + 3] = q.w;
-    }
+    for (int v = 0; v < kRegDwords; ++v)
+        if (v < vecs) reinterpret_cast<u32x4 *>(dst)[v] = *reinterpret_cast<const u32x4 *>(rec + 4 * v);
 }
 
 // sum over four taps of x * w (signed bytes) plus acc: v_dot4_i32_i8.
@@ -236,7 +231,7 @@ __device__ __forceinline__ uint32_t join_pairs(uint32_t lo, uint32_t hi) {
 // into the next one's addend: s = ((sum c << 8) + sum b) << 8) + sum a + K,
 // which saves setting up two of the three accumulators.
 template <int ND>
-__device__ __forceinline__ void quad_sums(const uint8_t *p, uint32_t sh, const uint32_t (&r)[kRegRecord],
+__device__ __forceinline__ void quad_sums(const uint8_t *p, uint32_t sh, const uint32_t *r,
                                           int32_t (&s)[4]) {
     u32x4 g[ND + 1];
 #pragma unroll
@@ -284,7 +279,7 @@ __device__ __forceinline__ void quad_sums_any(const uint8_t *p, uint32_t sh, con
 }
 
 template <int ND>
-__device__ __forceinline__ void window_sums(const uint8_t *p, uint32_t sh, const uint32_t (&r)[kRegRecord],
+__device__ __forceinline__ void window_sums(const uint8_t *p, uint32_t sh, const uint32_t *r,
                                             const int32_t *rec, int nd, int32_t (&s)[4]) {
     if (ND)
         quad_sums<ND ? ND : 1>(p, sh, r, s);
@@ -299,7 +294,7 @@ __device__ __forceinline__ void window_sums(const uint8_t *p, uint32_t sh, const
 // as one dword.
 template <int ND>
 __device__ __forceinline__ void h_pass(const uint8_t *stage, int sgroup, uint8_t *bcol, int bgroup, int groups,
-                                       int x0, const uint32_t (&r)[kRegRecord], const int32_t *rec, int nd,
+                                       int x0, const uint32_t *r, const int32_t *rec, int nd,
                                        int tid) {
     for (int rq = tid >> 5; rq < groups; rq += kHfThreads / kUnitPx) {
         const uint8_t *src = stage + rq * 3 * sgroup + (x0 >> 2) * 16;
@@ -318,7 +313,7 @@ __device__ __forceinline__ void h_pass(const uint8_t *stage, int sgroup, uint8_t
 // bytes through the rescale-and-normalise table, handed to put.
 template <int ND, typename Put>
 __device__ __forceinline__ void v_pass(const uint8_t *band, int bgroup, int y0, const float *lut,
-                                       const uint32_t (&r)[kRegRecord], const int32_t *rec, int nd, int n_items,
+                                       const uint32_t *r, const int32_t *rec, int nd, int n_items,
                                        int gsh, int tid, Put &&put) {
     for (int idx = tid; idx < n_items; idx += kHfThreads) {
         const int qd = idx & 3;
@@ -357,11 +352,15 @@ __device__ __forceinline__ void store_pair<uint16_t>(uint16_t *p, const float (&
     __builtin_nontemporal_store(q, reinterpret_cast<u32x2 *>(p + kPlane));
 }
 
+// Six waves per SIMD: a 6000x4000 batch's tile takes about 26 KB of LDS,
+// so six workgroups fill a CU; the register budget that leaves (80) holds
+// the kernel without spilling.
 template <typename OutT>
-__global__ __launch_bounds__(kHfThreads) void hf_preprocess_kernel(HfArgs a) {
+__global__ __launch_bounds__(kHfThreads) __attribute__((amdgpu_waves_per_eu(6))) void hf_preprocess_kernel(HfArgs a) {
     extern __shared__ uint32_t lds[];
     float *lut = reinterpret_cast<float *>(lds);  // [3][256]
-    uint8_t *region = reinterpret_cast<uint8_t *>(lds) + kLutBytes;
+    uint32_t *recs = lds + kLutBytes / 4;  // [column records x 32][row records x 32], kRegRecord dwords each
+    uint8_t *region = reinterpret_cast<uint8_t *>(lds) + kLutBytes + kRecBytes;
     const int64_t tile = xcd_contiguous_tile(blockIdx.x, gridDim.x);
     const int img = find_segment(a.tile_begin, a.n, tile);
     const HfItem d = a.items[img];
@@ -435,9 +434,16 @@ __global__ __launch_bounds__(kHfThreads) void hf_preprocess_kernel(HfArgs a) {
     const int oy_a = oy0 + g0;
     const int32_t *xrec = xt + dst_w + int64_t(ox0 + hx) * rec_dwords(ndx);
     const int32_t *yrec = yt + dst_h + int64_t(oy_a + yl) * rec_dwords(ndy);
-    uint32_t xr[kRegRecord], yr[kRegRecord];
-    if (ndx <= kRegDwords) load_record(xrec, ndx, xr);
-    if (ndy <= kRegDwords) load_record(yrec, ndy, yr);
+    // the tile's records (windows of up to 12 taps) into LDS: 32 columns, G rows
+    const uint32_t *xr = recs + hx * kRegRecord;
+    const uint32_t *yr = recs + (kUnitPx + yl) * kRegRecord;
+    if (tid < kUnitPx) {
+        if (ndx <= kRegDwords) copy_record(xt + dst_w + int64_t(ox0 + tid) * rec_dwords(ndx), ndx, recs + tid * kRegRecord);
+    } else if (tid < kUnitPx + G) {
+        const int i = tid - kUnitPx;
+        if (ndy <= kRegDwords)
+            copy_record(yt + dst_h + int64_t(oy_a + i) * rec_dwords(ndy), ndy, recs + (kUnitPx + i) * kRegRecord);
+    }
     for (int i = tid; i < 3 * 256; i += kHfThreads) lut[i] = a.lut[i];
     // the tile's source block: columns [xlo, xlo + xspan), rows [ylo, ylo + nrows)
     // (4 nd inputs past each axis's last first input; bytes past an output's
@@ -655,7 +661,7 @@ struct HfTables {
     int64_t rows = 0;
     int32_t band_bytes = 0, stage_bytes = 0;  // dynamic LDS the batch needs (see HfArgs)
     size_t lds_bytes() const {
-        return size_t(kLutBytes) + std::max<size_t>(kBlockBytes, size_t(band_bytes) + size_t(stage_bytes));
+        return size_t(kLutBytes) + kRecBytes + std::max<size_t>(kBlockBytes, size_t(band_bytes) + size_t(stage_bytes));
     }
 };
 
