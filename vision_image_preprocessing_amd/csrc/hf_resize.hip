@@ -352,10 +352,242 @@ __device__ __forceinline__ void store_pair<uint16_t>(uint16_t *p, const float (&
     __builtin_nontemporal_store(q, reinterpret_cast<u32x2 *>(p + kPlane));
 }
 
-// Six waves per SIMD: a 6000x4000 batch's tile takes about 26 KB of LDS,
-// so six workgroups fill a CU; the register budget that leaves (80) holds
-// the kernel without spilling.
+// ---- the matrix-core instance -------------------------------------------
+//
+// Both passes of one tile are integer matrix products with banded weight
+// matrices: band[r][x] = sum_k stage[r][k] Wx[k][x] (r a band row, k a staged
+// source column, x an output column), then out[y][x] = sum_r Wy[y][r]
+// band[r][x].  When every tile of a batch reads at most 64 source columns
+// and 64 band rows with windows of at most 12 taps (downscales up to about
+// 1.8x, and upscales), each 16 x 16 block of either product is one
+// v_mfma_i32_16x16x64_i8 per weight digit plane: exact int32 sums of
+// signed-byte products, chained through the accumulator as in the dot
+// products above.  A tile's banded matrices are built in LDS (zero but for
+// each output's own taps) as 64-byte lines, which the matrix cores read as
+// 16-byte fragments: lane l reads line l % 16, bytes 16 (l / 16) .. + 15,
+// and holds result rows 4 (l / 16) .. + 3 of column l % 16.
+constexpr int kMfmaSpan = 64;  // the K of one instruction: staged columns, band rows
+constexpr int kMfMaxNd = 3;    // window dwords (12 taps) the instance takes
+// LDS while the horizontal pass runs: [stage][band][Wx][Kx] ...
+constexpr int kMfStage = 0;                              // [channel][64 rows][64 bytes]
+constexpr int kMfBand = kMfStage + 3 * kMfmaSpan * 64;   // [channel][32 columns][64 rows]
+constexpr int kMfWx = kMfBand + 3 * kUnitPx * 64;        // [digit plane][32 output columns][64]
+constexpr int kMfKx = kMfWx + 3 * kUnitPx * 64;          // int32 [32] record constants
+constexpr int kMfLdsBytes = kMfKx + kUnitPx * 4;
+// ... and for the vertical pass the stage's bytes hold the table, Wy and Ky
+// (24 KB in all: six workgroups fit a CU)
+constexpr int kMfLut = kMfStage;                         // float [3][256]
+constexpr int kMfWy = kMfLut + kLutBytes;                // [digit plane][32 output rows][64]
+constexpr int kMfKy = kMfWy + 3 * kUnitPx * 64;          // int32 [32]
+static_assert(kMfKy + kUnitPx * 4 <= kMfBand, "the vertical pass's tables fit the stage's bytes");
+
+typedef int32_t i32x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4v lds_frag(const uint8_t *p) {
+    return __builtin_bit_cast(i32x4v, *reinterpret_cast<const u32x4 *>(p));
+}
+
+// acc = A x (c, b, a digit planes of B), chained: ((A Bc << 8) + A Bb) << 8
+// + A Ba + K; K per column of the result (lane l's column l % 16).  K is
+// added last, by an ordinary VALU instruction: the packing instructions
+// that read the result are inline assembly, which the compiler cannot
+// space from a matrix-core write, but it does space this add.
+__device__ __forceinline__ i32x4v digit_product(i32x4v a, i32x4v bc, i32x4v bb, i32x4v ba, int32_t k) {
+    i32x4v acc = {0, 0, 0, 0};
+    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bc, acc, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = int32_t(uint32_t(acc[i]) << 8);
+    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bb, acc, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = int32_t(uint32_t(acc[i]) << 8);
+    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, ba, acc, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = int32_t(uint32_t(acc[i]) + uint32_t(k));
+    return acc;
+}
+
+// The digit plane p of a record (nd <= kMfMaxNd dwords), into registers.
+__device__ __forceinline__ void load_digits(const int32_t *rec, int nd, int p, uint32_t (&dg)[kMfMaxNd]) {
+#pragma unroll
+    for (int q = 0; q < kMfMaxNd; ++q) dg[q] = q < nd ? uint32_t(rec[1 + p * nd + q]) : 0u;
+}
+
+// Line i of a banded weight matrix (64 bytes): the digits dg placed at byte
+// o, zero elsewhere.  The line is zeroed 16 bytes at a time, each group of 4
+// lines starting at its own chunk: lines are 64 bytes apart, so lanes
+// writing the same chunk of lines 4 apart would share banks.
+__device__ __forceinline__ void write_line(uint8_t *line, int i, const uint32_t (&dg)[kMfMaxNd], int nd, int o) {
+    const int rot = (i >> 2) & 3;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4 *>(line + 16 * ((k + rot) & 3)) = u32x4{0u, 0u, 0u, 0u};
+    const int a = o >> 2, sh = o & 3;
+    uint32_t *w = reinterpret_cast<uint32_t *>(line) + a;
+    uint32_t prev = 0;
+#pragma unroll
+    for (int q = 0; q <= kMfMaxNd; ++q) {
+        const uint32_t cur = q < kMfMaxNd && q < nd ? dg[q] : 0u;
+        // bytes 4 (a + q) .. + 3 of the line: the tail of dword q - 1 and the head of dword q
+        const uint32_t val = sh ? __builtin_amdgcn_alignbyte(cur, prev, uint32_t(4 - sh)) : cur;
+        if (q <= nd && a + q < kMfmaSpan / 4) w[q] = val;
+        prev = cur;
+    }
+}
+
 template <typename OutT>
+__device__ __forceinline__ void resize_mfma(const HfArgs &a, const HfItem &d, int br, int bc, int tid,
+                                            uint8_t *lds8) {
+    const int dst_w = d.blocks_w * kUnitPx, dst_h = d.blocks_h * kUnitPx;
+    const int32_t *xt = a.taps + d.x_tab;
+    const int32_t *yt = a.taps + d.y_tab;
+    const int ndx = d.ndx, ndy = d.ndy;
+    const int oy0 = br * kUnitPx, ox0 = bc * kUnitPx;
+    const int xlo = xt[ox0], ylo = yt[oy0];
+    const int nrows = yt[oy0 + kUnitPx - 1] - ylo + 4 * ndy;  // <= 64 (the host checked), so are the columns
+    const int C = d.channels;
+    const uint32_t row_bytes = uint32_t(d.src_w) * uint32_t(C);
+
+    // Wx (96 lines: digit plane, output column) and Kx now; the vertical
+    // pass's lines, constants and table are read now and written after the
+    // horizontal pass, into the stage's bytes
+    const bool xline = tid < 3 * kUnitPx;
+    const bool yline = !xline && tid < 2 * 3 * kUnitPx;
+    const int lp = (xline ? tid : tid - 3 * kUnitPx) >> 5, li = tid & (kUnitPx - 1);
+    uint32_t dg[kMfMaxNd];
+    int lo = 0, lk = 0;
+    if (xline || yline) {
+        const int32_t *rec = xline ? xt + dst_w + int64_t(ox0 + li) * rec_dwords(ndx)
+                                   : yt + dst_h + int64_t(oy0 + li) * rec_dwords(ndy);
+        load_digits(rec, xline ? ndx : ndy, lp, dg);
+        lo = xline ? xt[ox0 + li] - xlo : yt[oy0 + li] - ylo;
+        lk = rec[0];
+    }
+    float lut_v[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) lut_v[i] = a.lut[tid + i * kHfThreads];
+    if (xline) {
+        write_line(lds8 + kMfWx + (lp * kUnitPx + li) * 64, li, dg, ndx, lo);
+        if (lp == 0) reinterpret_cast<int32_t *>(lds8 + kMfKx)[li] = lk;
+    }
+    // staged source rows [ylo, ylo + nrows) x columns [xlo, xlo + 64), as
+    // channel planes of signed bytes (columns past the tile's span, and
+    // rows past nrows, meet only zero weights)
+    {
+        const SrcWindow win = src_window(a, reinterpret_cast<uint64_t>(a.src + d.src_offset) +
+                                                uint64_t(int64_t(ylo) * row_bytes + int64_t(xlo) * C));
+        const int total = nrows * (kMfmaSpan / 4);
+        for (int base = tid; base < total; base += kStageBatch * kHfThreads) {
+            uint32_t u[kStageBatch][4];
+#pragma unroll
+            for (int k = 0; k < kStageBatch; ++k) {
+                const uint32_t idx = uint32_t(base + k * kHfThreads);
+                load_quad_bytes(win, win.lead + __umul24(idx >> 4, row_bytes) + (idx & 15u) * uint32_t(4 * C), C, u[k]);
+            }
+#pragma unroll
+            for (int k = 0; k < kStageBatch; ++k) {
+                const int idx = base + k * kHfThreads;
+                if (idx < total) {
+                    uint32_t pl[3];
+                    quad_planes(u[k], C, pl);
+#pragma unroll
+                    for (int c = 0; c < 3; ++c)
+                        *reinterpret_cast<uint32_t *>(lds8 + kMfStage + c * kMfmaSpan * 64 + idx * 4) = pl[c];
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lrow = lane & 15, lkb = (lane >> 4) * 16;  // the lane's fragment line and bytes
+    // The band's 64-byte lines (one per channel and output column) keep
+    // their four 16-byte chunks XOR-swizzled by bits 2-3 of the line: the
+    // horizontal pass's dword writes then fall into distinct banks, and a
+    // 16-byte read stays aligned.  (Lines of a 16-line block share those
+    // bits with lrow.)
+    const int swz = (lrow >> 2) & 3;
+    // horizontal pass: blocks (channel, 16 band rows, 16 output columns),
+    // two per step so that their matrix-core chains overlap
+    const int rblocks = (nrows + 15) >> 4;  // 1 .. 4
+    const int nblk = 3 * rblocks * 2;
+    const int inv_rblocks = (256 + rblocks - 1) / rblocks;  // t / rblocks = (t * inv) >> 8 for t < 12
+    const int32_t *kx = reinterpret_cast<const int32_t *>(lds8 + kMfKx);
+    auto h_block = [&](int blk) {
+        const int t = blk >> 1;
+        const int c = (t * inv_rblocks) >> 8;
+        const int cb = blk & 1, rb = t - c * rblocks;
+        const i32x4v av = lds_frag(lds8 + kMfStage + (c * kMfmaSpan + rb * 16 + lrow) * 64 + lkb);
+        const uint8_t *wl = lds8 + kMfWx + (cb * 16 + lrow) * 64 + lkb;
+        return digit_product(av, lds_frag(wl + 2 * kUnitPx * 64), lds_frag(wl + kUnitPx * 64), lds_frag(wl),
+                             kx[cb * 16 + lrow]);
+    };
+    auto h_store = [&](int blk, const i32x4v &acc) {
+        const int t = blk >> 1;
+        const int c = (t * inv_rblocks) >> 8;
+        const int cb = blk & 1, rb = t - c * rblocks;
+        // rows 4 (lane / 16) .. + 3 of column cb * 16 + lrow, as signed bytes
+        *reinterpret_cast<uint32_t *>(lds8 + kMfBand + (c * kUnitPx + cb * 16 + lrow) * 64 + 16 * (rb ^ swz) +
+                                      lkb / 4) = join_pairs(shift_pack_i8(acc[0], acc[1]), shift_pack_i8(acc[2], acc[3]));
+    };
+    for (int blk = wave; blk < nblk; blk += 2 * (kHfThreads / 64)) {
+        const int blk2 = blk + kHfThreads / 64;
+        const i32x4v acc = h_block(blk);
+        const i32x4v acc2 = h_block(min(blk2, nblk - 1));
+        h_store(blk, acc);
+        if (blk2 < nblk) h_store(blk2, acc2);
+    }
+    __syncthreads();
+
+    // the vertical pass's table, Wy and Ky, into the stage's bytes
+#pragma unroll
+    for (int i = 0; i < 3; ++i) reinterpret_cast<float *>(lds8 + kMfLut)[tid + i * kHfThreads] = lut_v[i];
+    if (yline) {
+        write_line(lds8 + kMfWy + (lp * kUnitPx + li) * 64, li, dg, ndy, lo);
+        if (lp == 0) reinterpret_cast<int32_t *>(lds8 + kMfKy)[li] = lk;
+    }
+    __syncthreads();
+
+    // vertical pass, transposed: out^T[x][y] = sum_r band^T[x][r] Wy^T[r][y],
+    // blocks (channel, 16 output columns, 16 output rows), three per wave;
+    // lane l holds output columns 4 (l / 16) .. + 3 of row l % 16: four
+    // pixels of a patch row
+    const float *lut = reinterpret_cast<const float *>(lds8 + kMfLut);
+    const int32_t *ky = reinterpret_cast<const int32_t *>(lds8 + kMfKy);
+    const int64_t unit_row_m = d.row_offset + int64_t(br * d.blocks_w + bc) * kRowsPerUnit;
+    const int64_t unit_row_c = d.row_offset + int64_t(bc * d.blocks_h + br) * kRowsPerUnit;
+    const int lane_off = lrow * kPatch + lkb / 4;  // py * 16 + px of the lane's first value
+    OutT *out_m = a.rows ? static_cast<OutT *>(a.rows) + unit_row_m * kRowLen + lane_off : nullptr;
+    OutT *out_c = a.rows_col ? static_cast<OutT *>(a.rows_col) + unit_row_c * kRowLen + lane_off : nullptr;
+    static_assert(3 * 2 * 2 == 3 * (kHfThreads / 64), "three vertical blocks per wave");
+    i32x4v vacc[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int blk = wave + j * (kHfThreads / 64);
+        const int xb = blk & 1, yb = (blk >> 1) & 1, c = blk >> 2;
+        const i32x4v av = lds_frag(lds8 + kMfBand + (c * kUnitPx + xb * 16 + lrow) * 64 + 16 * ((lkb >> 4) ^ swz));
+        const uint8_t *wl = lds8 + kMfWy + (yb * 16 + lrow) * 64 + lkb;
+        vacc[j] = digit_product(av, lds_frag(wl + 2 * kUnitPx * 64), lds_frag(wl + kUnitPx * 64), lds_frag(wl),
+                                ky[yb * 16 + lrow]);
+    }
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int blk = wave + j * (kHfThreads / 64);
+        const int xb = blk & 1, yb = (blk >> 1) & 1, c = blk >> 2;
+        const uint32_t bytes = join_pairs(shift_pack_u8(vacc[j][0], vacc[j][1]), shift_pack_u8(vacc[j][2], vacc[j][3]));
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = lut[c * 256 + ((bytes >> (8 * q)) & 255u)];
+        // unit row yb * 2 + xb (patch row yb, column xb), channel c
+        const int off = (yb * kMerge + xb) * kRowLen + c * (kTemporal * kPlane);
+        if (out_m) store_pair<OutT>(out_m + off, v);
+        if (out_c) store_pair<OutT>(out_c + off, v);
+    }
+}
+
+// Six waves per SIMD: a 6000x4000 batch's tile takes about 26 KB of LDS
+// (24 KB in the matrix-core instance), so six workgroups fill a CU; the
+// register budget that leaves (80) holds the kernel without spilling.
+template <typename OutT, bool kMfma>
 __global__ __launch_bounds__(kHfThreads) __attribute__((amdgpu_waves_per_eu(6))) void hf_preprocess_kernel(HfArgs a) {
     extern __shared__ uint32_t lds[];
     float *lut = reinterpret_cast<float *>(lds);  // [3][256]
@@ -426,6 +658,10 @@ __global__ __launch_bounds__(kHfThreads) __attribute__((amdgpu_waves_per_eu(6)))
         return;
     }
 
+    if (kMfma) {
+        resize_mfma<OutT>(a, d, br, bc, tid, reinterpret_cast<uint8_t *>(lds));
+        return;
+    }
     const int dst_w = d.blocks_w * kUnitPx, dst_h = d.blocks_h * kUnitPx;
     const int32_t *xt = a.taps + d.x_tab;  // first[dst_w], then the records
     const int32_t *yt = a.taps + d.y_tab;
@@ -660,7 +896,12 @@ struct HfTables {
     int64_t tiles = 0;
     int64_t rows = 0;
     int32_t band_bytes = 0, stage_bytes = 0;  // dynamic LDS the batch needs (see HfArgs)
+    // every resized item's tiles read at most kMfmaSpan source columns and
+    // band rows (one group per unit) with windows of at most kMfMaxNd
+    // dwords: the matrix-core instance runs the batch
+    bool mfma = true;
     size_t lds_bytes() const {
+        if (mfma) return size_t(kMfLdsBytes);
         return size_t(kLutBytes) + kRecBytes + std::max<size_t>(kBlockBytes, size_t(band_bytes) + size_t(stage_bytes));
     }
 };
@@ -757,13 +998,18 @@ int build_hf_tables(int32_t n, const mimo_image_desc *desc, const float *mean01,
                 return set_error(MIMO_E_UNSUPPORTED, "preprocess_hf: descriptor " + std::to_string(i) +
                                                          ": vertical downscale beyond the kernel's band");
             // the widest source block one tile's 32 output columns read
-            int spitch = 0;  // bytes per staged row and channel
-            for (int32_t x0 = 0; x0 < s.dst_w; x0 += kUnitPx)
-                spitch = std::max(spitch, 4 * stage_pitch(xfirst[x0 + kUnitPx - 1] + 4 * d.ndx - xfirst[x0]));
+            int spitch = 0, xspan = 0;  // bytes per staged row and channel; source columns
+            for (int32_t x0 = 0; x0 < s.dst_w; x0 += kUnitPx) {
+                const int span = xfirst[x0 + kUnitPx - 1] + 4 * d.ndx - xfirst[x0];
+                xspan = std::max(xspan, span);
+                spitch = std::max(spitch, 4 * stage_pitch(span));
+            }
             if (spitch > kMaxStagePitch)
                 return set_error(MIMO_E_UNSUPPORTED, "preprocess_hf: descriptor " + std::to_string(i) +
                                                          ": horizontal downscale beyond the kernel's staging");
             const int nrows = band_rows(yfirst, d.ndy, s.dst_h, d.group);
+            out.mfma = out.mfma && d.group == kUnitPx && xspan <= kMfmaSpan && nrows <= kMfmaSpan &&
+                       d.ndx <= kMfMaxNd && d.ndy <= kMfMaxNd;
             out.band_bytes = std::max(out.band_bytes, 3 * kUnitPx * 4 * band_pitch(nrows));
             // a chunk of staged rows: all of them when that fits, else whole
             // quarters of kMaxStageBytes' worth (at least 4 rows)
@@ -896,17 +1142,24 @@ int mimo_preprocess_hf_batch(int32_t n, const mimo_image_desc *desc, const uint8
     a.stage_bytes = t.stage_bytes;
     const size_t lds = t.lds_bytes();
     const bool f32 = out_dtype == MIMO_F32;
-    const void *kernel = f32 ? reinterpret_cast<const void *>(hf_preprocess_kernel<float>)
-                             : reinterpret_cast<const void *>(hf_preprocess_kernel<uint16_t>);
+    const void *kernel =
+        t.mfma ? (f32 ? reinterpret_cast<const void *>(hf_preprocess_kernel<float, true>)
+                      : reinterpret_cast<const void *>(hf_preprocess_kernel<uint16_t, true>))
+               : (f32 ? reinterpret_cast<const void *>(hf_preprocess_kernel<float, false>)
+                      : reinterpret_cast<const void *>(hf_preprocess_kernel<uint16_t, false>));
     e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return hip_error(e, "preprocess_hf: LDS size");
     const dim3 grid{unsigned(t.tiles), 1, 1};
     const dim3 block{unsigned(kHfThreads), 1, 1};
     e = timed_launch(s, [&] {
-        if (f32)
-            hipLaunchKernelGGL((hf_preprocess_kernel<float>), grid, block, lds, s, a);
+        if (t.mfma && f32)
+            hipLaunchKernelGGL((hf_preprocess_kernel<float, true>), grid, block, lds, s, a);
+        else if (t.mfma)
+            hipLaunchKernelGGL((hf_preprocess_kernel<uint16_t, true>), grid, block, lds, s, a);
+        else if (f32)
+            hipLaunchKernelGGL((hf_preprocess_kernel<float, false>), grid, block, lds, s, a);
         else
-            hipLaunchKernelGGL((hf_preprocess_kernel<uint16_t>), grid, block, lds, s, a);
+            hipLaunchKernelGGL((hf_preprocess_kernel<uint16_t, false>), grid, block, lds, s, a);
     });
     if (e != hipSuccess) return hip_error(e, "preprocess_hf: kernel launch");
     g_dispatches.fetch_add(1);
