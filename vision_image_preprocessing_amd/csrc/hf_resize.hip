@@ -91,6 +91,25 @@ struct HfItem {
 };
 static_assert(sizeof(HfItem) == 64, "HfItem must stay 64 bytes");
 
+// Per-tile record of the matrix-core instance (64 bytes), written by
+// hf_tiles_kernel: all a tile needs before its first source load, so the
+// tile reads one record instead of walking tile -> item -> tap tables.
+struct HfTile {
+    int64_t stage_off;   // bytes into the sources of the tile's first staged pixel (row ylo, column xlo)
+    int64_t row_m;       // the unit's first row in merge-block order
+    int64_t row_c;       // ... and in column order
+    int32_t x_tab, y_tab;  // table offsets (x_tab < 0: no resize; stage_off is then the unit's first pixel)
+    int32_t xlo, ylo;    // the tile's first staged source column and row
+    int32_t row_bytes;
+    int16_t ox0, oy0;    // the unit's first output column and row (the instance takes sides below 2^15)
+    int16_t dst_w, dst_h;
+    int16_t nrows, channels;
+    int16_t ndx, ndy;
+    int16_t pad[2];
+};
+constexpr int kMfMaxSide = 32767;  // output sides the matrix-core instance takes (HfTile's 16-bit fields)
+static_assert(sizeof(HfTile) == 64, "HfTile must stay 64 bytes");
+
 // An axis table is first[n_out] (each output's first input) followed by one
 // record of rec_dwords(nd) int32 per output: the constant 2^21 + 128 sum w,
 // then the digit planes a[nd], b[nd], c[nd], tap t in byte t % 4 of dword
@@ -110,6 +129,8 @@ struct HfArgs {
     // dynamic LDS, sized for the batch: [lut][band][stage]; the direct path
     // uses the bytes after the lut for its block
     int32_t band_bytes, stage_bytes;
+    HfTile *tiles;              // matrix-core instance: one record per tile
+    int64_t n_tiles;
 };
 
 // workspace: [HfItem x n][int64 tile_begin x (n+1)][float lut x 768][int32 taps]
@@ -406,6 +427,15 @@ __device__ __forceinline__ i32x4v digit_product(i32x4v a, i32x4v bc, i32x4v bb, 
     return acc;
 }
 
+// Every 64-byte line the matrix cores read (staged rows, weight lines, band
+// lines) keeps its four 16-byte chunks XOR-swizzled by bits 2-3 of the
+// line's index: a fragment read's 16 lanes, which read one chunk of 16
+// consecutive lines, then fall into distinct banks (unswizzled, lines 4
+// apart share banks), and every 16-byte read stays aligned.
+__device__ __forceinline__ int swizzled_dword(int line, int dw) {
+    return (((dw >> 2) ^ ((line >> 2) & 3)) << 2) | (dw & 3);
+}
+
 // The digit plane p of a record (nd <= kMfMaxNd dwords), into registers.
 __device__ __forceinline__ void load_digits(const int32_t *rec, int nd, int p, uint32_t (&dg)[kMfMaxNd]) {
 #pragma unroll
@@ -421,30 +451,29 @@ __device__ __forceinline__ void write_line(uint8_t *line, int i, const uint32_t 
 #pragma unroll
     for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4 *>(line + 16 * ((k + rot) & 3)) = u32x4{0u, 0u, 0u, 0u};
     const int a = o >> 2, sh = o & 3;
-    uint32_t *w = reinterpret_cast<uint32_t *>(line) + a;
+    uint32_t *w = reinterpret_cast<uint32_t *>(line);
     uint32_t prev = 0;
 #pragma unroll
     for (int q = 0; q <= kMfMaxNd; ++q) {
         const uint32_t cur = q < kMfMaxNd && q < nd ? dg[q] : 0u;
         // bytes 4 (a + q) .. + 3 of the line: the tail of dword q - 1 and the head of dword q
         const uint32_t val = sh ? __builtin_amdgcn_alignbyte(cur, prev, uint32_t(4 - sh)) : cur;
-        if (q <= nd && a + q < kMfmaSpan / 4) w[q] = val;
+        const int dw = a + q;
+        if (q <= nd && dw < kMfmaSpan / 4) w[swizzled_dword(i, dw)] = val;
         prev = cur;
     }
 }
 
 template <typename OutT>
-__device__ __forceinline__ void resize_mfma(const HfArgs &a, const HfItem &d, int br, int bc, int tid,
-                                            uint8_t *lds8) {
-    const int dst_w = d.blocks_w * kUnitPx, dst_h = d.blocks_h * kUnitPx;
-    const int32_t *xt = a.taps + d.x_tab;
-    const int32_t *yt = a.taps + d.y_tab;
-    const int ndx = d.ndx, ndy = d.ndy;
-    const int oy0 = br * kUnitPx, ox0 = bc * kUnitPx;
-    const int xlo = xt[ox0], ylo = yt[oy0];
-    const int nrows = yt[oy0 + kUnitPx - 1] - ylo + 4 * ndy;  // <= 64 (the host checked), so are the columns
-    const int C = d.channels;
-    const uint32_t row_bytes = uint32_t(d.src_w) * uint32_t(C);
+__device__ __forceinline__ void resize_mfma(const HfArgs &a, const HfTile &td, int tid, uint8_t *lds8) {
+    const int32_t *xt = a.taps + td.x_tab;
+    const int32_t *yt = a.taps + td.y_tab;
+    const int ndx = td.ndx, ndy = td.ndy;
+    const int oy0 = td.oy0, ox0 = td.ox0;
+    const int xlo = td.xlo, ylo = td.ylo;
+    const int nrows = td.nrows;  // <= 64 (the host checked), so are the columns
+    const int C = td.channels;
+    const uint32_t row_bytes = uint32_t(td.row_bytes);
 
     // Wx (96 lines: digit plane, output column) and Kx now; the vertical
     // pass's lines, constants and table are read now and written after the
@@ -455,8 +484,8 @@ __device__ __forceinline__ void resize_mfma(const HfArgs &a, const HfItem &d, in
     uint32_t dg[kMfMaxNd];
     int lo = 0, lk = 0;
     if (xline || yline) {
-        const int32_t *rec = xline ? xt + dst_w + int64_t(ox0 + li) * rec_dwords(ndx)
-                                   : yt + dst_h + int64_t(oy0 + li) * rec_dwords(ndy);
+        const int32_t *rec = xline ? xt + td.dst_w + int64_t(ox0 + li) * rec_dwords(ndx)
+                                   : yt + td.dst_h + int64_t(oy0 + li) * rec_dwords(ndy);
         load_digits(rec, xline ? ndx : ndy, lp, dg);
         lo = xline ? xt[ox0 + li] - xlo : yt[oy0 + li] - ylo;
         lk = rec[0];
@@ -472,8 +501,7 @@ __device__ __forceinline__ void resize_mfma(const HfArgs &a, const HfItem &d, in
     // channel planes of signed bytes (columns past the tile's span, and
     // rows past nrows, meet only zero weights)
     {
-        const SrcWindow win = src_window(a, reinterpret_cast<uint64_t>(a.src + d.src_offset) +
-                                                uint64_t(int64_t(ylo) * row_bytes + int64_t(xlo) * C));
+        const SrcWindow win = src_window(a, reinterpret_cast<uint64_t>(a.src) + uint64_t(td.stage_off));
         const int total = nrows * (kMfmaSpan / 4);
         for (int base = tid; base < total; base += kStageBatch * kHfThreads) {
             uint32_t u[kStageBatch][4];
@@ -488,9 +516,11 @@ __device__ __forceinline__ void resize_mfma(const HfArgs &a, const HfItem &d, in
                 if (idx < total) {
                     uint32_t pl[3];
                     quad_planes(u[k], C, pl);
+                    // row idx / 16, dword idx % 16
+                    const int sw = (idx & ~15) | swizzled_dword(idx >> 4, idx & 15);
 #pragma unroll
                     for (int c = 0; c < 3; ++c)
-                        *reinterpret_cast<uint32_t *>(lds8 + kMfStage + c * kMfmaSpan * 64 + idx * 4) = pl[c];
+                        *reinterpret_cast<uint32_t *>(lds8 + kMfStage + c * kMfmaSpan * 64 + sw * 4) = pl[c];
                 }
             }
         }
@@ -500,12 +530,10 @@ __device__ __forceinline__ void resize_mfma(const HfArgs &a, const HfItem &d, in
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lrow = lane & 15, lkb = (lane >> 4) * 16;  // the lane's fragment line and bytes
-    // The band's 64-byte lines (one per channel and output column) keep
-    // their four 16-byte chunks XOR-swizzled by bits 2-3 of the line: the
-    // horizontal pass's dword writes then fall into distinct banks, and a
-    // 16-byte read stays aligned.  (Lines of a 16-line block share those
-    // bits with lrow.)
+    // the lane's chunk of its line, swizzled (lines of a 16-line block share
+    // their index's bits 2-3 with lrow)
     const int swz = (lrow >> 2) & 3;
+    const int lks = 16 * ((lkb >> 4) ^ swz);
     // horizontal pass: blocks (channel, 16 band rows, 16 output columns),
     // two per step so that their matrix-core chains overlap
     const int rblocks = (nrows + 15) >> 4;  // 1 .. 4
@@ -516,8 +544,8 @@ __device__ __forceinline__ void resize_mfma(const HfArgs &a, const HfItem &d, in
         const int t = blk >> 1;
         const int c = (t * inv_rblocks) >> 8;
         const int cb = blk & 1, rb = t - c * rblocks;
-        const i32x4v av = lds_frag(lds8 + kMfStage + (c * kMfmaSpan + rb * 16 + lrow) * 64 + lkb);
-        const uint8_t *wl = lds8 + kMfWx + (cb * 16 + lrow) * 64 + lkb;
+        const i32x4v av = lds_frag(lds8 + kMfStage + (c * kMfmaSpan + rb * 16 + lrow) * 64 + lks);
+        const uint8_t *wl = lds8 + kMfWx + (cb * 16 + lrow) * 64 + lks;
         return digit_product(av, lds_frag(wl + 2 * kUnitPx * 64), lds_frag(wl + kUnitPx * 64), lds_frag(wl),
                              kx[cb * 16 + lrow]);
     };
@@ -553,19 +581,17 @@ __device__ __forceinline__ void resize_mfma(const HfArgs &a, const HfItem &d, in
     // pixels of a patch row
     const float *lut = reinterpret_cast<const float *>(lds8 + kMfLut);
     const int32_t *ky = reinterpret_cast<const int32_t *>(lds8 + kMfKy);
-    const int64_t unit_row_m = d.row_offset + int64_t(br * d.blocks_w + bc) * kRowsPerUnit;
-    const int64_t unit_row_c = d.row_offset + int64_t(bc * d.blocks_h + br) * kRowsPerUnit;
     const int lane_off = lrow * kPatch + lkb / 4;  // py * 16 + px of the lane's first value
-    OutT *out_m = a.rows ? static_cast<OutT *>(a.rows) + unit_row_m * kRowLen + lane_off : nullptr;
-    OutT *out_c = a.rows_col ? static_cast<OutT *>(a.rows_col) + unit_row_c * kRowLen + lane_off : nullptr;
+    OutT *out_m = a.rows ? static_cast<OutT *>(a.rows) + td.row_m * kRowLen + lane_off : nullptr;
+    OutT *out_c = a.rows_col ? static_cast<OutT *>(a.rows_col) + td.row_c * kRowLen + lane_off : nullptr;
     static_assert(3 * 2 * 2 == 3 * (kHfThreads / 64), "three vertical blocks per wave");
     i32x4v vacc[3];
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
         const int blk = wave + j * (kHfThreads / 64);
         const int xb = blk & 1, yb = (blk >> 1) & 1, c = blk >> 2;
-        const i32x4v av = lds_frag(lds8 + kMfBand + (c * kUnitPx + xb * 16 + lrow) * 64 + 16 * ((lkb >> 4) ^ swz));
-        const uint8_t *wl = lds8 + kMfWy + (yb * 16 + lrow) * 64 + lkb;
+        const i32x4v av = lds_frag(lds8 + kMfBand + (c * kUnitPx + xb * 16 + lrow) * 64 + lks);
+        const uint8_t *wl = lds8 + kMfWy + (yb * 16 + lrow) * 64 + lks;
         vacc[j] = digit_product(av, lds_frag(wl + 2 * kUnitPx * 64), lds_frag(wl + kUnitPx * 64), lds_frag(wl),
                                 ky[yb * 16 + lrow]);
     }
@@ -584,6 +610,87 @@ __device__ __forceinline__ void resize_mfma(const HfArgs &a, const HfItem &d, in
     }
 }
 
+// A unit that neither axis resizes, from its tile record: its 32 x 32
+// source pixels into an LDS block (after the table), then through the table
+// to the outputs.
+template <typename OutT>
+__device__ __forceinline__ void direct_unit(const HfArgs &a, const HfTile &td, int tid, uint32_t *lds) {
+    float *lut = reinterpret_cast<float *>(lds);
+    uint32_t *block = lds + kLutBytes / 4;
+    for (int i = tid; i < 3 * 256; i += kHfThreads) lut[i] = a.lut[i];
+    const int C = td.channels;
+    const uint32_t row_bytes = uint32_t(td.row_bytes);
+    const SrcWindow win = src_window(a, reinterpret_cast<uint64_t>(a.src) + uint64_t(td.stage_off));
+    for (int idx = tid; idx < kUnitPx * kUnitPx / 4; idx += kHfThreads) {
+        const int r = idx >> 3, q = idx & 7;
+        uint32_t u[4];
+        load_quad_bytes(win, win.lead + __umul24(uint32_t(r), row_bytes) + uint32_t(4 * q * C), C, u);
+        *reinterpret_cast<u32x4 *>(&block[r * kUnitPx + 4 * q]) = quad_pixels(u, C);
+    }
+    __syncthreads();
+    // items (row, patch column, channel, quad), the row fixed per thread
+    const int yl = (tid >> 2) & (kUnitPx - 1);
+    const int py_off = (yl & (kPatch - 1)) * kPatch;
+    const int64_t mh2 = (yl >> 4) * kMerge;
+    OutT *out_m = a.rows ? static_cast<OutT *>(a.rows) + (td.row_m + mh2) * kRowLen + py_off : nullptr;
+    OutT *out_c = a.rows_col ? static_cast<OutT *>(a.rows_col) + (td.row_c + mh2) * kRowLen + py_off : nullptr;
+    for (int idx = tid; idx < kUnitPx * 2 * 3 * 4; idx += kHfThreads) {
+        const int qd = idx & 3;
+        const int mc = idx >> 7;
+        const int mw = mc >= 3 ? 1 : 0;
+        const int c = mc - 3 * mw;
+        const uint32_t *px = &block[yl * kUnitPx + mw * kPatch + qd * 4];
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = lut[c * 256 + ((px[j] >> (8 * c)) & 255u)];
+        const int off = mw * kRowLen + c * (kTemporal * kPlane) + qd * 4;
+        if (out_m) store_pair<OutT>(out_m + off, v);
+        if (out_c) store_pair<OutT>(out_c + off, v);
+    }
+}
+
+// One thread per tile of a matrix-core batch (every item one tile per
+// unit): its record, from the item and the tap tables.
+__global__ __launch_bounds__(256) void hf_tiles_kernel(HfArgs a) {
+    const int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (t >= a.n_tiles) return;
+    int lo = 0, hi = a.n;  // the item: largest i with tile_begin[i] <= t
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (a.tile_begin[mid] <= t) lo = mid; else hi = mid;
+    }
+    const HfItem d = a.items[lo];
+    const int unit = int(t - a.tile_begin[lo]);
+    const int br = unit / d.blocks_w, bc = unit - br * d.blocks_w;
+    HfTile r;
+    r.ox0 = int16_t(bc * kUnitPx);
+    r.oy0 = int16_t(br * kUnitPx);
+    r.dst_w = int16_t(d.blocks_w * kUnitPx);
+    r.dst_h = int16_t(d.blocks_h * kUnitPx);
+    r.row_m = d.row_offset + int64_t(br * d.blocks_w + bc) * kRowsPerUnit;
+    r.row_c = d.row_offset + int64_t(bc * d.blocks_h + br) * kRowsPerUnit;
+    r.row_bytes = d.src_w * d.channels;
+    r.channels = int16_t(d.channels);
+    r.x_tab = int32_t(d.x_tab);
+    r.y_tab = int32_t(d.y_tab);
+    r.ndx = int16_t(d.ndx);
+    r.ndy = int16_t(d.ndy);
+    r.pad[0] = r.pad[1] = 0;
+    if (d.x_tab >= 0) {
+        const int32_t *xt = a.taps + d.x_tab;
+        const int32_t *yt = a.taps + d.y_tab;
+        r.xlo = xt[bc * kUnitPx];
+        r.ylo = yt[br * kUnitPx];
+        r.nrows = int16_t(yt[br * kUnitPx + kUnitPx - 1] - r.ylo + 4 * d.ndy);
+    } else {
+        r.xlo = bc * kUnitPx;
+        r.ylo = br * kUnitPx;
+        r.nrows = kUnitPx;
+    }
+    r.stage_off = d.src_offset + int64_t(r.ylo) * r.row_bytes + int64_t(r.xlo) * d.channels;
+    a.tiles[t] = r;
+}
+
 // Six waves per SIMD: a 6000x4000 batch's tile takes about 26 KB of LDS
 // (24 KB in the matrix-core instance), so six workgroups fill a CU; the
 // register budget that leaves (80) holds the kernel without spilling.
@@ -594,6 +701,14 @@ __global__ __launch_bounds__(kHfThreads) __attribute__((amdgpu_waves_per_eu(6)))
     uint32_t *recs = lds + kLutBytes / 4;  // [column records x 32][row records x 32], kRegRecord dwords each
     uint8_t *region = reinterpret_cast<uint8_t *>(lds) + kLutBytes + kRecBytes;
     const int64_t tile = xcd_contiguous_tile(blockIdx.x, gridDim.x);
+    if (kMfma) {
+        const HfTile td = a.tiles[tile];
+        if (td.x_tab < 0)
+            direct_unit<OutT>(a, td, threadIdx.x, lds);
+        else
+            resize_mfma<OutT>(a, td, threadIdx.x, reinterpret_cast<uint8_t *>(lds));
+        return;
+    }
     const int img = find_segment(a.tile_begin, a.n, tile);
     const HfItem d = a.items[img];
     // An item lists one tile per (merge unit, group of G output rows); G is
@@ -658,10 +773,6 @@ __global__ __launch_bounds__(kHfThreads) __attribute__((amdgpu_waves_per_eu(6)))
         return;
     }
 
-    if (kMfma) {
-        resize_mfma<OutT>(a, d, br, bc, tid, reinterpret_cast<uint8_t *>(lds));
-        return;
-    }
     const int dst_w = d.blocks_w * kUnitPx, dst_h = d.blocks_h * kUnitPx;
     const int32_t *xt = a.taps + d.x_tab;  // first[dst_w], then the records
     const int32_t *yt = a.taps + d.y_tab;
@@ -987,6 +1098,7 @@ int build_hf_tables(int32_t n, const mimo_image_desc *desc, const float *mean01,
         d.channels = s.channels;
         d.blocks_h = s.dst_h / kUnitPx;
         d.blocks_w = s.dst_w / kUnitPx;
+        out.mfma = out.mfma && s.dst_w <= kMfMaxSide && s.dst_h <= kMfMaxSide;
         if (s.dst_w != s.src_w || s.dst_h != s.src_h) {
             // both axes get a table (an axis that keeps its length: one tap of weight 1)
             axis_table(s.src_w, s.dst_w, true, d.x_tab, d.ndx);
@@ -1060,6 +1172,17 @@ int build_hf_tables(int32_t n, const mimo_image_desc *desc, const float *mean01,
     return MIMO_OK;
 }
 
+// Room for one HfTile per merge unit (the matrix-core instance's tiles).
+size_t hf_tiles_bytes(int32_t n, const mimo_image_desc *desc) {
+    size_t units = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        const mimo_image_desc &s = desc[i];
+        if (s.status != MIMO_OK || s.rows == 0 || s.dst_w < 1 || s.dst_h < 1) continue;
+        units += size_t(s.dst_h / kUnitPx) * size_t(s.dst_w / kUnitPx);
+    }
+    return align256(units * sizeof(HfTile));
+}
+
 }  // namespace
 }  // namespace mimo
 
@@ -1080,7 +1203,7 @@ size_t mimo_hf_workspace_bytes(int32_t n, const mimo_image_desc *desc) {
         entries += axis_table_entries(s.dst_w, axis_dwords(kx)) + axis_table_entries(s.dst_h, axis_dwords(ky));
     }
     return hf_items_bytes(n) + hf_prefix_bytes(n) + align256(kLutBytes) +
-           align256(std::max<size_t>(entries, 1) * sizeof(int32_t));
+           align256(std::max<size_t>(entries, 1) * sizeof(int32_t)) + hf_tiles_bytes(n, desc);
 }
 
 int mimo_preprocess_hf_batch(int32_t n, const mimo_image_desc *desc, const uint8_t *src,
@@ -1106,7 +1229,8 @@ int mimo_preprocess_hf_batch(int32_t n, const mimo_image_desc *desc, const uint8
     HfTables t;
     int st = build_hf_tables(n, desc, mean01, std01, t);
     if (st != MIMO_OK) return st;
-    const size_t need = t.head.size() + align256(std::max<size_t>(t.taps.size(), 1) * sizeof(int32_t));
+    const size_t taps_bytes = align256(std::max<size_t>(t.taps.size(), 1) * sizeof(int32_t));
+    const size_t need = t.head.size() + taps_bytes + (t.mfma ? align256(size_t(t.tiles) * sizeof(HfTile)) : 0);
     if (workspace_bytes < need)
         return set_error(MIMO_E_CAPACITY, "preprocess_hf: workspace smaller than mimo_hf_workspace_bytes(n, desc)");
     int64_t src_needed = 0;
@@ -1140,6 +1264,8 @@ int mimo_preprocess_hf_batch(int32_t n, const mimo_image_desc *desc, const uint8
     a.n = n;
     a.band_bytes = t.band_bytes;
     a.stage_bytes = t.stage_bytes;
+    a.tiles = t.mfma ? reinterpret_cast<HfTile *>(ws + t.head.size() + taps_bytes) : nullptr;
+    a.n_tiles = t.tiles;
     const size_t lds = t.lds_bytes();
     const bool f32 = out_dtype == MIMO_F32;
     const void *kernel =
@@ -1151,7 +1277,9 @@ int mimo_preprocess_hf_batch(int32_t n, const mimo_image_desc *desc, const uint8
     if (e != hipSuccess) return hip_error(e, "preprocess_hf: LDS size");
     const dim3 grid{unsigned(t.tiles), 1, 1};
     const dim3 block{unsigned(kHfThreads), 1, 1};
+    const dim3 tgrid{unsigned((t.tiles + 255) / 256), 1, 1};
     e = timed_launch(s, [&] {
+        if (t.mfma) hipLaunchKernelGGL(hf_tiles_kernel, tgrid, dim3(256), 0, s, a);
         if (t.mfma && f32)
             hipLaunchKernelGGL((hf_preprocess_kernel<float, true>), grid, block, lds, s, a);
         else if (t.mfma)
