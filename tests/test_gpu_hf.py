@@ -115,9 +115,11 @@ def test_random_shapes_bitwise(V, seed, out_dtype):
 
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 def test_mild_resizes_bitwise(V, out_dtype):
-    """A batch of over 1024 tiles whose every resized axis has at most 5
-    taps per output (mild up- and downscales under the stock geometry) runs
-    in 256-thread workgroups; same bar."""
+    """A batch of mild up- and downscales under the stock geometry (every
+    tile within 64 source columns and band rows, windows of at most 12
+    taps) runs the matrix-core instance; same bar.  (The ragged batch above
+    runs it too, with identity-size items; the random batches, which hold
+    strong downscales, run the dot-product instance.)"""
     _say("mild resizes", out_dtype)
     b = W.uniform_images([(200, 300, 3), (300, 200, 4), (250, 250, 3), (90, 500, 4), (1000, 700, 3),
                           (1000, 1400, 4), (2000, 1500, 3)], seed=88)
