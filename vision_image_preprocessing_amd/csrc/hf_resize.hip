@@ -389,18 +389,20 @@ __device__ __forceinline__ void store_pair<uint16_t>(uint16_t *p, const float (&
 // and holds result rows 4 (l / 16) .. + 3 of column l % 16.
 constexpr int kMfmaSpan = 64;  // the K of one instruction: staged columns, band rows
 constexpr int kMfMaxNd = 3;    // window dwords (12 taps) the instance takes
-// LDS while the horizontal pass runs: [stage][band][Wx][Kx] ...
-constexpr int kMfStage = 0;                              // [channel][64 rows][64 bytes]
-constexpr int kMfBand = kMfStage + 3 * kMfmaSpan * 64;   // [channel][32 columns][64 rows]
+// LDS (20 KB: eight workgroups fit a CU): two buffers of one staged
+// channel plane each (the horizontal pass takes the channels in turn, the
+// other planes wait in registers), the band, and Wx; the vertical pass's
+// table then takes the first buffer and Wy takes Wx's place.  The records'
+// constants stay in registers.
+constexpr int kMfPlane = kMfmaSpan * 64;                 // [64 rows][64 bytes]
+constexpr int kMfStage0 = 0;
+constexpr int kMfStage1 = kMfStage0 + kMfPlane;
+constexpr int kMfBand = kMfStage1 + kMfPlane;            // [channel][32 columns][64 rows]
 constexpr int kMfWx = kMfBand + 3 * kUnitPx * 64;        // [digit plane][32 output columns][64]
-constexpr int kMfKx = kMfWx + 3 * kUnitPx * 64;          // int32 [32] record constants
-constexpr int kMfLdsBytes = kMfKx + kUnitPx * 4;
-// ... and for the vertical pass the stage's bytes hold the table, Wy and Ky
-// (24 KB in all: six workgroups fit a CU)
-constexpr int kMfLut = kMfStage;                         // float [3][256]
-constexpr int kMfWy = kMfLut + kLutBytes;                // [digit plane][32 output rows][64]
-constexpr int kMfKy = kMfWy + 3 * kUnitPx * 64;          // int32 [32]
-static_assert(kMfKy + kUnitPx * 4 <= kMfBand, "the vertical pass's tables fit the stage's bytes");
+constexpr int kMfLdsBytes = kMfWx + 3 * kUnitPx * 64;
+constexpr int kMfLut = kMfStage0;                        // float [3][256], after the horizontal pass
+constexpr int kMfWy = kMfWx;                             // [digit plane][32 output rows][64], likewise
+static_assert(kLutBytes <= kMfPlane && kMfLdsBytes == 20 * 1024, "the vertical pass's tables fit");
 
 typedef int32_t i32x4v __attribute__((ext_vector_type(4)));
 
@@ -474,105 +476,106 @@ __device__ __forceinline__ void resize_mfma(const HfArgs &a, const HfTile &td, i
     const int nrows = td.nrows;  // <= 64 (the host checked), so are the columns
     const int C = td.channels;
     const uint32_t row_bytes = uint32_t(td.row_bytes);
+    const int32_t *xrec = xt + td.dst_w;  // records of output columns ox0 ..
+    const int32_t *yrec = yt + td.dst_h;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lrow = lane & 15, lkb = (lane >> 4) * 16;  // the lane's fragment line and bytes
 
-    // Wx (96 lines: digit plane, output column) and Kx now; the vertical
-    // pass's lines, constants and table are read now and written after the
-    // horizontal pass, into the stage's bytes
+    // Everything the tile reads from memory, first: the source block (64
+    // columns x nrows rows, 4 quads per thread), Wx's and Wy's lines (one
+    // per thread of the first 192: digit plane, output), the records'
+    // constants of the lane's result columns, and the table.
+    const SrcWindow win = src_window(a, reinterpret_cast<uint64_t>(a.src) + uint64_t(td.stage_off));
+    const int total = nrows * (kMfmaSpan / 4);  // <= 1024: one batch
+    static_assert(kMfmaSpan * kMfmaSpan / 4 <= kStageBatch * kHfThreads, "one staging batch per tile");
+    uint32_t u[kStageBatch][4];
+#pragma unroll
+    for (int k = 0; k < kStageBatch; ++k) {
+        const uint32_t idx = uint32_t(tid + k * kHfThreads);
+        load_quad_bytes(win, win.lead + __umul24(idx >> 4, row_bytes) + (idx & 15u) * uint32_t(4 * C), C, u[k]);
+    }
     const bool xline = tid < 3 * kUnitPx;
     const bool yline = !xline && tid < 2 * 3 * kUnitPx;
     const int lp = (xline ? tid : tid - 3 * kUnitPx) >> 5, li = tid & (kUnitPx - 1);
     uint32_t dg[kMfMaxNd];
-    int lo = 0, lk = 0;
+    int lo = 0;
     if (xline || yline) {
-        const int32_t *rec = xline ? xt + td.dst_w + int64_t(ox0 + li) * rec_dwords(ndx)
-                                   : yt + td.dst_h + int64_t(oy0 + li) * rec_dwords(ndy);
+        const int32_t *rec = xline ? xrec + int64_t(ox0 + li) * rec_dwords(ndx) : yrec + int64_t(oy0 + li) * rec_dwords(ndy);
         load_digits(rec, xline ? ndx : ndy, lp, dg);
         lo = xline ? xt[ox0 + li] - xlo : yt[oy0 + li] - ylo;
-        lk = rec[0];
     }
+    // the constants of result columns lrow and 16 + lrow (scalars: an array
+    // picked from by a wave-uniform index would go to scratch)
+    const int32_t kx0 = xrec[int64_t(ox0 + lrow) * rec_dwords(ndx)];
+    const int32_t kx1 = xrec[int64_t(ox0 + 16 + lrow) * rec_dwords(ndx)];
+    const int32_t ky0 = yrec[int64_t(oy0 + lrow) * rec_dwords(ndy)];
+    const int32_t ky1 = yrec[int64_t(oy0 + 16 + lrow) * rec_dwords(ndy)];
     float lut_v[3];
 #pragma unroll
     for (int i = 0; i < 3; ++i) lut_v[i] = a.lut[tid + i * kHfThreads];
-    if (xline) {
-        write_line(lds8 + kMfWx + (lp * kUnitPx + li) * 64, li, dg, ndx, lo);
-        if (lp == 0) reinterpret_cast<int32_t *>(lds8 + kMfKx)[li] = lk;
-    }
-    // staged source rows [ylo, ylo + nrows) x columns [xlo, xlo + 64), as
-    // channel planes of signed bytes (columns past the tile's span, and
-    // rows past nrows, meet only zero weights)
-    {
-        const SrcWindow win = src_window(a, reinterpret_cast<uint64_t>(a.src) + uint64_t(td.stage_off));
-        const int total = nrows * (kMfmaSpan / 4);
-        for (int base = tid; base < total; base += kStageBatch * kHfThreads) {
-            uint32_t u[kStageBatch][4];
+    if (xline) write_line(lds8 + kMfWx + (lp * kUnitPx + li) * 64, li, dg, ndx, lo);
+
+    // the block as channel planes of signed bytes (columns past the tile's
+    // span, and rows past nrows, meet only zero weights); plane 0 now
+    uint32_t pl[kStageBatch][3];
 #pragma unroll
-            for (int k = 0; k < kStageBatch; ++k) {
-                const uint32_t idx = uint32_t(base + k * kHfThreads);
-                load_quad_bytes(win, win.lead + __umul24(idx >> 4, row_bytes) + (idx & 15u) * uint32_t(4 * C), C, u[k]);
-            }
+    for (int k = 0; k < kStageBatch; ++k) quad_planes(u[k], C, pl[k]);
+    auto write_plane = [&](int c, int buf) {
 #pragma unroll
-            for (int k = 0; k < kStageBatch; ++k) {
-                const int idx = base + k * kHfThreads;
-                if (idx < total) {
-                    uint32_t pl[3];
-                    quad_planes(u[k], C, pl);
-                    // row idx / 16, dword idx % 16
-                    const int sw = (idx & ~15) | swizzled_dword(idx >> 4, idx & 15);
-#pragma unroll
-                    for (int c = 0; c < 3; ++c)
-                        *reinterpret_cast<uint32_t *>(lds8 + kMfStage + c * kMfmaSpan * 64 + sw * 4) = pl[c];
-                }
-            }
+        for (int k = 0; k < kStageBatch; ++k) {
+            const int idx = tid + k * kHfThreads;  // row idx / 16, dword idx % 16
+            if (idx < total)
+                *reinterpret_cast<uint32_t *>(lds8 + buf + 4 * ((idx & ~15) | swizzled_dword(idx >> 4, idx & 15))) =
+                    pl[k][c];
         }
-    }
+    };
+    write_plane(0, kMfStage0);
     __syncthreads();
 
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lrow = lane & 15, lkb = (lane >> 4) * 16;  // the lane's fragment line and bytes
     // the lane's chunk of its line, swizzled (lines of a 16-line block share
     // their index's bits 2-3 with lrow)
     const int swz = (lrow >> 2) & 3;
     const int lks = 16 * ((lkb >> 4) ^ swz);
-    // horizontal pass: blocks (channel, 16 band rows, 16 output columns),
-    // two per step so that their matrix-core chains overlap
+    // horizontal pass, one channel at a time: blocks (16 band rows, 16
+    // output columns), two per wave so that their matrix-core chains overlap
     const int rblocks = (nrows + 15) >> 4;  // 1 .. 4
-    const int nblk = 3 * rblocks * 2;
-    const int inv_rblocks = (256 + rblocks - 1) / rblocks;  // t / rblocks = (t * inv) >> 8 for t < 12
-    const int32_t *kx = reinterpret_cast<const int32_t *>(lds8 + kMfKx);
-    auto h_block = [&](int blk) {
-        const int t = blk >> 1;
-        const int c = (t * inv_rblocks) >> 8;
-        const int cb = blk & 1, rb = t - c * rblocks;
-        const i32x4v av = lds_frag(lds8 + kMfStage + (c * kMfmaSpan + rb * 16 + lrow) * 64 + lks);
+    const int nblk = rblocks * 2;           // <= 8: one step per wave
+    auto h_block = [&](int buf, int blk) {
+        const int cb = blk & 1, rb = blk >> 1;
+        const i32x4v av = lds_frag(lds8 + buf + (rb * 16 + lrow) * 64 + lks);
         const uint8_t *wl = lds8 + kMfWx + (cb * 16 + lrow) * 64 + lks;
         return digit_product(av, lds_frag(wl + 2 * kUnitPx * 64), lds_frag(wl + kUnitPx * 64), lds_frag(wl),
-                             kx[cb * 16 + lrow]);
+                             cb ? kx1 : kx0);
     };
-    auto h_store = [&](int blk, const i32x4v &acc) {
-        const int t = blk >> 1;
-        const int c = (t * inv_rblocks) >> 8;
-        const int cb = blk & 1, rb = t - c * rblocks;
+    auto h_store = [&](int c, int blk, const i32x4v &acc) {
+        const int cb = blk & 1, rb = blk >> 1;
         // rows 4 (lane / 16) .. + 3 of column cb * 16 + lrow, as signed bytes
         *reinterpret_cast<uint32_t *>(lds8 + kMfBand + (c * kUnitPx + cb * 16 + lrow) * 64 + 16 * (rb ^ swz) +
                                       lkb / 4) = join_pairs(shift_pack_i8(acc[0], acc[1]), shift_pack_i8(acc[2], acc[3]));
     };
-    for (int blk = wave; blk < nblk; blk += 2 * (kHfThreads / 64)) {
-        const int blk2 = blk + kHfThreads / 64;
-        const i32x4v acc = h_block(blk);
-        const i32x4v acc2 = h_block(min(blk2, nblk - 1));
-        h_store(blk, acc);
-        if (blk2 < nblk) h_store(blk2, acc2);
-    }
+    auto h_pass_channel = [&](int c, int buf) {
+        const int blk = wave, blk2 = wave + kHfThreads / 64;
+        if (blk < nblk) {
+            const i32x4v acc = h_block(buf, blk);
+            const i32x4v acc2 = h_block(buf, min(blk2, nblk - 1));
+            h_store(c, blk, acc);
+            if (blk2 < nblk) h_store(c, blk2, acc2);
+        }
+    };
+    h_pass_channel(0, kMfStage0);
+    write_plane(1, kMfStage1);
+    __syncthreads();
+    h_pass_channel(1, kMfStage1);
+    write_plane(2, kMfStage0);
+    __syncthreads();
+    h_pass_channel(2, kMfStage0);
     __syncthreads();
 
-    // the vertical pass's table, Wy and Ky, into the stage's bytes
+    // the vertical pass's table and Wy, where the first buffer and Wx were
 #pragma unroll
     for (int i = 0; i < 3; ++i) reinterpret_cast<float *>(lds8 + kMfLut)[tid + i * kHfThreads] = lut_v[i];
-    if (yline) {
-        write_line(lds8 + kMfWy + (lp * kUnitPx + li) * 64, li, dg, ndy, lo);
-        if (lp == 0) reinterpret_cast<int32_t *>(lds8 + kMfKy)[li] = lk;
-    }
+    if (yline) write_line(lds8 + kMfWy + (lp * kUnitPx + li) * 64, li, dg, ndy, lo);
     __syncthreads();
 
     // vertical pass, transposed: out^T[x][y] = sum_r band^T[x][r] Wy^T[r][y],
@@ -580,7 +583,6 @@ __device__ __forceinline__ void resize_mfma(const HfArgs &a, const HfTile &td, i
     // lane l holds output columns 4 (l / 16) .. + 3 of row l % 16: four
     // pixels of a patch row
     const float *lut = reinterpret_cast<const float *>(lds8 + kMfLut);
-    const int32_t *ky = reinterpret_cast<const int32_t *>(lds8 + kMfKy);
     const int lane_off = lrow * kPatch + lkb / 4;  // py * 16 + px of the lane's first value
     OutT *out_m = a.rows ? static_cast<OutT *>(a.rows) + td.row_m * kRowLen + lane_off : nullptr;
     OutT *out_c = a.rows_col ? static_cast<OutT *>(a.rows_col) + td.row_c * kRowLen + lane_off : nullptr;
@@ -593,7 +595,7 @@ __device__ __forceinline__ void resize_mfma(const HfArgs &a, const HfTile &td, i
         const i32x4v av = lds_frag(lds8 + kMfBand + (c * kUnitPx + xb * 16 + lrow) * 64 + lks);
         const uint8_t *wl = lds8 + kMfWy + (yb * 16 + lrow) * 64 + lks;
         vacc[j] = digit_product(av, lds_frag(wl + 2 * kUnitPx * 64), lds_frag(wl + kUnitPx * 64), lds_frag(wl),
-                                ky[yb * 16 + lrow]);
+                                yb ? ky1 : ky0);
     }
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
@@ -695,7 +697,7 @@ __global__ __launch_bounds__(256) void hf_tiles_kernel(HfArgs a) {
 // (24 KB in the matrix-core instance), so six workgroups fill a CU; the
 // register budget that leaves (80) holds the kernel without spilling.
 template <typename OutT, bool kMfma>
-__global__ __launch_bounds__(kHfThreads) __attribute__((amdgpu_waves_per_eu(6))) void hf_preprocess_kernel(HfArgs a) {
+__global__ __launch_bounds__(kHfThreads) __attribute__((amdgpu_waves_per_eu(kMfma ? 8 : 6))) void hf_preprocess_kernel(HfArgs a) {
     extern __shared__ uint32_t lds[];
     float *lut = reinterpret_cast<float *>(lds);  // [3][256]
     uint32_t *recs = lds + kLutBytes / 4;  // [column records x 32][row records x 32], kRegRecord dwords each
