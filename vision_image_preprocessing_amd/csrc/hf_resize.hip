@@ -76,6 +76,9 @@ constexpr int kLutBytes = 3 * 256 * 4;
 constexpr int kBlockBytes = kUnitPx * kUnitPx * 4;  // the direct path's unit block (RGB per dword)
 constexpr int64_t kParallelTapWork = 1 << 18;  // weights (outputs x taps) worth several host threads
 constexpr int kBufferWord3 = 0x00020000;     // raw buffer resource word 3 (gfx9 family)
+// Zero dwords after the last table: a record's digit planes are read three
+// dwords at a time, which may run up to two dwords past the last record.
+constexpr size_t kTapsTail = 4;
 
 // Per-item record of the contrast kernel (64 bytes).
 struct HfItem {
@@ -131,6 +134,7 @@ struct HfArgs {
     int32_t band_bytes, stage_bytes;
     HfTile *tiles;              // matrix-core instance: one record per tile
     int64_t n_tiles;
+    int32_t taps_bytes;         // the tables' exact size (the matrix-core instance reads them through a resource)
 };
 
 // workspace: [HfItem x n][int64 tile_begin x (n+1)][float lut x 768][int32 taps]
@@ -410,23 +414,23 @@ __device__ __forceinline__ i32x4v lds_frag(const uint8_t *p) {
     return __builtin_bit_cast(i32x4v, *reinterpret_cast<const u32x4 *>(p));
 }
 
-// acc = A x (c, b, a digit planes of B), chained: ((A Bc << 8) + A Bb) << 8
-// + A Ba + K; K per column of the result (lane l's column l % 16).  K is
-// added last, by an ordinary VALU instruction: the packing instructions
-// that read the result are inline assembly, which the compiler cannot
-// space from a matrix-core write, but it does space this add.
+// A x B for B = (c << 16) + (b << 8) + a (signed digit planes), plus K per
+// column of the result (lane l's column l % 16): the products of planes c
+// and b are independent, (A Bb << 8) + K seeds the product of plane a, and
+// (A Bc << 16) joins last, so each value takes two shift-adds.  The sums
+// wrap modulo 2^32, which is harmless, since the true sum fits an int32.
 __device__ __forceinline__ i32x4v digit_product(i32x4v a, i32x4v bc, i32x4v bb, i32x4v ba, int32_t k) {
-    i32x4v acc = {0, 0, 0, 0};
-    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bc, acc, 0, 0, 0);
+    const i32x4v zero = {0, 0, 0, 0};
+    const i32x4v pc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bc, zero, 0, 0, 0);
+    const i32x4v pb = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bb, zero, 0, 0, 0);
+    i32x4v seed;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = int32_t(uint32_t(acc[i]) << 8);
-    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bb, acc, 0, 0, 0);
+    for (int i = 0; i < 4; ++i) seed[i] = int32_t((uint32_t(pb[i]) << 8) + uint32_t(k));
+    const i32x4v pa = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, ba, seed, 0, 0, 0);
+    i32x4v r;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = int32_t(uint32_t(acc[i]) << 8);
-    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, ba, acc, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = int32_t(uint32_t(acc[i]) + uint32_t(k));
-    return acc;
+    for (int i = 0; i < 4; ++i) r[i] = int32_t((uint32_t(pc[i]) << 16) + uint32_t(pa[i]));
+    return r;
 }
 
 // Every 64-byte line the matrix cores read (staged rows, weight lines, band
@@ -438,17 +442,15 @@ __device__ __forceinline__ int swizzled_dword(int line, int dw) {
     return (((dw >> 2) ^ ((line >> 2) & 3)) << 2) | (dw & 3);
 }
 
-// The digit plane p of a record (nd <= kMfMaxNd dwords), into registers.
-__device__ __forceinline__ void load_digits(const int32_t *rec, int nd, int p, uint32_t (&dg)[kMfMaxNd]) {
-#pragma unroll
-    for (int q = 0; q < kMfMaxNd; ++q) dg[q] = q < nd ? uint32_t(rec[1 + p * nd + q]) : 0u;
-}
-
 // Line i of a banded weight matrix (64 bytes): the digits dg placed at byte
 // o, zero elsewhere.  The line is zeroed 16 bytes at a time, each group of 4
 // lines starting at its own chunk: lines are 64 bytes apart, so lanes
-// writing the same chunk of lines 4 apart would share banks.
-__device__ __forceinline__ void write_line(uint8_t *line, int i, const uint32_t (&dg)[kMfMaxNd], int nd, int o) {
+// writing the same chunk of lines 4 apart would share banks.  Then dwords
+// o / 4 .. + 3 take the digits shifted by o % 4 bytes, without a condition:
+// the digits end by byte 63 (o + 4 nd is at most the tile's span of 64), so
+// a dword index past the line's end carries zeros only, and it wraps to a
+// dword before o / 4, which is zero as well.
+__device__ __forceinline__ void write_line(uint8_t *line, int i, const uint32_t (&dg)[kMfMaxNd], int o) {
     const int rot = (i >> 2) & 3;
 #pragma unroll
     for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4 *>(line + 16 * ((k + rot) & 3)) = u32x4{0u, 0u, 0u, 0u};
@@ -457,27 +459,28 @@ __device__ __forceinline__ void write_line(uint8_t *line, int i, const uint32_t 
     uint32_t prev = 0;
 #pragma unroll
     for (int q = 0; q <= kMfMaxNd; ++q) {
-        const uint32_t cur = q < kMfMaxNd && q < nd ? dg[q] : 0u;
+        const uint32_t cur = q < kMfMaxNd ? dg[q] : 0u;
         // bytes 4 (a + q) .. + 3 of the line: the tail of dword q - 1 and the head of dword q
         const uint32_t val = sh ? __builtin_amdgcn_alignbyte(cur, prev, uint32_t(4 - sh)) : cur;
-        const int dw = a + q;
-        if (q <= nd && dw < kMfmaSpan / 4) w[swizzled_dword(i, dw)] = val;
+        w[swizzled_dword(i, (a + q) & (kMfmaSpan / 4 - 1))] = val;
         prev = cur;
     }
 }
 
 template <typename OutT>
 __device__ __forceinline__ void resize_mfma(const HfArgs &a, const HfTile &td, int tid, uint8_t *lds8) {
-    const int32_t *xt = a.taps + td.x_tab;
-    const int32_t *yt = a.taps + td.y_tab;
     const int ndx = td.ndx, ndy = td.ndy;
     const int oy0 = td.oy0, ox0 = td.ox0;
     const int xlo = td.xlo, ylo = td.ylo;
     const int nrows = td.nrows;  // <= 64 (the host checked), so are the columns
     const int C = td.channels;
     const uint32_t row_bytes = uint32_t(td.row_bytes);
-    const int32_t *xrec = xt + td.dst_w;  // records of output columns ox0 ..
-    const int32_t *yrec = yt + td.dst_h;
+    // the tables through a buffer resource (32-bit offsets)
+    const __amdgpu_buffer_rsrc_t tabs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t *>(a.taps), 0, a.taps_bytes, kBufferWord3);
+    auto tab = [&](uint32_t dword) { return int32_t(__builtin_amdgcn_raw_buffer_load_b32(tabs, int(4 * dword), 0, 0)); };
+    const uint32_t xrec = uint32_t(td.x_tab + td.dst_w), yrec = uint32_t(td.y_tab + td.dst_h);  // first records
+    const uint32_t rdx = uint32_t(rec_dwords(ndx)), rdy = uint32_t(rec_dwords(ndy));
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lrow = lane & 15, lkb = (lane >> 4) * 16;  // the lane's fragment line and bytes
@@ -495,26 +498,35 @@ __device__ __forceinline__ void resize_mfma(const HfArgs &a, const HfTile &td, i
         const uint32_t idx = uint32_t(tid + k * kHfThreads);
         load_quad_bytes(win, win.lead + __umul24(idx >> 4, row_bytes) + (idx & 15u) * uint32_t(4 * C), C, u[k]);
     }
+    // thread t < 96 builds line t of Wx, 96 <= t < 192 line t - 96 of Wy
+    // (digit plane (t / 32) % 3, output t % 32); the others load what Wy's
+    // last line loads, so that every load is unconditional
     const bool xline = tid < 3 * kUnitPx;
     const bool yline = !xline && tid < 2 * 3 * kUnitPx;
-    const int lp = (xline ? tid : tid - 3 * kUnitPx) >> 5, li = tid & (kUnitPx - 1);
+    const int lt = xline ? tid : min(tid - 3 * kUnitPx, 3 * kUnitPx - 1);
+    const int lp = lt >> 5, li = lt & (kUnitPx - 1);
+    const int nd = xline ? ndx : ndy;  // >= 1
+    // digit plane lp of the line's record, read three dwords at a time (past
+    // its nd dwords: the next record or the tables' zero tail, masked)
+    const uint32_t dbase =
+        (xline ? xrec + __umul24(uint32_t(ox0 + li), rdx) : yrec + __umul24(uint32_t(oy0 + li), rdy)) + 1 + lp * nd;
     uint32_t dg[kMfMaxNd];
-    int lo = 0;
-    if (xline || yline) {
-        const int32_t *rec = xline ? xrec + int64_t(ox0 + li) * rec_dwords(ndx) : yrec + int64_t(oy0 + li) * rec_dwords(ndy);
-        load_digits(rec, xline ? ndx : ndy, lp, dg);
-        lo = xline ? xt[ox0 + li] - xlo : yt[oy0 + li] - ylo;
+#pragma unroll
+    for (int q = 0; q < kMfMaxNd; ++q) {
+        const uint32_t v = uint32_t(tab(dbase + q));
+        dg[q] = q < nd ? v : 0u;
     }
-    // the constants of result columns lrow and 16 + lrow (scalars: an array
-    // picked from by a wave-uniform index would go to scratch)
-    const int32_t kx0 = xrec[int64_t(ox0 + lrow) * rec_dwords(ndx)];
-    const int32_t kx1 = xrec[int64_t(ox0 + 16 + lrow) * rec_dwords(ndx)];
-    const int32_t ky0 = yrec[int64_t(oy0 + lrow) * rec_dwords(ndy)];
-    const int32_t ky1 = yrec[int64_t(oy0 + 16 + lrow) * rec_dwords(ndy)];
+    const int lo = tab(xline ? uint32_t(td.x_tab + ox0 + li) : uint32_t(td.y_tab + oy0 + li)) - (xline ? xlo : ylo);
+    // the records' constants of the lane's result column: a wave's
+    // horizontal blocks (wave, wave + 4) all lie in column block wave % 2,
+    // its vertical ones (wave + 4 j) in row block (wave / 2) % 2
+    static_assert(kHfThreads / 64 == 4, "block assignment");
+    const int32_t kx = tab(xrec + __umul24(uint32_t(ox0 + 16 * (wave & 1) + lrow), rdx));
+    const int32_t ky = tab(yrec + __umul24(uint32_t(oy0 + 16 * ((wave >> 1) & 1) + lrow), rdy));
     float lut_v[3];
 #pragma unroll
     for (int i = 0; i < 3; ++i) lut_v[i] = a.lut[tid + i * kHfThreads];
-    if (xline) write_line(lds8 + kMfWx + (lp * kUnitPx + li) * 64, li, dg, ndx, lo);
+    if (xline) write_line(lds8 + kMfWx + (lp * kUnitPx + li) * 64, li, dg, lo);
 
     // the block as channel planes of signed bytes (columns past the tile's
     // span, and rows past nrows, meet only zero weights); plane 0 now
@@ -546,7 +558,7 @@ __device__ __forceinline__ void resize_mfma(const HfArgs &a, const HfTile &td, i
         const i32x4v av = lds_frag(lds8 + buf + (rb * 16 + lrow) * 64 + lks);
         const uint8_t *wl = lds8 + kMfWx + (cb * 16 + lrow) * 64 + lks;
         return digit_product(av, lds_frag(wl + 2 * kUnitPx * 64), lds_frag(wl + kUnitPx * 64), lds_frag(wl),
-                             cb ? kx1 : kx0);
+                             kx);
     };
     auto h_store = [&](int c, int blk, const i32x4v &acc) {
         const int cb = blk & 1, rb = blk >> 1;
@@ -575,7 +587,7 @@ __device__ __forceinline__ void resize_mfma(const HfArgs &a, const HfTile &td, i
     // the vertical pass's table and Wy, where the first buffer and Wx were
 #pragma unroll
     for (int i = 0; i < 3; ++i) reinterpret_cast<float *>(lds8 + kMfLut)[tid + i * kHfThreads] = lut_v[i];
-    if (yline) write_line(lds8 + kMfWy + (lp * kUnitPx + li) * 64, li, dg, ndy, lo);
+    if (yline) write_line(lds8 + kMfWy + (lp * kUnitPx + li) * 64, li, dg, lo);
     __syncthreads();
 
     // vertical pass, transposed: out^T[x][y] = sum_r band^T[x][r] Wy^T[r][y],
@@ -595,7 +607,7 @@ __device__ __forceinline__ void resize_mfma(const HfArgs &a, const HfTile &td, i
         const i32x4v av = lds_frag(lds8 + kMfBand + (c * kUnitPx + xb * 16 + lrow) * 64 + lks);
         const uint8_t *wl = lds8 + kMfWy + (yb * 16 + lrow) * 64 + lks;
         vacc[j] = digit_product(av, lds_frag(wl + 2 * kUnitPx * 64), lds_frag(wl + kUnitPx * 64), lds_frag(wl),
-                                yb ? ky1 : ky0);
+                                ky);
     }
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
@@ -1171,6 +1183,7 @@ int build_hf_tables(int32_t n, const mimo_image_desc *desc, const float *mean01,
         for (auto &th : pool) th.join();
     }
     if (!ok.load()) return set_error(MIMO_E_UNSUPPORTED, "preprocess_hf: a resampling weight out of range");
+    out.taps.resize(out.taps.size() + kTapsTail, 0);
     return MIMO_OK;
 }
 
@@ -1205,7 +1218,7 @@ size_t mimo_hf_workspace_bytes(int32_t n, const mimo_image_desc *desc) {
         entries += axis_table_entries(s.dst_w, axis_dwords(kx)) + axis_table_entries(s.dst_h, axis_dwords(ky));
     }
     return hf_items_bytes(n) + hf_prefix_bytes(n) + align256(kLutBytes) +
-           align256(std::max<size_t>(entries, 1) * sizeof(int32_t)) + hf_tiles_bytes(n, desc);
+           align256((entries + kTapsTail) * sizeof(int32_t)) + hf_tiles_bytes(n, desc);
 }
 
 int mimo_preprocess_hf_batch(int32_t n, const mimo_image_desc *desc, const uint8_t *src,
@@ -1247,6 +1260,8 @@ int mimo_preprocess_hf_batch(int32_t n, const mimo_image_desc *desc, const uint8
     if (t.tiles == 0) return MIMO_OK;
     if (t.tiles > 0x7FFFFFFFll)
         return set_error(MIMO_E_TOO_LARGE, "preprocess_hf: more than 2^31 - 1 tiles");
+    if (t.taps.size() > size_t(0x7FFFFFF0 / sizeof(int32_t)))
+        return set_error(MIMO_E_TOO_LARGE, "preprocess_hf: resampling tables beyond 2 GiB");
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint8_t *ws = static_cast<uint8_t *>(workspace);
@@ -1268,6 +1283,7 @@ int mimo_preprocess_hf_batch(int32_t n, const mimo_image_desc *desc, const uint8
     a.stage_bytes = t.stage_bytes;
     a.tiles = t.mfma ? reinterpret_cast<HfTile *>(ws + t.head.size() + taps_bytes) : nullptr;
     a.n_tiles = t.tiles;
+    a.taps_bytes = int32_t(t.taps.size() * sizeof(int32_t));
     const size_t lds = t.lds_bytes();
     const bool f32 = out_dtype == MIMO_F32;
     const void *kernel =
