@@ -147,17 +147,18 @@ size_t hf_prefix_bytes(int32_t n) { return align256(sizeof(int64_t) * (size_t(n)
 __host__ __device__ __forceinline__ int stage_pitch(int span) { return ((span + 3) >> 2) + 1; }
 __host__ __device__ __forceinline__ int band_pitch(int rows) { return (((rows + 3) >> 2) + 1) | 1; }
 
-// A raw buffer resource over [base & ~3, src_end): reads past the end
-// return zero.  `lead` is base's offset inside it.
+// A raw buffer resource over [base & ~3, src_end), cut to `limit` bytes:
+// reads past its end return zero.  `lead` is base's offset inside it.
 struct SrcWindow {
     __amdgpu_buffer_rsrc_t rsrc;
     uint32_t lead;
 };
 
-__device__ __forceinline__ SrcWindow src_window(const HfArgs &a, uint64_t base) {
+__device__ __forceinline__ SrcWindow src_window(const HfArgs &a, uint64_t base, uint64_t limit = ~uint64_t(0)) {
     const uint64_t start = base & ~uint64_t(3);
     const uint64_t end = reinterpret_cast<uint64_t>(a.src) + uint64_t(a.src_end);
-    const uint64_t avail = end > start ? end - start : 0;
+    uint64_t avail = end > start ? end - start : 0;
+    avail = avail < limit ? avail : limit;
     SrcWindow w;
     w.rsrc = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(start), 0,
                                                avail > 0x7FFFFFF0ull ? 0x7FFFFFF0 : int(avail),
@@ -486,11 +487,14 @@ __device__ __forceinline__ void resize_mfma(const HfArgs &a, const HfTile &td, i
     const int lrow = lane & 15, lkb = (lane >> 4) * 16;  // the lane's fragment line and bytes
 
     // Everything the tile reads from memory, first: the source block (64
-    // columns x nrows rows, 4 quads per thread), Wx's and Wy's lines (one
-    // per thread of the first 192: digit plane, output), the records'
-    // constants of the lane's result columns, and the table.
-    const SrcWindow win = src_window(a, reinterpret_cast<uint64_t>(a.src) + uint64_t(td.stage_off));
-    const int total = nrows * (kMfmaSpan / 4);  // <= 1024: one batch
+    // columns x 64 rows, 4 quads per thread), Wx's and Wy's lines (one per
+    // thread of the first 192: digit plane, output), the records' constants
+    // of the lane's result columns, and the table.  The block's resource
+    // ends with row nrows - 1's reads (a row's reads span 64 C + 8 bytes at
+    // most), so later rows read zero without a memory access.
+    const uint64_t stage_base = reinterpret_cast<uint64_t>(a.src) + uint64_t(td.stage_off);
+    const SrcWindow win = src_window(a, stage_base,
+                                     (stage_base & 3u) + uint64_t(nrows - 1) * row_bytes + uint64_t(64 * C + 8));
     static_assert(kMfmaSpan * kMfmaSpan / 4 <= kStageBatch * kHfThreads, "one staging batch per tile");
     uint32_t u[kStageBatch][4];
 #pragma unroll
@@ -528,19 +532,22 @@ __device__ __forceinline__ void resize_mfma(const HfArgs &a, const HfTile &td, i
     for (int i = 0; i < 3; ++i) lut_v[i] = a.lut[tid + i * kHfThreads];
     if (xline) write_line(lds8 + kMfWx + (lp * kUnitPx + li) * 64, li, dg, lo);
 
-    // the block as channel planes of signed bytes (columns past the tile's
-    // span, and rows past nrows, meet only zero weights); plane 0 now
+    // the block as channel planes of signed bytes, all 64 rows: columns
+    // past the tile's span, and rows past nrows (read as whatever the
+    // source holds there, or zero past its end), meet only zero weights;
+    // plane 0 now
     uint32_t pl[kStageBatch][3];
 #pragma unroll
     for (int k = 0; k < kStageBatch; ++k) quad_planes(u[k], C, pl[k]);
+    uint32_t waddr[kStageBatch];  // row idx / 16, dword idx % 16, swizzled
+#pragma unroll
+    for (int k = 0; k < kStageBatch; ++k) {
+        const int idx = tid + k * kHfThreads;
+        waddr[k] = uint32_t(4 * ((idx & ~15) | swizzled_dword(idx >> 4, idx & 15)));
+    }
     auto write_plane = [&](int c, int buf) {
 #pragma unroll
-        for (int k = 0; k < kStageBatch; ++k) {
-            const int idx = tid + k * kHfThreads;  // row idx / 16, dword idx % 16
-            if (idx < total)
-                *reinterpret_cast<uint32_t *>(lds8 + buf + 4 * ((idx & ~15) | swizzled_dword(idx >> 4, idx & 15))) =
-                    pl[k][c];
-        }
+        for (int k = 0; k < kStageBatch; ++k) *reinterpret_cast<uint32_t *>(lds8 + buf + waddr[k]) = pl[k][c];
     };
     write_plane(0, kMfStage0);
     __syncthreads();
