@@ -488,39 +488,40 @@ __device__ __forceinline__ void resize_mfma(const HfArgs &a, const HfTile &td, i
 
     // Everything the tile reads from memory, first: the source block (64
     // columns x 64 rows, 4 quads per thread), Wx's and Wy's lines (one per
-    // thread of the first 192: digit plane, output), the records' constants
-    // of the lane's result columns, and the table.  The block's resource
-    // ends with row nrows - 1's reads (a row's reads span 64 C + 8 bytes at
-    // most), so later rows read zero without a memory access.
+    // thread: digit plane, output), the records' constants of the lane's
+    // result columns, and the table.  The block's resource ends with row
+    // nrows - 1's reads (a row's reads span 64 C + 8 bytes at most), so
+    // later rows read zero without a memory access.
     const uint64_t stage_base = reinterpret_cast<uint64_t>(a.src) + uint64_t(td.stage_off);
     const SrcWindow win = src_window(a, stage_base,
                                      (stage_base & 3u) + uint64_t(nrows - 1) * row_bytes + uint64_t(64 * C + 8));
-    static_assert(kMfmaSpan * kMfmaSpan / 4 <= kStageBatch * kHfThreads, "one staging batch per tile");
+    static_assert(kMfmaSpan * kMfmaSpan / 4 == kStageBatch * kHfThreads, "one staging batch per tile");
     uint32_t u[kStageBatch][4];
 #pragma unroll
     for (int k = 0; k < kStageBatch; ++k) {
         const uint32_t idx = uint32_t(tid + k * kHfThreads);
         load_quad_bytes(win, win.lead + __umul24(idx >> 4, row_bytes) + (idx & 15u) * uint32_t(4 * C), C, u[k]);
     }
-    // thread t < 96 builds line t of Wx, 96 <= t < 192 line t - 96 of Wy
-    // (digit plane (t / 32) % 3, output t % 32); the others load what Wy's
-    // last line loads, so that every load is unconditional
-    const bool xline = tid < 3 * kUnitPx;
-    const bool yline = !xline && tid < 2 * 3 * kUnitPx;
-    const int lt = xline ? tid : min(tid - 3 * kUnitPx, 3 * kUnitPx - 1);
+    // waves 0-1 build Wx's lines, waves 2-3 Wy's: thread t of the pair,
+    // t < 96, line t (digit plane t / 32, output t % 32); the pair's other
+    // threads load what line 95 loads, so that every load is unconditional
+    const bool xaxis = wave < 2;
+    const int pt = tid & 127;
+    const bool writer = pt < 3 * kUnitPx;
+    const int lt = min(pt, 3 * kUnitPx - 1);
     const int lp = lt >> 5, li = lt & (kUnitPx - 1);
-    const int nd = xline ? ndx : ndy;  // >= 1
+    const int nd = xaxis ? ndx : ndy;  // >= 1
     // digit plane lp of the line's record, read three dwords at a time (past
     // its nd dwords: the next record or the tables' zero tail, masked)
-    const uint32_t dbase =
-        (xline ? xrec + __umul24(uint32_t(ox0 + li), rdx) : yrec + __umul24(uint32_t(oy0 + li), rdy)) + 1 + lp * nd;
+    const uint32_t dbase = (xaxis ? xrec + __umul24(uint32_t(ox0 + li), rdx) : yrec + __umul24(uint32_t(oy0 + li), rdy)) +
+                           1 + lp * nd;
     uint32_t dg[kMfMaxNd];
 #pragma unroll
     for (int q = 0; q < kMfMaxNd; ++q) {
         const uint32_t v = uint32_t(tab(dbase + q));
         dg[q] = q < nd ? v : 0u;
     }
-    const int lo = tab(xline ? uint32_t(td.x_tab + ox0 + li) : uint32_t(td.y_tab + oy0 + li)) - (xline ? xlo : ylo);
+    const int lo = tab(xaxis ? uint32_t(td.x_tab + ox0 + li) : uint32_t(td.y_tab + oy0 + li)) - (xaxis ? xlo : ylo);
     // the records' constants of the lane's result column: a wave's
     // horizontal blocks (wave, wave + 4) all lie in column block wave % 2,
     // its vertical ones (wave + 4 j) in row block (wave / 2) % 2
@@ -530,7 +531,7 @@ __device__ __forceinline__ void resize_mfma(const HfArgs &a, const HfTile &td, i
     float lut_v[3];
 #pragma unroll
     for (int i = 0; i < 3; ++i) lut_v[i] = a.lut[tid + i * kHfThreads];
-    if (xline) write_line(lds8 + kMfWx + (lp * kUnitPx + li) * 64, li, dg, lo);
+    if (xaxis && writer) write_line(lds8 + kMfWx + (lp * kUnitPx + li) * 64, li, dg, lo);
 
     // the block as channel planes of signed bytes, all 64 rows: columns
     // past the tile's span, and rows past nrows (read as whatever the
@@ -594,7 +595,7 @@ __device__ __forceinline__ void resize_mfma(const HfArgs &a, const HfTile &td, i
     // the vertical pass's table and Wy, where the first buffer and Wx were
 #pragma unroll
     for (int i = 0; i < 3; ++i) reinterpret_cast<float *>(lds8 + kMfLut)[tid + i * kHfThreads] = lut_v[i];
-    if (yline) write_line(lds8 + kMfWy + (lp * kUnitPx + li) * 64, li, dg, lo);
+    if (!xaxis && writer) write_line(lds8 + kMfWy + (lp * kUnitPx + li) * 64, li, dg, lo);
     __syncthreads();
 
     // vertical pass, transposed: out^T[x][y] = sum_r band^T[x][r] Wy^T[r][y],
