@@ -515,6 +515,12 @@ const char *mimo_last_error(void);
  * proof that timings come from the GPU path). */
 int64_t mimo_dispatch_count(void);
 
+/* Number of mimo_preprocess_hf_batch launches that ran the contrast kernel's
+ * matrix-core instance (every resized tile within 64 source columns and 64
+ * band rows, at most 12 taps per output on each axis) rather than its
+ * dot-product instance.  A diagnostic: both give the same bytes. */
+int64_t mimo_hf_matrix_dispatch_count(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -123,7 +123,28 @@ def test_mild_resizes_bitwise(V, out_dtype):
     _say("mild resizes", out_dtype)
     b = W.uniform_images([(200, 300, 3), (300, 200, 4), (250, 250, 3), (90, 500, 4), (1000, 700, 3),
                           (1000, 1400, 4), (2000, 1500, 3)], seed=88)
+    before = V.hf_matrix_dispatch_count()
     plan, out = _run(V, b, out_dtype, merge=True, column=True)
+    assert V.hf_matrix_dispatch_count() == before + 1
+    _check(V, b, plan, out, out_dtype)
+
+
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_matrix_core_edge_cases_bitwise(V, out_dtype):
+    """The matrix-core instance where its reads run past what a tile needs.
+    Sources narrower than a tile's 64-column read (20x30 RGB, 40x21 RGBA,
+    33x61) put the rows past a tile's band partly inside the tile's source
+    resource. An axis that keeps its length (50x160, 160x53) runs one tap of
+    weight 1. 301x157 RGBA has odd rows. The last item's vertical upscale
+    (19 -> 64 rows) is the last table in the batch, so the digit planes of
+    its last record are read past the record, into the tables' zero tail.
+    The instance that ran is checked; same bar."""
+    shapes = [(20, 30, 3), (40, 21, 4), (33, 61, 3), (50, 160, 3), (160, 53, 4), (301, 157, 4), (19, 44, 3)]
+    _say("matrix-core edge cases", out_dtype)
+    b = W.uniform_images(shapes, seed=89)
+    before = V.hf_matrix_dispatch_count()
+    plan, out = _run(V, b, out_dtype, merge=True, column=True)
+    assert V.hf_matrix_dispatch_count() == before + 1
     _check(V, b, plan, out, out_dtype)
 
 

@@ -17,6 +17,7 @@ from ._abi import (  # noqa: F401
     MIMO_E_HIP, MIMO_E_INVALID, MIMO_E_TOO_LARGE, MIMO_E_UNSUPPORTED, MIMO_F32, MIMO_OK,
     ROW_LEN, LibraryNotBuilt, MimoError, MimoParams, column_permutation, column_permute,
     chunk_seqlens, default_params, dispatch_count, fold_patch_weights, get_number_of_image_patches,
+    hf_matrix_dispatch_count,
     hf_smart_resize,
     hf_workspace_bytes, last_error, load, make_params, patch_embed, plan_frames, plan_geometry,
     plan_hf,

@@ -89,6 +89,7 @@ SIGNATURES = {
     "mimo_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "mimo_last_error": ([], ctypes.c_char_p),
     "mimo_dispatch_count": ([], _I64),
+    "mimo_hf_matrix_dispatch_count": ([], _I64),
     "mimo_set_launch_events": ([_P, _P], ctypes.c_int),
     "mimo_rope_inv_freq": ([_I32, ctypes.c_double, _P], ctypes.c_int),
     "mimo_rotary_tables": ([_I32, _P, _I32, _I32, ctypes.c_double, _P, _P, _P, _I64, _P, _SZ, _P],
@@ -154,6 +155,12 @@ def last_error() -> str:
 
 def dispatch_count() -> int:
     return int(load().mimo_dispatch_count())
+
+
+def hf_matrix_dispatch_count() -> int:
+    """mimo_hf_matrix_dispatch_count: contrast launches that ran the
+    matrix-core instance."""
+    return int(load().mimo_hf_matrix_dispatch_count())
 
 
 def set_launch_events(start=None, stop=None):

@@ -76,6 +76,8 @@ constexpr int kLutBytes = 3 * 256 * 4;
 constexpr int kBlockBytes = kUnitPx * kUnitPx * 4;  // the direct path's unit block (RGB per dword)
 constexpr int64_t kParallelTapWork = 1 << 18;  // weights (outputs x taps) worth several host threads
 constexpr int kBufferWord3 = 0x00020000;     // raw buffer resource word 3 (gfx9 family)
+// Launches of the matrix-core instance so far (mimo_hf_matrix_dispatch_count).
+std::atomic<int64_t> g_hf_matrix_dispatches{0};
 // Zero dwords after the last table: a record's digit planes are read three
 // dwords at a time, which may run up to two dwords past the last record.
 constexpr size_t kTapsTail = 4;
@@ -713,9 +715,10 @@ __global__ __launch_bounds__(256) void hf_tiles_kernel(HfArgs a) {
     a.tiles[t] = r;
 }
 
-// Six waves per SIMD: a 6000x4000 batch's tile takes about 26 KB of LDS
-// (24 KB in the matrix-core instance), so six workgroups fill a CU; the
-// register budget that leaves (80) holds the kernel without spilling.
+// The dot-product instance runs six waves per SIMD: a 6000x4000 batch's
+// tile takes about 26 KB of LDS there, so six workgroups fill a CU, and the
+// register budget that leaves (80) holds it without spilling.  The
+// matrix-core instance's tile takes 20 KB, so it runs eight (64 registers).
 template <typename OutT, bool kMfma>
 __global__ __launch_bounds__(kHfThreads) __attribute__((amdgpu_waves_per_eu(kMfma ? 8 : 6))) void hf_preprocess_kernel(HfArgs a) {
     extern __shared__ uint32_t lds[];
@@ -1213,6 +1216,8 @@ using namespace mimo;
 
 extern "C" {
 
+int64_t mimo_hf_matrix_dispatch_count(void) { return g_hf_matrix_dispatches.load(); }
+
 size_t mimo_hf_workspace_bytes(int32_t n, const mimo_image_desc *desc) {
     if (n < 0 || (n > 0 && !desc)) return 0;
     size_t entries = 0;
@@ -1317,6 +1322,7 @@ int mimo_preprocess_hf_batch(int32_t n, const mimo_image_desc *desc, const uint8
     });
     if (e != hipSuccess) return hip_error(e, "preprocess_hf: kernel launch");
     g_dispatches.fetch_add(1);
+    if (t.mfma) g_hf_matrix_dispatches.fetch_add(1);
     return MIMO_OK;
 }
 
