@@ -560,29 +560,35 @@ __device__ __forceinline__ void resize_mfma(const HfArgs &a, const HfTile &td, i
     const int swz = (lrow >> 2) & 3;
     const int lks = 16 * ((lkb >> 4) ^ swz);
     // horizontal pass, one channel at a time: blocks (16 band rows, 16
-    // output columns), two per wave so that their matrix-core chains overlap
+    // output columns), two per wave so that their matrix-core products
+    // overlap: wave w takes column block w % 2 and row blocks w / 2 and
+    // w / 2 + 2 (the second only where the band reaches it; otherwise the
+    // first is computed twice and stored once).  The lane's LDS addresses
+    // are the same in every channel but for the buffer and the band's
+    // channel offset, so they are formed once.
     const int rblocks = (nrows + 15) >> 4;  // 1 .. 4
-    const int nblk = rblocks * 2;           // <= 8: one step per wave
-    auto h_block = [&](int buf, int blk) {
-        const int cb = blk & 1, rb = blk >> 1;
-        const i32x4v av = lds_frag(lds8 + buf + (rb * 16 + lrow) * 64 + lks);
-        const uint8_t *wl = lds8 + kMfWx + (cb * 16 + lrow) * 64 + lks;
-        return digit_product(av, lds_frag(wl + 2 * kUnitPx * 64), lds_frag(wl + kUnitPx * 64), lds_frag(wl),
-                             kx);
+    const int cb = wave & 1, rb0 = wave >> 1;
+    const bool one = rb0 < rblocks, two = rb0 + 2 < rblocks;
+    const uint32_t a0 = uint32_t((rb0 * 16 + lrow) * 64 + lks);
+    const uint32_t a1 = two ? a0 + 2 * 16 * 64 : a0;
+    const uint8_t *wl = lds8 + kMfWx + (cb * 16 + lrow) * 64 + lks;
+    // rows 4 (lane / 16) .. + 3 of column cb * 16 + lrow, as signed bytes
+    const uint32_t st_line = uint32_t(kMfBand + (cb * 16 + lrow) * 64 + lkb / 4);
+    const uint32_t s0 = st_line + 16 * (rb0 ^ swz), s1 = st_line + 16 * ((rb0 + 2) ^ swz);
+    auto h_block = [&](int buf, uint32_t aoff) {
+        return digit_product(lds_frag(lds8 + buf + aoff), lds_frag(wl + 2 * kUnitPx * 64), lds_frag(wl + kUnitPx * 64),
+                             lds_frag(wl), kx);
     };
-    auto h_store = [&](int c, int blk, const i32x4v &acc) {
-        const int cb = blk & 1, rb = blk >> 1;
-        // rows 4 (lane / 16) .. + 3 of column cb * 16 + lrow, as signed bytes
-        *reinterpret_cast<uint32_t *>(lds8 + kMfBand + (c * kUnitPx + cb * 16 + lrow) * 64 + 16 * (rb ^ swz) +
-                                      lkb / 4) = join_pairs(shift_pack_i8(acc[0], acc[1]), shift_pack_i8(acc[2], acc[3]));
+    auto h_store = [&](int c, uint32_t soff, const i32x4v &acc) {
+        *reinterpret_cast<uint32_t *>(lds8 + c * kUnitPx * 64 + soff) =
+            join_pairs(shift_pack_i8(acc[0], acc[1]), shift_pack_i8(acc[2], acc[3]));
     };
     auto h_pass_channel = [&](int c, int buf) {
-        const int blk = wave, blk2 = wave + kHfThreads / 64;
-        if (blk < nblk) {
-            const i32x4v acc = h_block(buf, blk);
-            const i32x4v acc2 = h_block(buf, min(blk2, nblk - 1));
-            h_store(c, blk, acc);
-            if (blk2 < nblk) h_store(c, blk2, acc2);
+        if (one) {
+            const i32x4v acc = h_block(buf, a0);
+            const i32x4v acc2 = h_block(buf, a1);
+            h_store(c, s0, acc);
+            if (two) h_store(c, s1, acc2);
         }
     };
     h_pass_channel(0, kMfStage0);
