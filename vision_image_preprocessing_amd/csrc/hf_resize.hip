@@ -446,26 +446,30 @@ __device__ __forceinline__ int swizzled_dword(int line, int dw) {
 }
 
 // Line i of a banded weight matrix (64 bytes): the digits dg placed at byte
-// o, zero elsewhere.  The line is zeroed 16 bytes at a time, each group of 4
-// lines starting at its own chunk: lines are 64 bytes apart, so lanes
-// writing the same chunk of lines 4 apart would share banks.  Then dwords
-// o / 4 .. + 3 take the digits shifted by o % 4 bytes, without a condition:
-// the digits end by byte 63 (o + 4 nd is at most the tile's span of 64), so
-// a dword index past the line's end carries zeros only, and it wraps to a
-// dword before o / 4, which is zero as well.
+// o, zero elsewhere.  The line is zeroed first, 16 bytes at a time, each
+// group of 4 lines in its own chunk order (lines are 64 bytes apart, so
+// lanes writing the same chunk of lines 4 apart would share banks); then
+// four dwords take the digits shifted by s = o % 4 bytes,
+// each the byte-aligned join of two neighbouring digit dwords.  The
+// alignment instruction reads its shift (4 - s) modulo 4: at s = 0 the join
+// of dwords q and q - 1 is dword q - 1, so the writes start one dword
+// earlier, at ceil(o / 4) - 1, and no case needs a select.  No write needs a
+// condition either: the digits end by byte 63 (o + 4 nd is at most the
+// tile's span of 64), so a dword index past the line carries zeros only,
+// and it wraps to a dword before the digits, which is zero as well.
 __device__ __forceinline__ void write_line(uint8_t *line, int i, const uint32_t (&dg)[kMfMaxNd], int o) {
-    const int rot = (i >> 2) & 3;
+    const int key16 = ((i >> 2) & 3) << 4;  // the group's chunk order, in bytes
 #pragma unroll
-    for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4 *>(line + 16 * ((k + rot) & 3)) = u32x4{0u, 0u, 0u, 0u};
-    const int a = o >> 2, sh = o & 3;
+    for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4 *>(line + ((16 * k) ^ key16)) = u32x4{0u, 0u, 0u, 0u};
+    const int first = ((o + 3) >> 2) - 1;
+    const uint32_t shift = uint32_t(-o) & 3u;  // (4 - s) modulo 4
+    const int key = ((i >> 2) & 3) << 2;       // the line's chunk swizzle, as a dword index
     uint32_t *w = reinterpret_cast<uint32_t *>(line);
     uint32_t prev = 0;
 #pragma unroll
     for (int q = 0; q <= kMfMaxNd; ++q) {
         const uint32_t cur = q < kMfMaxNd ? dg[q] : 0u;
-        // bytes 4 (a + q) .. + 3 of the line: the tail of dword q - 1 and the head of dword q
-        const uint32_t val = sh ? __builtin_amdgcn_alignbyte(cur, prev, uint32_t(4 - sh)) : cur;
-        w[swizzled_dword(i, (a + q) & (kMfmaSpan / 4 - 1))] = val;
+        w[((first + q) & (kMfmaSpan / 4 - 1)) ^ key] = __builtin_amdgcn_alignbyte(cur, prev, shift);
         prev = cur;
     }
 }
