@@ -577,7 +577,9 @@ template <typename OutT, int TT>
 __device__ __forceinline__ void tile_pass(const PreArgs &a, const DevImage &d, const TileGeom &g,
                                           int64_t frame_offset, OutT *out, bool column,
                                           uint32_t *band) {
-    const int wave = threadIdx.x >> 6;
+    // the wave index as a scalar: a row's tile coordinates and output
+    // address are then the same in every lane, formed on the scalar unit
+    const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
     const int waves = blockDim.x >> 6;
     if (d.flags & kFlagIdentity) {
         const int64_t row_bytes = int64_t(d.src_w) * d.channels;
@@ -634,7 +636,7 @@ __device__ __forceinline__ void clip_pair_pass(const PreArgs &a, const DevImage 
     const int r0 = div_small(threadIdx.x, b.groups, 1.0f / float(b.groups));
     const int gi = threadIdx.x - r0 * b.groups;
     const bool active = r0 < step;
-    const int wave = threadIdx.x >> 6, waves = blockDim.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6)), waves = blockDim.x >> 6;
     const BandPixels px = band_pixels(band, a, d, g, b);
     RowBatch next;
     if (active) {
