@@ -265,7 +265,9 @@ __device__ __forceinline__ OutT *row_dest(OutT *out, const DevImage &d, int t, i
                          (column ? int64_t(bc) * d.blocks_h + br : int64_t(br) * d.blocks_w + bc);
     const int64_t row = d.row_offset + unit * kRowsPerUnit + mh * kMerge + mw;
     const int lane = threadIdx.x & 63;
-    return out + row * kRowLen + (lane >> 2) * kPatch + 4 * (lane & 3);
+    // the row's start (uniform across the wave) plus the lane's 32-bit offset
+    OutT *const start = out + row * kRowLen;
+    return start + ((lane >> 2) * kPatch + 4 * (lane & 3));
 }
 
 // Identity resize (dst == src): output pixel (y, x) is source pixel (y, x).
@@ -365,7 +367,8 @@ __device__ __forceinline__ void bilinear_patch_band(const BandPixels &px, const 
     const int oy = (br * kMerge + mh) * kPatch + py;
     const int xc = (bc * kMerge + mw) * kPatch + 4 * q - px.ox_first;
     const Tap ty = make_tap(d.scale_y, oy, d.src_h);
-    const uint32_t *r0 = px.band + (ty.i0 - px.r_lo) * px.pitch;
+    // (both factors below 2^23: the 24-bit multiplier)
+    const uint32_t *r0 = px.band + __mul24(ty.i0 - px.r_lo, px.pitch);
     const uint32_t *r1 = r0 + px.pitch;
     const i32x4 xi = *reinterpret_cast<const i32x4 *>(px.xi + xc);
     const f32x4 l0 = *reinterpret_cast<const f32x4 *>(px.xl0 + xc);
