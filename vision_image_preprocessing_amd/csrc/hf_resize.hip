@@ -540,9 +540,9 @@ __device__ __forceinline__ void resize_mfma(const HfArgs &a, const HfTile &td, i
     if (xaxis && writer) write_line(lds8 + kMfWx + (lp * kUnitPx + li) * 64, li, dg, lo);
 
     // the block as channel planes of signed bytes, all 64 rows: columns
-    // past the tile's span, and rows past nrows (read as whatever the
-    // source holds there, or zero past its end), meet only zero weights;
-    // plane 0 now
+    // past the tile's span, and rows past nrows (zero, or in a source
+    // narrower than a row's reads, the bytes that follow), meet only zero
+    // weights; plane 0 now
     uint32_t pl[kStageBatch][3];
 #pragma unroll
     for (int k = 0; k < kStageBatch; ++k) quad_planes(u[k], C, pl[k]);
