@@ -175,8 +175,11 @@ def test_strong_downscale_row_groups(V):
     row groups."""
     _say("strong downscale")
     b = W.uniform_images([(4000, 6000, 3), (3000, 300, 3)], seed=84)
+    before = V.hf_matrix_dispatch_count()
     plan, out = _run(V, b, "f32", min_pixels=4096, max_pixels=8192)
     assert plan.desc["dst_h"][0] < 200
+    # windows of hundreds of taps: the dot-product instance, not the matrix cores
+    assert V.hf_matrix_dispatch_count() == before
     _check(V, b, plan, out, "f32", min_pixels=4096, max_pixels=8192)
 
 

@@ -60,6 +60,7 @@ constexpr int kBandBudgetDwords = 12288;  // 48 KB
 // Most output columns of one tile (three merge units side by side): the size
 // of each of the three x-tap arrays that follow the band in LDS.
 constexpr int kMaxTileCols = 3 * kUnitPx;
+constexpr int kMaxTileRows = kUnitPx;  // output rows one tile covers
 static_assert(MIMO_ROWS_PER_TILE <= 3 * kRowsPerUnit && MIMO_ROWS_PER_TILE_CLIPS <= 3 * kRowsPerUnit &&
                   MIMO_ROWS_PER_TILE_DUAL <= kRowsPerUnit,
               "a tile spans at most three merge units of output columns");
@@ -306,6 +307,11 @@ struct BandPixels {  // staged in LDS, edge already replicated
     const int32_t *xi;
     const float *xl0, *xl1;
     int ox_first;
+    // (clip instance) the y taps of its output rows (from row oy_first),
+    // likewise: per row the band offsets (dwords) of its two rows, then its
+    // two weights
+    const i32x4 *yt;
+    int oy_first;
 };
 
 struct GlobalPixels {  // straight from memory, clamped
@@ -358,7 +364,7 @@ __device__ __forceinline__ void bilinear_patch(const Pixels &px, const DevImage 
 // from the tile's table (three 16-byte LDS reads for the lane's 4 pixels),
 // the second taps always one row / column on (the band repeats the image's
 // last row and column).  Bitwise the same values as bilinear_patch.
-template <typename OutT, int TT>
+template <typename OutT, int TT, bool kYTab>
 __device__ __forceinline__ void bilinear_patch_band(const BandPixels &px, const DevImage &d, const PreArgs &a,
                                                     int t, int br, int bc, int mh, int mw, OutT *out,
                                                     bool column) {
@@ -366,10 +372,23 @@ __device__ __forceinline__ void bilinear_patch_band(const BandPixels &px, const 
     const int py = lane >> 2, q = lane & 3;
     const int oy = (br * kMerge + mh) * kPatch + py;
     const int xc = (bc * kMerge + mw) * kPatch + 4 * q - px.ox_first;
-    const Tap ty = make_tap(d.scale_y, oy, d.src_h);
-    // (both factors below 2^23: the 24-bit multiplier)
-    const uint32_t *r0 = px.band + __mul24(ty.i0 - px.r_lo, px.pitch);
-    const uint32_t *r1 = r0 + px.pitch;
+    Tap ty{0, 0.0f, 0.0f};
+    const uint32_t *r0, *r1;
+    if (kYTab) {
+        // the row offsets now, the weights (a load of their own) where the
+        // vertical step needs them
+        const int32_t *ye = reinterpret_cast<const int32_t *>(px.yt + (oy - px.oy_first));
+        r0 = px.band + ye[0];
+        r1 = px.band + ye[1];
+        const float *yw = reinterpret_cast<const float *>(ye + 2);
+        ty.l0 = yw[0];
+        ty.l1 = yw[1];
+    } else {
+        ty = make_tap(d.scale_y, oy, d.src_h);
+        // (both factors below 2^23: the 24-bit multiplier)
+        r0 = px.band + __mul24(ty.i0 - px.r_lo, px.pitch);
+        r1 = r0 + px.pitch;
+    }
     const i32x4 xi = *reinterpret_cast<const i32x4 *>(px.xi + xc);
     const f32x4 l0 = *reinterpret_cast<const f32x4 *>(px.xl0 + xc);
     const f32x4 l1 = *reinterpret_cast<const f32x4 *>(px.xl1 + xc);
@@ -551,6 +570,7 @@ __device__ __forceinline__ void replicate_right_edge(uint32_t *band, const DevIm
 // The x taps of the tile's output columns into the table that follows the
 // band in LDS (the band's first column c_lo as origin); made before the
 // band's barrier.
+template <bool kYTab>
 __device__ __forceinline__ BandPixels band_pixels(uint32_t *band, const PreArgs &a, const DevImage &d,
                                                   const TileGeom &g, const Band &b) {
     BandPixels px;
@@ -571,12 +591,23 @@ __device__ __forceinline__ BandPixels band_pixels(uint32_t *band, const PreArgs 
     px.xl0 = xl0;
     px.xl1 = xl1;
     px.ox_first = g.ox_first;
+    px.yt = nullptr;
+    px.oy_first = g.oy_first;
+    if (kYTab) {
+        i32x4 *yt = reinterpret_cast<i32x4 *>(xl1 + kMaxTileCols);  // 16-byte aligned
+        for (int i = threadIdx.x; i <= g.oy_last - g.oy_first; i += blockDim.x) {
+            const Tap ty = make_tap(d.scale_y, g.oy_first + i, d.src_h);
+            const int r0 = __mul24(ty.i0 - b.r_lo, b.pitch);
+            yt[i] = i32x4{r0, r0 + b.pitch, __builtin_bit_cast(int32_t, ty.l0), __builtin_bit_cast(int32_t, ty.l1)};
+        }
+        px.yt = yt;
+    }
     return px;
 }
 
 // Resamples one source frame (at frame_offset) of the tile into temporal
 // slot TT of its rows (both slots when TT < 0).
-template <typename OutT, int TT>
+template <typename OutT, int TT, bool kYTab>
 __device__ __forceinline__ void tile_pass(const PreArgs &a, const DevImage &d, const TileGeom &g,
                                           int64_t frame_offset, OutT *out, bool column,
                                           uint32_t *band) {
@@ -600,7 +631,7 @@ __device__ __forceinline__ void tile_pass(const PreArgs &a, const DevImage &d, c
 
     const Band b = tile_band(a, d, g);
     if (b.fits) {
-        const BandPixels px = band_pixels(band, a, d, g, b);
+        const BandPixels px = band_pixels<kYTab>(band, a, d, g, b);
         stage_band(band, a, d, frame_offset, b.r_lo, b.c_lo, b.rows, b.groups, b.pitch);
         __syncthreads();
         if (b.c_end == d.src_w) {
@@ -609,7 +640,7 @@ __device__ __forceinline__ void tile_pass(const PreArgs &a, const DevImage &d, c
         }
         for (int p = wave; p < g.count; p += waves) {
             const int qr = g.first + p;
-            bilinear_patch_band<OutT, TT>(px, d, a, g.t, g.br, qr >> 2, (qr >> 1) & 1, qr & 1, out, column);
+            bilinear_patch_band<OutT, TT, kYTab>(px, d, a, g.t, g.br, qr >> 2, (qr >> 1) & 1, qr & 1, out, column);
         }
     } else {
         const GlobalPixels px{a.src + frame_offset, int64_t(d.src_w) * d.channels, d.channels,
@@ -625,7 +656,7 @@ __device__ __forceinline__ void tile_pass(const PreArgs &a, const DevImage &d, c
 // row has no more 4-pixel groups than the workgroup has threads: frame 1's
 // first batch of band loads goes out before frame 0 is resampled, so that
 // its latency is spent there.
-template <typename OutT, int C>
+template <typename OutT, int C, bool kYTab>
 __device__ __forceinline__ void clip_pair_pass(const PreArgs &a, const DevImage &d, const TileGeom &g,
                                                const Band &b, int64_t off0, int64_t off1, OutT *out,
                                                bool column, uint32_t *band) {
@@ -640,7 +671,7 @@ __device__ __forceinline__ void clip_pair_pass(const PreArgs &a, const DevImage 
     const int gi = threadIdx.x - r0 * b.groups;
     const bool active = r0 < step;
     const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6)), waves = blockDim.x >> 6;
-    const BandPixels px = band_pixels(band, a, d, g, b);
+    const BandPixels px = band_pixels<kYTab>(band, a, d, g, b);
     RowBatch next;
     if (active) {
         stage_rows<C>(band, w0, row_bytes, r0, step, b.rows, last_row, gi, b.pitch);
@@ -653,7 +684,7 @@ __device__ __forceinline__ void clip_pair_pass(const PreArgs &a, const DevImage 
     }
     for (int p = wave; p < g.count; p += waves) {
         const int qr = g.first + p;
-        bilinear_patch_band<OutT, 0>(px, d, a, g.t, g.br, qr >> 2, (qr >> 1) & 1, qr & 1, out, column);
+        bilinear_patch_band<OutT, 0, kYTab>(px, d, a, g.t, g.br, qr >> 2, (qr >> 1) & 1, qr & 1, out, column);
     }
     __syncthreads();  // the first frame's band is no longer read
     if (active) {
@@ -672,7 +703,7 @@ __device__ __forceinline__ void clip_pair_pass(const PreArgs &a, const DevImage 
     }
     for (int p = wave; p < g.count; p += waves) {
         const int qr = g.first + p;
-        bilinear_patch_band<OutT, 1>(px, d, a, g.t, g.br, qr >> 2, (qr >> 1) & 1, qr & 1, out, column);
+        bilinear_patch_band<OutT, 1, kYTab>(px, d, a, g.t, g.br, qr >> 2, (qr >> 1) & 1, qr & 1, out, column);
     }
 }
 
@@ -744,7 +775,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kClips
     // its one frame.  Identical frames are computed once and stored to both
     // slots; distinct frames take one pass per slot.
     if (!kClips) {
-        tile_pass<OutT, -1>(a, d, g, d.src_offset, out, column, band);
+        tile_pass<OutT, -1, false>(a, d, g, d.src_offset, out, column, band);
         return;
     }
     const int64_t frame_bytes = int64_t(d.src_h) * d.src_w * d.channels;
@@ -752,22 +783,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kClips
     const int f1 = min(kTemporal * g.t + 1, d.frames - 1);
     const int64_t off0 = d.src_offset + int64_t(f0) * frame_bytes;
     if (f0 == f1) {
-        tile_pass<OutT, -1>(a, d, g, off0, out, column, band);
+        tile_pass<OutT, -1, true>(a, d, g, off0, out, column, band);
     } else {
         const int64_t off1 = d.src_offset + int64_t(f1) * frame_bytes;
         if (!(d.flags & kFlagIdentity)) {
             const Band b = tile_band(a, d, g);
             if (b.fits && b.groups <= int(blockDim.x)) {
                 if (d.channels == 3)
-                    clip_pair_pass<OutT, 3>(a, d, g, b, off0, off1, out, column, band);
+                    clip_pair_pass<OutT, 3, true>(a, d, g, b, off0, off1, out, column, band);
                 else
-                    clip_pair_pass<OutT, 4>(a, d, g, b, off0, off1, out, column, band);
+                    clip_pair_pass<OutT, 4, true>(a, d, g, b, off0, off1, out, column, band);
                 return;
             }
         }
-        tile_pass<OutT, 0>(a, d, g, off0, out, column, band);
+        tile_pass<OutT, 0, true>(a, d, g, off0, out, column, band);
         __syncthreads();  // the first frame's band is no longer read
-        tile_pass<OutT, 1>(a, d, g, off1, out, column, band);
+        tile_pass<OutT, 1, true>(a, d, g, off1, out, column, band);
     }
 }
 
@@ -1057,7 +1088,8 @@ int preprocess_common(const char *who, int32_t n, const mimo_image_desc *desc, c
     a.rows_per_tile = tiling.rows_per_tile;
     a.xcd_order = tiling.xcd_order;
     a.tiles_per_pass = rows ? t.total_tiles : int64_t(1) << 62;
-    const size_t lds = (size_t(t.band_capacity) + 3 * kMaxTileCols) * 4;  // band, then the x-tap table
+    // band, then the x-tap table, then (clip instance) the y-tap table
+    const size_t lds = (size_t(t.band_capacity) + 3 * kMaxTileCols + (t.clips ? 4 * kMaxTileRows : 0)) * 4;
     const dim3 grid{unsigned(t.total_tiles * tiling.passes), 1, 1},
         block{unsigned(tiling.threads()), 1, 1};
     const bool inl = n <= kInlineImages;
