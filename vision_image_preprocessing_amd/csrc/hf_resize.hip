@@ -228,10 +228,11 @@ __device__ __forceinline__ int32_t dot4(uint32_t x, uint32_t w, int32_t acc) {
 
 // Two sums s0, s1 shifted right by kWeightBits and saturated to a byte
 // (unsigned, or signed for the _i8 form), in bytes 0 and 1 of the result;
-// the upper half of the result register is left undefined.  The inputs come
-// from v_dot4 instructions, whose results a VALU instruction may read only
-// three wait states later; the compiler keeps that distance for its own
-// instructions but cannot see into this one, hence the s_nop.
+// the upper half of the result register is left undefined.  In the
+// dot-product instance the inputs come straight from v_dot4 instructions,
+// whose results a VALU instruction may read only three wait states later;
+// the compiler keeps that distance for its own instructions but cannot see
+// into this one, hence the s_nop.
 __device__ __forceinline__ uint32_t shift_pack_u8(int32_t s0, int32_t s1) {
     uint32_t d;
     asm("s_nop 2\n\tv_ashr_pk_u8_i32 %0, %1, %2, 22" : "=v"(d) : "v"(s0), "v"(s1));
@@ -389,8 +390,8 @@ __device__ __forceinline__ void store_pair<uint16_t>(uint16_t *p, const float (&
 // and 64 band rows with windows of at most 12 taps (downscales up to about
 // 1.8x, and upscales), each 16 x 16 block of either product is one
 // v_mfma_i32_16x16x64_i8 per weight digit plane: exact int32 sums of
-// signed-byte products, chained through the accumulator as in the dot
-// products above.  A tile's banded matrices are built in LDS (zero but for
+// signed-byte products, joined by shift-adds (digit_product below).  A
+// tile's banded matrices are built in LDS (zero but for
 // each output's own taps) as 64-byte lines, which the matrix cores read as
 // 16-byte fragments: lane l reads line l % 16, bytes 16 (l / 16) .. + 15,
 // and holds result rows 4 (l / 16) .. + 3 of column l % 16.
