@@ -367,7 +367,11 @@ __global__ __launch_bounds__(kEmbedThreads) void pixel_embed_kernel(PixelEmbedAr
             }
         }
     };
-#pragma unroll
+    // the no-resample instance runs its stages fully unrolled (every buffer
+    // choice a constant, every load tracked exactly); the resampling one is
+    // too large to unroll and loops
+    constexpr int kStageUnroll = kGeneral ? 1 : kStages;
+#pragma unroll kStageUnroll
     for (int s = 0; s < kStages; ++s) {
         const bool even = s % 2 == 0;
         stage(s, even ? sa0 : sa1, even ? sb0 : sb1, even ? sa1 : sa0, even ? sb1 : sb0);
